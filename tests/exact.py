@@ -1,0 +1,121 @@
+"""Exact reference arithmetic for pinning the oracle (test helper, CPU only).
+
+Nothing here shares code with ``oracle/``: values are decoded with the formats'
+bit-level definitions through numpy views, and rounding picks the nearest
+representable value by exact rational comparison against an enumerated or
+neighbour-searched candidate set, ties going to the pattern with an even last
+mantissa bit (IEEE 754 roundTiesToEven).
+"""
+from __future__ import annotations
+
+import bisect
+from fractions import Fraction
+from functools import lru_cache
+
+import numpy as np
+
+
+def f16_value(bits: int) -> float:
+    return float(np.array([bits], dtype=np.uint16).view(np.float16)[0])
+
+
+def bf16_value(bits: int) -> float:
+    # bfloat16 is by definition the upper half of an IEEE binary32 pattern.
+    return float(np.array([bits << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+def f16_values(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    with np.errstate(invalid="ignore"):
+        return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@lru_cache(maxsize=None)
+def _table(t: str):
+    """Sorted non-negative finite values of a 16-bit format with their bit patterns,
+    followed by a pseudo-entry 2^(emax+1) standing for +inf (its pattern has an even
+    mantissa, so a tie at max + half-ulp goes to infinity as IEEE 754 requires)."""
+    bits = np.arange(0x8000, dtype=np.uint16)
+    vals = f16_values(bits) if t == "f16" else bf16_values(bits)
+    keep = np.isfinite(vals)
+    vals, bits = vals[keep], bits[keep]
+    order = np.argsort(vals, kind="stable")
+    vals, bits = list(vals[order]), [int(b) for b in bits[order]]
+    inf_bits = 0x7C00 if t == "f16" else 0x7F80
+    top = 2.0 ** 16 if t == "f16" else 2.0 ** 128
+    return vals + [top], bits + [inf_bits]
+
+
+def round16(x: Fraction, t: str) -> int:
+    """Bits of the f16/bf16 value nearest to the exact rational x (ties to even)."""
+    sign = 0x8000 if x < 0 else 0
+    a = -x if x < 0 else x
+    vals, bits = _table(t)
+    if a >= Fraction(vals[-1]):
+        return sign | bits[-1]
+    hi = bisect.bisect_left(vals, float(a))
+    cands = [c for c in (hi - 2, hi - 1, hi, hi + 1) if 0 <= c < len(vals)]
+    best = min(cands, key=lambda c: (abs(Fraction(vals[c]) - a), bits[c] & 1))
+    return sign | bits[best]
+
+
+def round32(x: Fraction) -> np.float32:
+    """The binary32 value nearest to the exact rational x (ties to even)."""
+    c = np.float32(float(x))
+    if not np.isfinite(c):
+        return c
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    cands = [v for v in cands if np.isfinite(v)]
+    def key(v):
+        return (abs(Fraction(float(v)) - x), int(np.array([v], dtype=np.float32).view(np.uint32)[0]) & 1)
+    best = min(cands, key=key)
+    if best == 0 and x < 0:
+        return np.float32(-0.0)
+    return best
+
+
+def exact_value(bits, t: str) -> Fraction:
+    if t == "f16":
+        return Fraction(f16_value(int(bits)))
+    if t == "bf16":
+        return Fraction(bf16_value(int(bits)))
+    if t == "f32":
+        return Fraction(float(bits))
+    return Fraction(int(bits))
+
+
+def brute_gemm(p):
+    """Exact D of a (tiny) workload: rational sums for floats, Python ints for int8.
+
+    Reads operands element by element from the raw storage with the BLAS-convention
+    addressing, independently of the oracle's loops.
+    """
+    def a_at(b, i, k):
+        off = b * p.stride_a + (i * p.lda + k if p.layout_a == "row" else i + k * p.lda)
+        return exact_value(p.A[off], p.in_type)
+
+    def b_at(b, k, j):
+        off = b * p.stride_b + (k * p.ldb + j if p.layout_b == "row" else k + j * p.ldb)
+        return exact_value(p.B[off], p.in_type)
+
+    c_t = "i32" if p.in_type == "i8" else p.out_type
+    out = np.zeros(p.batch * p.stride_d, dtype={"f32": np.float32, "f16": np.uint16,
+                                                "bf16": np.uint16, "i32": np.int32}[p.out_type])
+    for b in range(p.batch):
+        for i in range(p.M):
+            for j in range(p.N):
+                s = sum((a_at(b, i, k) * b_at(b, k, j) for k in range(p.K)), Fraction(0))
+                if p.C is not None:
+                    s += exact_value(p.C[b * p.stride_c + i * p.ldc + j], c_t)
+                o = b * p.stride_d + i * p.ldd + j
+                if p.out_type == "i32":
+                    v = int(s) & 0xFFFFFFFF
+                    out[o] = v - (1 << 32) if v >= (1 << 31) else v
+                elif p.out_type == "f32":
+                    out[o] = round32(s)
+                else:
+                    out[o] = round16(s, p.out_type)
+    return out

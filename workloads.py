@@ -1,0 +1,211 @@
+"""Seeded synthetic inputs for D = A*B + C, shared by the GPU path and the oracle.
+
+This module holds no part of the product's arithmetic: it only draws values,
+rounds them to the input type with numpy/torch conversions, and lays them out
+with the call parameters (sizes, layouts, leading dimensions, strides) that
+both sides receive unchanged.  The workloads follow the five problems that
+centre the pages' discussion:
+
+  c1   fp16 256^3, A and B row-major, fp32 accumulate and output, C = 0
+  c2   bf16 4096^3, A and B row-major, fp32 accumulate, bf16 output
+  c3   fp16 5000 x 3000 x 2050, A row-major, B column-major, fp16 output
+  c4s  batch 32 of S = Q K^T, Q and K 4096 x 128 (B column-major), fp32 output
+  c4o  batch 32 of O = P V, P 4096 x 4096 softmax rows, V 4096 x 128, fp32 output
+  c5   int8 8192^3, A row-major, B column-major, int32 output
+
+Random draws come from ``numpy.random.default_rng([config_id, matrix_id, seed])``
+in fp64 and are rounded to the input type.  ``structured`` copies hold small
+integers whose products have closed forms; they are exact in every type.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+
+CONFIG_IDS = {"c1": 1, "c2": 2, "c3": 3, "c4s": 41, "c4o": 42, "c5": 5}
+
+# (M, N, K, batch, in_type, out_type, acc_type, layout_a, layout_b)
+FULL = {
+    "c1": (256, 256, 256, 1, "f16", "f32", "f32", "row", "row"),
+    "c2": (4096, 4096, 4096, 1, "bf16", "bf16", "f32", "row", "row"),
+    "c3": (5000, 3000, 2050, 1, "f16", "f16", "f16", "row", "col"),
+    "c4s": (4096, 4096, 128, 32, "f16", "f32", "f32", "row", "col"),
+    "c4o": (4096, 128, 4096, 32, "f16", "f32", "f32", "row", "row"),
+    "c5": (8192, 8192, 8192, 1, "i8", "i32", "i32", "row", "col"),
+}
+
+_NP_BITS = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32, "i8": np.int8, "i32": np.int32}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "f32": 4, "i8": 1, "i32": 4}
+
+
+@dataclass
+class Problem:
+    """One call's worth of inputs, as raw element bits plus the call parameters."""
+
+    name: str
+    M: int
+    N: int
+    K: int
+    batch: int
+    in_type: str
+    acc_type: str
+    out_type: str
+    layout_a: str
+    layout_b: str
+    A: np.ndarray
+    lda: int
+    stride_a: int
+    B: np.ndarray
+    ldb: int
+    stride_b: int
+    C: Optional[np.ndarray] = None
+    ldc: int = 0
+    stride_c: int = 0
+    ldd: int = 0
+    stride_d: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K * self.batch
+
+    def d_elems(self) -> int:
+        return self.batch * self.stride_d if self.batch else 0
+
+
+def to_bits(x: np.ndarray, t: str) -> np.ndarray:
+    """Round fp64 draws to the input type (library conversions) and return raw bits."""
+    if t == "f16":
+        return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+    if t == "bf16":
+        import torch
+
+        f = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        return f.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if t == "f32":
+        return np.asarray(x, dtype=np.float32)
+    if t == "i8":
+        return np.asarray(x, dtype=np.int8)
+    if t == "i32":
+        return np.asarray(x, dtype=np.int32)
+    raise ValueError(t)
+
+
+def _rng(cfg: str, matrix_id: int, seed: int) -> np.random.Generator:
+    return np.random.default_rng([CONFIG_IDS.get(cfg, 99), matrix_id, seed])
+
+
+def _layout_params(M, N, K, layout_a, layout_b, pad=0):
+    """Leading dimensions for densely stored operands (plus optional padding)."""
+    lda = (K if layout_a == "row" else M) + pad
+    ldb = (N if layout_b == "row" else K) + pad
+    rows_a = M if layout_a == "row" else K
+    rows_b = K if layout_b == "row" else N
+    return lda, ldb, rows_a * lda, rows_b * ldb
+
+
+def _storage(logical: np.ndarray, layout: str, ld: int) -> np.ndarray:
+    """Store a logical [batch, R, Cc] array row- or column-major with leading dim ld."""
+    b, r, c = logical.shape
+    if layout == "row":
+        out = np.zeros((b, r, ld), dtype=logical.dtype)
+        out[:, :, :c] = logical
+    else:
+        out = np.zeros((b, c, ld), dtype=logical.dtype)
+        out[:, :, :r] = np.transpose(logical, (0, 2, 1))
+    return out.reshape(-1)
+
+
+def make(cfg: str, kind: str = "random", seed: int = 0, *, M=None, N=None, K=None, batch=None,
+         pad: int = 0, with_c: bool = False) -> Problem:
+    """Build a workload.  Sizes default to the full problem; override to shrink it.
+
+    kind: "random" (the problem's value distribution) or "structured" (closed form).
+    pad:  extra elements per leading dimension (exercises ld > rows/cols).
+    with_c: add a seeded C operand (the full problems pass C = 0 or none).
+    """
+    fM, fN, fK, fb, in_t, out_t, acc_t, la, lb = FULL[cfg]
+    M = fM if M is None else M
+    N = fN if N is None else N
+    K = fK if K is None else K
+    batch = fb if batch is None else batch
+    lda, ldb, sa, sb = _layout_params(M, N, K, la, lb, pad)
+    i = np.arange(M)[:, None]
+    j = np.arange(N)[None, :]
+    meta = {"kind": kind, "seed": seed, "cfg": cfg}
+
+    if kind == "random":
+        ra, rb = _rng(cfg, 0, seed), _rng(cfg, 1, seed)
+        if cfg == "c1" or cfg == "c4s":
+            a = ra.uniform(-1, 1, (batch, M, K))
+            b = rb.uniform(-1, 1, (batch, K, N))
+        elif cfg == "c2":
+            s = 1.0 / np.sqrt(K) if K else 1.0
+            a = ra.standard_normal((batch, M, K)) * s
+            b = rb.standard_normal((batch, K, N)) * s
+        elif cfg == "c3":
+            a = ra.uniform(-0.5, 0.5, (batch, M, K))
+            b = rb.uniform(-0.5, 0.5, (batch, K, N))
+        elif cfg == "c4o":
+            a = np.empty((batch, M, K))
+            for q in range(batch):  # softmax rows of N(0,1) logits, one batch at a time
+                z = ra.standard_normal((M, K))
+                z -= z.max(axis=1, keepdims=True)
+                np.exp(z, out=z)
+                z /= z.sum(axis=1, keepdims=True)
+                a[q] = z
+            b = rb.uniform(-1, 1, (batch, K, N))
+        elif cfg == "c5":
+            a = ra.integers(-128, 128, (batch, M, K))
+            b = rb.integers(-128, 128, (batch, K, N))
+        else:
+            raise ValueError(cfg)
+    elif kind == "structured":
+        bidx = np.arange(batch)[:, None, None]
+        kk = np.arange(K)
+        if cfg in ("c1", "c2", "c5"):
+            a = np.broadcast_to((i % 16) + 0 * kk[None, :], (batch, M, K)).astype(np.float64)
+            b = np.broadcast_to((j % 8) + 0 * kk[:, None], (batch, K, N)).astype(np.float64)
+        elif cfg == "c3":
+            a = np.broadcast_to((kk[None, :] % 16 == i % 16).astype(np.float64), (batch, M, K))
+            b = np.broadcast_to((j % 8) + 0.0 * kk[:, None], (batch, K, N))
+        elif cfg == "c4s":
+            a = ((np.arange(M)[None, :, None] + bidx) % 16) + 0.0 * kk[None, None, :]
+            b = np.broadcast_to((j % 8) + 0.0 * kk[:, None], (batch, K, N))
+        elif cfg == "c4o":
+            a = (kk[None, None, :] == (np.arange(M)[None, :, None] + bidx) % K).astype(np.float64)
+            b = ((kk[None, :, None] + 3 * bidx + np.arange(N)[None, None, :]) % 64) - 32.0
+        else:
+            raise ValueError(cfg)
+    else:
+        raise ValueError(kind)
+
+    a = to_bits(np.ascontiguousarray(a).reshape(-1), in_t).reshape(batch, M, K)
+    b = to_bits(np.ascontiguousarray(b).reshape(-1), in_t).reshape(batch, K, N)
+    A = _storage(a, la, lda)
+    B = _storage(b, lb, ldb)
+    ldd = N + pad
+    p = Problem(cfg, M, N, K, batch, in_t, acc_t, out_t, la, lb, A, lda, sa if batch > 1 else 0,
+                B, ldb, sb if batch > 1 else 0, ldd=ldd, stride_d=M * ldd, meta=meta)
+    if cfg == "c1" and not with_c:
+        # c1 states C = 0 explicitly: pass a zero C operand.
+        p.C = np.zeros(batch * M * ldd, dtype=_NP_BITS[out_t])
+        p.ldc, p.stride_c = ldd, (M * ldd if batch > 1 else 0)
+    if with_c:
+        rc = _rng(cfg, 2, seed)
+        c_t = "i32" if in_t == "i8" else out_t
+        if c_t == "i32":
+            cv = rc.integers(-1000, 1000, batch * M * ldd)
+        else:
+            cv = rc.uniform(-1, 1, batch * M * ldd)
+            if kind == "structured":
+                cv = np.round(cv * 8)
+        p.C = to_bits(cv, c_t)
+        p.ldc, p.stride_c = ldd, (M * ldd if batch > 1 else 0)
+    return p
+
+
+def shrink(p: Problem, **kw) -> Problem:
+    return replace(p, **kw)
