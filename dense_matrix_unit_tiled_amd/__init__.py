@@ -1,0 +1,168 @@
+"""Python binding of ``libdmu.so`` (the gfx950 GEMM library, C ABI in include/dmu.h).
+
+Argument marshalling only: every step of the product runs in the library's HIP
+kernels.  The functions keep the C names (``dmu_gemm``, ``dmu_gemm_check``,
+``dmu_gemm_kernel_name``, ``dmu_status_string``, ``dmu_last_error``,
+``dmu_probe``, ``dmu_probe_info``); ``gemm_args`` fills the argument struct from
+torch tensors (or raw integer device addresses).  PyTorch supplies device
+memory and streams only.
+
+If ``libdmu.so`` has not been built, the first call raises ``RuntimeError``:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdmu.so")
+
+DMU_F16, DMU_BF16, DMU_F32, DMU_I8, DMU_I32 = 1, 2, 3, 4, 5
+DMU_ROW_MAJOR, DMU_COL_MAJOR = 0, 1
+DMU_OK, DMU_ERR_INVALID_ARG, DMU_ERR_UNSUPPORTED, DMU_ERR_HIP = 0, -1, -2, -3
+
+DMU_PROBE_MFMA_32x32x16_BF16 = 1
+DMU_PROBE_MFMA_32x32x16_F16 = 2
+DMU_PROBE_MFMA_16x16x32_BF16 = 3
+DMU_PROBE_MFMA_16x16x32_F16 = 4
+DMU_PROBE_MFMA_32x32x32_I8 = 5
+DMU_PROBE_MFMA_16x16x64_I8 = 6
+DMU_PROBE_LDS_READ_B128 = 10
+DMU_PROBE_LDS_READ_TR16 = 11
+DMU_PROBE_LDS_FRAG = 12
+DMU_PROBE_CVT_BF16 = 30
+DMU_PROBE_CVT_F16 = 31
+
+DTYPES = {"f16": DMU_F16, "bf16": DMU_BF16, "f32": DMU_F32, "i8": DMU_I8, "i32": DMU_I32}
+LAYOUTS = {"row": DMU_ROW_MAJOR, "col": DMU_COL_MAJOR}
+
+
+class dmu_gemm_args(ctypes.Structure):
+    """Mirror of ``struct dmu_gemm_args`` (include/dmu.h)."""
+
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("batch", ctypes.c_int64),
+        ("in_type", ctypes.c_int32), ("acc_type", ctypes.c_int32), ("out_type", ctypes.c_int32),
+        ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
+        ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("stride_a", ctypes.c_int64),
+        ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+        ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("stride_c", ctypes.c_int64),
+        ("D", ctypes.c_void_p), ("ldd", ctypes.c_int64), ("stride_d", ctypes.c_int64),
+    ]
+
+
+class DmuError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{dmu_status_string(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with dense_matrix_unit_tiled_amd.build.build()")
+    # PyTorch ships its own HIP runtime.  Importing it first makes the library's
+    # libamdhip64 dependency resolve to that already-loaded copy, so the process
+    # holds one HIP runtime and torch's device pointers and streams are valid here.
+    import torch  # noqa: F401
+
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(dmu_gemm_args)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.dmu_gemm.argtypes, lib.dmu_gemm.restype = [P, vp], i32
+    lib.dmu_gemm_check.argtypes, lib.dmu_gemm_check.restype = [P], i32
+    lib.dmu_gemm_kernel_name.argtypes, lib.dmu_gemm_kernel_name.restype = [P], ctypes.c_char_p
+    lib.dmu_status_string.argtypes, lib.dmu_status_string.restype = [i32], ctypes.c_char_p
+    lib.dmu_last_error.argtypes, lib.dmu_last_error.restype = [], ctypes.c_char_p
+    lib.dmu_probe.argtypes, lib.dmu_probe.restype = [i32, vp, vp, vp, vp], i32
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.dmu_probe_info.argtypes, lib.dmu_probe_info.restype = [i32, ip, ip, ip, ip, ip], i32
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises RuntimeError when it is not built)."""
+    return _load()
+
+
+def _addr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gemm_args(M, N, K, A, lda, B, ldb, D, ldd, *, in_type, out_type, acc_type=None,
+              layout_a="row", layout_b="row", batch=1, stride_a=0, stride_b=0, C=None, ldc=0,
+              stride_c=0, stride_d=0) -> dmu_gemm_args:
+    """Fill a dmu_gemm_args from tensors/addresses and type/layout names."""
+    if acc_type is None:
+        acc_type = "i32" if in_type == "i8" else "f32"
+    a = dmu_gemm_args()
+    a.M, a.N, a.K, a.batch = M, N, K, batch
+    a.in_type, a.acc_type, a.out_type = DTYPES[in_type], DTYPES[acc_type], DTYPES[out_type]
+    a.layout_a, a.layout_b = LAYOUTS[layout_a], LAYOUTS[layout_b]
+    a.A, a.lda, a.stride_a = _addr(A), lda, stride_a
+    a.B, a.ldb, a.stride_b = _addr(B), ldb, stride_b
+    a.C, a.ldc, a.stride_c = _addr(C), ldc, stride_c
+    a.D, a.ldd, a.stride_d = _addr(D), ldd, stride_d
+    return a
+
+
+def dmu_gemm(args: dmu_gemm_args, stream=None, check: bool = True) -> int:
+    """Launch D = A*B + C on ``stream`` (default: torch's current stream)."""
+    st = _load().dmu_gemm(ctypes.byref(args), _stream(stream))
+    if check and st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return st
+
+
+def dmu_gemm_check(args: dmu_gemm_args) -> int:
+    return _load().dmu_gemm_check(ctypes.byref(args))
+
+
+def dmu_gemm_kernel_name(args: dmu_gemm_args) -> str | None:
+    r = _load().dmu_gemm_kernel_name(ctypes.byref(args))
+    return None if r is None else r.decode()
+
+
+def dmu_status_string(status: int) -> str:
+    return _load().dmu_status_string(status).decode()
+
+
+def dmu_last_error() -> str:
+    return _load().dmu_last_error().decode()
+
+
+def dmu_probe(variant: int, in0, in1, out, stream=None, check: bool = True) -> int:
+    st = _load().dmu_probe(variant, _addr(in0), _addr(in1), _addr(out), _stream(stream))
+    if check and st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return st
+
+
+def dmu_probe_info(variant: int):
+    """(m, n, k, in_type, regs_per_lane) of a probe variant."""
+    v = [ctypes.c_int() for _ in range(5)]
+    st = _load().dmu_probe_info(variant, *[ctypes.byref(x) for x in v])
+    if st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return tuple(x.value for x in v)

@@ -1,0 +1,332 @@
+// C ABI of the GEMM library: argument validation, kernel selection, launch.
+//
+// Validation follows the host entry point of "Tensor Cores, CUTLASS and CuTe"
+// section 4.4 (type, rank and layout are checked before an untyped pointer is
+// reinterpreted), extended to what that entry point leaves to its caller:
+// ragged sizes, any element alignment, leading dimensions and batch strides
+// (section 7's strided-batched form), and aliasing of the output.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/dmu.h"
+#include "dmu_host.hpp"
+
+namespace dmu {
+
+static thread_local char g_err[512];
+
+void set_error(const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+int check_launch(const char *what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error("%s: kernel launch failed: %s", what, hipGetErrorString(e));
+        return DMU_ERR_HIP;
+    }
+    return DMU_OK;
+}
+
+namespace {
+
+struct Plan {
+    bool launch;     // false: nothing to do (empty problem)
+    LaunchCfg cfg;
+    GemmParams p;
+    int combo;       // index into the launcher table
+    const char *name;
+};
+
+constexpr int64_t LIM31 = (int64_t)1 << 31;
+
+int elem_bytes(int t) { return (t == DMU_F32 || t == DMU_I32) ? 4 : (t == DMU_I8 ? 1 : 2); }
+
+// Supported (in, acc, out) triples -> launcher index.
+int combo_of(int in, int acc, int out)
+{
+    if (in == DMU_F16 && acc == DMU_F32 && out == DMU_F32) return 0;
+    if (in == DMU_F16 && acc == DMU_F32 && out == DMU_F16) return 1;
+    if (in == DMU_F16 && acc == DMU_F16 && out == DMU_F16) return 1; // fp32 sum, one rounding to fp16
+    if (in == DMU_BF16 && acc == DMU_F32 && out == DMU_BF16) return 2;
+    if (in == DMU_BF16 && acc == DMU_F32 && out == DMU_F32) return 3;
+    if (in == DMU_I8 && acc == DMU_I32 && out == DMU_I32) return 4;
+    return -1;
+}
+
+const char *const COMBO_NAMES[] = {"f16_f32", "f16_f16", "bf16_bf16", "bf16_f32", "i8_i32"};
+
+// Names of every kernel variant, built once (thread-safe static init).
+struct NameTable {
+    char at[4][3][3][5][48];
+};
+
+const NameTable &kernel_names()
+{
+    static const NameTable table = [] {
+        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64"};
+        static const char *const MODE_NAMES[] = {"k16", "k4", "t16"};
+        NameTable t;
+        for (int a = 0; a < 4; ++a)
+            for (int x = 0; x < 3; ++x)
+                for (int y = 0; y < 3; ++y)
+                    for (int c = 0; c < 5; ++c)
+                        snprintf(t.at[a][x][y][c], sizeof(t.at[a][x][y][c]), "mfma_%s_%s_%s_%s", TILE_NAMES[a],
+                                 a == TILE_GENERIC ? "any" : MODE_NAMES[x], a == TILE_GENERIC ? "any" : MODE_NAMES[y],
+                                 COMBO_NAMES[c]);
+        return t;
+    }();
+    return table;
+}
+
+// Elements spanned by a rows x cols matrix stored with `layout` and `ld`.
+int64_t extent(int layout, int64_t rows, int64_t cols, int64_t ld)
+{
+    if (rows == 0 || cols == 0)
+        return 0;
+    return layout == DMU_ROW_MAJOR ? (rows - 1) * ld + cols : (cols - 1) * ld + rows;
+}
+
+// Byte range [lo, hi) covered by all batch slices of an operand.
+void span(const void *ptr, int64_t stride, int64_t batch, int64_t ext, int esz, uintptr_t *lo, uintptr_t *hi)
+{
+    *lo = (uintptr_t)ptr;
+    *hi = *lo + (uintptr_t)(((batch - 1) * stride + ext) * esz);
+}
+
+bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+bool aligned(const void *p, int64_t ld, int64_t stride, int esz, int vb)
+{
+    return ((uintptr_t)p % vb) == 0 && (ld * esz) % vb == 0 && (stride * esz) % vb == 0;
+}
+
+// Load mode of one operand: -1 if only the generic kernel can read it.
+//  kc: K is the contiguous dimension; mn: the operand's M (or N) size.
+int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, int64_t K, int64_t mn)
+{
+    if (kc) {
+        if (aligned(p, ld, stride, esz, 16) && (K * esz) % 16 == 0)
+            return KC16;
+        if (aligned(p, ld, stride, esz, 4) && (K * esz) % 4 == 0)
+            return KC4;
+        return -1;
+    }
+    if (esz == 2 && aligned(p, ld, stride, esz, 16) && mn % 8 == 0)
+        return MC16;
+    return -1;
+}
+
+int validate(const dmu_gemm_args *a, Plan *plan)
+{
+    memset(plan, 0, sizeof(*plan));
+    if (!a) {
+        set_error("args is NULL");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->M < 0 || a->N < 0 || a->K < 0 || a->batch < 0) {
+        set_error("negative size (M=%lld N=%lld K=%lld batch=%lld)", (long long)a->M, (long long)a->N,
+                  (long long)a->K, (long long)a->batch);
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->M >= LIM31 || a->N >= LIM31 || a->K >= LIM31 || a->batch >= LIM31) {
+        set_error("size of 2^31 or more is not supported");
+        return DMU_ERR_UNSUPPORTED;
+    }
+    const int combo = combo_of(a->in_type, a->acc_type, a->out_type);
+    if (combo < 0) {
+        set_error("unsupported (in, acc, out) types (%d, %d, %d)", a->in_type, a->acc_type, a->out_type);
+        return DMU_ERR_UNSUPPORTED;
+    }
+    if ((a->layout_a != DMU_ROW_MAJOR && a->layout_a != DMU_COL_MAJOR) ||
+        (a->layout_b != DMU_ROW_MAJOR && a->layout_b != DMU_COL_MAJOR)) {
+        set_error("layout must be DMU_ROW_MAJOR or DMU_COL_MAJOR");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->stride_a < 0 || a->stride_b < 0 || a->stride_c < 0 || a->stride_d < 0) {
+        set_error("negative batch stride");
+        return DMU_ERR_INVALID_ARG;
+    }
+    plan->combo = combo;
+    if (a->M == 0 || a->N == 0 || a->batch == 0) {
+        plan->launch = false;
+        return DMU_OK;
+    }
+    const int64_t M = a->M, N = a->N, K = a->K, batch = a->batch;
+    const int esz = elem_bytes(a->in_type), osz = elem_bytes(a->out_type);
+    // leading dimensions (BLAS rule: at least the contiguous extent, at least 1)
+    const int64_t need_lda = a->layout_a == DMU_ROW_MAJOR ? K : M;
+    const int64_t need_ldb = a->layout_b == DMU_ROW_MAJOR ? N : K;
+    if (a->lda < (need_lda > 1 ? need_lda : 1) || a->ldb < (need_ldb > 1 ? need_ldb : 1)) {
+        set_error("lda=%lld / ldb=%lld below the contiguous extent (%lld / %lld)", (long long)a->lda,
+                  (long long)a->ldb, (long long)need_lda, (long long)need_ldb);
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->ldd < N || (a->C && a->ldc < N)) {
+        set_error("ldd=%lld / ldc=%lld below N=%lld", (long long)a->ldd, (long long)a->ldc, (long long)N);
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (!a->D || (K > 0 && (!a->A || !a->B))) {
+        set_error("NULL operand pointer");
+        return DMU_ERR_INVALID_ARG;
+    }
+    const int64_t ext_d = extent(DMU_ROW_MAJOR, M, N, a->ldd);
+    if (batch > 1 && a->stride_d < ext_d) {
+        set_error("stride_d=%lld lets batch slices of D overlap (needs >= %lld)", (long long)a->stride_d,
+                  (long long)ext_d);
+        return DMU_ERR_INVALID_ARG;
+    }
+    // aliasing: D must not overlap A or B; C may only coincide with D exactly
+    uintptr_t d0, d1;
+    span(a->D, a->stride_d, batch, ext_d, osz, &d0, &d1);
+    if (K > 0) {
+        uintptr_t x0, x1;
+        span(a->A, a->stride_a, batch, extent(a->layout_a, M, K, a->lda), esz, &x0, &x1);
+        if (overlap(d0, d1, x0, x1)) {
+            set_error("D overlaps A");
+            return DMU_ERR_INVALID_ARG;
+        }
+        span(a->B, a->stride_b, batch, extent(a->layout_b, K, N, a->ldb), esz, &x0, &x1);
+        if (overlap(d0, d1, x0, x1)) {
+            set_error("D overlaps B");
+            return DMU_ERR_INVALID_ARG;
+        }
+    }
+    if (a->C) {
+        uintptr_t c0, c1;
+        span(a->C, a->stride_c, batch, extent(DMU_ROW_MAJOR, M, N, a->ldc), osz, &c0, &c1);
+        const bool same = a->C == a->D && a->ldc == a->ldd && a->stride_c == a->stride_d;
+        if (!same && overlap(d0, d1, c0, c1)) {
+            set_error("C partially overlaps D (only C == D with equal ldc/stride is allowed)");
+            return DMU_ERR_INVALID_ARG;
+        }
+    }
+    if (((uintptr_t)a->D % osz) || (a->C && ((uintptr_t)a->C % osz)) || ((uintptr_t)a->A % esz) ||
+        ((uintptr_t)a->B % esz)) {
+        set_error("pointer not aligned to its element size");
+        return DMU_ERR_INVALID_ARG;
+    }
+
+    // kernel selection
+    const bool a_kc = a->layout_a == DMU_ROW_MAJOR, b_kc = a->layout_b == DMU_COL_MAJOR;
+    int amode = K > 0 ? operand_mode(a_kc, a->A, a->lda, batch > 1 ? a->stride_a : 0, esz, K, M) : -1;
+    int bmode = K > 0 ? operand_mode(b_kc, a->B, a->ldb, batch > 1 ? a->stride_b : 0, esz, K, N) : -1;
+    int tile = TILE_GENERIC;
+    const char *env = getenv("DMU_FORCE_KERNEL");
+    const bool force_generic = env && strcmp(env, "generic") == 0;
+    if (amode >= 0 && bmode >= 0 && !force_generic) {
+        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256) * batch;
+        if (N <= 128 && M > 128)
+            tile = TILE_256x128;
+        else if (big >= 240)
+            tile = TILE_256x256;
+        else
+            tile = TILE_128x128;
+        if (env && strcmp(env, "256x256") == 0) tile = TILE_256x256;
+        if (env && strcmp(env, "256x128") == 0) tile = TILE_256x128;
+        if (env && strcmp(env, "128x128") == 0) tile = TILE_128x128;
+    }
+    const int64_t bm = tile_bm(tile), bn = tile_bn(tile);
+    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+    if (tm * tn * batch >= ((int64_t)1 << 32)) {
+        set_error("too many tiles for one launch");
+        return DMU_ERR_UNSUPPORTED;
+    }
+    plan->launch = true;
+    plan->cfg.tile = tile;
+    plan->cfg.amode = amode < 0 ? 0 : amode;
+    plan->cfg.bmode = bmode < 0 ? 0 : bmode;
+    plan->name = kernel_names().at[tile][plan->cfg.amode][plan->cfg.bmode][combo];
+    GemmParams &p = plan->p;
+    p.A = static_cast<const char *>(a->A);
+    p.B = static_cast<const char *>(a->B);
+    p.C = static_cast<const char *>(a->C);
+    p.D = static_cast<char *>(a->D);
+    p.lda = a->lda;
+    p.ldb = a->ldb;
+    p.ldc = a->ldc;
+    p.ldd = a->ldd;
+    p.stride_a = batch > 1 ? a->stride_a : 0;
+    p.stride_b = batch > 1 ? a->stride_b : 0;
+    p.stride_c = batch > 1 ? a->stride_c : 0;
+    p.stride_d = batch > 1 ? a->stride_d : 0;
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.batch = (int32_t)batch;
+    p.tiles_m = (int32_t)tm;
+    p.tiles_n = (int32_t)tn;
+    p.total_tiles = (uint32_t)(tm * tn * batch);
+    p.a_kc = a_kc;
+    p.b_kc = b_kc;
+    const bool c_vec = !a->C || (((uintptr_t)a->C % (4 * osz)) == 0 && a->ldc % 4 == 0 && p.stride_c % 4 == 0);
+    p.d_vec4 = ((uintptr_t)a->D % (4 * osz)) == 0 && a->ldd % 4 == 0 && p.stride_d % 4 == 0 && c_vec;
+    return DMU_OK;
+}
+
+} // namespace
+} // namespace dmu
+
+using namespace dmu;
+
+extern "C" int dmu_gemm_check(const dmu_gemm_args *args)
+{
+    clear_error();
+    Plan plan;
+    return validate(args, &plan);
+}
+
+extern "C" const char *dmu_gemm_kernel_name(const dmu_gemm_args *args)
+{
+    clear_error();
+    Plan plan;
+    if (validate(args, &plan) != DMU_OK || !plan.launch)
+        return nullptr;
+    return plan.name;
+}
+
+extern "C" int dmu_gemm(const dmu_gemm_args *args, void *stream)
+{
+    clear_error();
+    Plan plan;
+    int rc = validate(args, &plan);
+    if (rc != DMU_OK || !plan.launch)
+        return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (plan.combo) {
+    case 0: e = launch_f16_f32(plan.cfg, plan.p, s); break;
+    case 1: e = launch_f16_f16(plan.cfg, plan.p, s); break;
+    case 2: e = launch_bf16_bf16(plan.cfg, plan.p, s); break;
+    case 3: e = launch_bf16_f32(plan.cfg, plan.p, s); break;
+    default: e = launch_i8_i32(plan.cfg, plan.p, s); break;
+    }
+    if (e != hipSuccess) {
+        set_error("dmu_gemm: launch of %s failed: %s", plan.name, hipGetErrorString(e));
+        return DMU_ERR_HIP;
+    }
+    return DMU_OK;
+}
+
+extern "C" const char *dmu_status_string(int status)
+{
+    switch (status) {
+    case DMU_OK: return "DMU_OK";
+    case DMU_ERR_INVALID_ARG: return "DMU_ERR_INVALID_ARG: invalid argument";
+    case DMU_ERR_UNSUPPORTED: return "DMU_ERR_UNSUPPORTED: unsupported type, variant or size";
+    case DMU_ERR_HIP: return "DMU_ERR_HIP: HIP runtime error";
+    default: return "unknown dmu status";
+    }
+}
+
+extern "C" const char *dmu_last_error(void) { return g_err; }

@@ -1,0 +1,42 @@
+// Host-side helpers of the C ABI: thread-local error text, launch checks and
+// the per-type launcher entry points implemented in dmu_launch_*.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dmu_device.hpp"
+
+namespace dmu {
+
+void set_error(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+// DMU_OK, or DMU_ERR_HIP with the runtime's message when the last launch failed.
+int check_launch(const char *what);
+
+// Kernel shapes of the tiled kernel (gemm_mfma) and the fallback (gemm_generic).
+enum TileCfg {
+    TILE_256x256 = 0, // 4 wavefronts 2 x 2, 128 x 128 each
+    TILE_256x128 = 1, // 4 wavefronts 2 x 2, 128 x 64 each
+    TILE_128x128 = 2, // 4 wavefronts 2 x 2, 64 x 64 each
+    TILE_GENERIC = 3  // 64 x 64, element loads
+};
+
+struct LaunchCfg {
+    int tile;  // TileCfg
+    int amode; // Mode of A (ignored for TILE_GENERIC)
+    int bmode; // Mode of B
+};
+
+inline int tile_bm(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_128x128 ? 128 : 256); }
+inline int tile_bn(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_256x256 ? 256 : 128); }
+
+// One launcher per (input type, output type); each returns hipSuccess or the
+// launch error.  The grid is p.total_tiles workgroups of 256 threads.
+hipError_t launch_f16_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_f16_f16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_bf16_bf16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_bf16_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_i8_i32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+
+} // namespace dmu

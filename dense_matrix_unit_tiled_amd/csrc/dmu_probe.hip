@@ -1,0 +1,199 @@
+// Single-wavefront layout probes: the gfx950 counterpart of the isolated
+// layout experiment (KingOfEgg, sections 6-7), which checks one matrix
+// instruction and its fragment loads lane by lane and register by register
+// before they are used in a large kernel.
+#include <hip/hip_runtime.h>
+
+#include "../../include/dmu.h"
+#include "dmu_device.hpp"
+#include "dmu_host.hpp"
+
+namespace dmu {
+
+// Operand fragment of an m x k (row-major, in_type) matrix X for lane l:
+// row l % m, the 16 bytes starting at byte 16 * (l / m) of that row.
+__device__ __forceinline__ u32x4 probe_frag(const char *x, int m, int row_bytes, uint32_t lane)
+{
+    const uint32_t row = lane % (uint32_t)m, part = lane / (uint32_t)m;
+    return *reinterpret_cast<const u32x4 *>(x + row * row_bytes + part * 16);
+}
+
+template <int V>
+__global__ void __launch_bounds__(64) probe_mfma(const char *a, const char *bt, uint32_t *out)
+{
+    const uint32_t l = threadIdx.x;
+    if (V == DMU_PROBE_MFMA_32x32x16_BF16 || V == DMU_PROBE_MFMA_32x32x16_F16) {
+        const u32x4 x = probe_frag(a, 32, 32, l), y = probe_frag(bt, 32, 32, l);
+        f32x16 c = {};
+        if (V == DMU_PROBE_MFMA_32x32x16_BF16)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y),
+                                                        c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
+                                                       0, 0, 0);
+        for (int r = 0; r < 16; ++r)
+            out[l * 16 + r] = __builtin_bit_cast(uint32_t, c[r]);
+    } else if (V == DMU_PROBE_MFMA_16x16x32_BF16 || V == DMU_PROBE_MFMA_16x16x32_F16) {
+        const u32x4 x = probe_frag(a, 16, 64, l), y = probe_frag(bt, 16, 64, l);
+        f32x4 c = {};
+        if (V == DMU_PROBE_MFMA_16x16x32_BF16)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y),
+                                                        c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
+                                                       0, 0, 0);
+        for (int r = 0; r < 4; ++r)
+            out[l * 4 + r] = __builtin_bit_cast(uint32_t, c[r]);
+    } else if (V == DMU_PROBE_MFMA_32x32x32_I8) {
+        const u32x4 x = probe_frag(a, 32, 32, l), y = probe_frag(bt, 32, 32, l);
+        i32x16 c = {};
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, x), __builtin_bit_cast(i32x4, y), c, 0, 0,
+                                                  0);
+        for (int r = 0; r < 16; ++r)
+            out[l * 16 + r] = (uint32_t)c[r];
+    } else if (V == DMU_PROBE_MFMA_16x16x64_I8) {
+        const u32x4 x = probe_frag(a, 16, 64, l), y = probe_frag(bt, 16, 64, l);
+        i32x4 c = {};
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, x), __builtin_bit_cast(i32x4, y), c, 0, 0,
+                                                  0);
+        for (int r = 0; r < 4; ++r)
+            out[l * 4 + r] = (uint32_t)c[r];
+    }
+}
+
+// LDS image of 4096 bytes: each of the 64 lanes copies 64 bytes.
+__device__ __forceinline__ void probe_fill_lds(char *lds, const char *img, uint32_t l)
+{
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x4 *>(lds + l * 64 + q * 16) = *reinterpret_cast<const u32x4 *>(img + l * 64 + q * 16);
+}
+
+__global__ void __launch_bounds__(64) probe_lds_b128(const char *img, const int32_t *addr, uint32_t *out)
+{
+    __shared__ __attribute__((aligned(16))) char lds[4096];
+    const uint32_t l = threadIdx.x;
+    probe_fill_lds(lds, img, l);
+    __syncthreads();
+    const uint32_t off = (uint32_t)addr[l] & (4096u - 16u); // aligned and in bounds
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + off);
+    for (int e = 0; e < 4; ++e)
+        out[l * 4 + e] = v[e];
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(64) probe_lds_tr16(const char *img, const int32_t *addr, uint32_t *out)
+{
+    __shared__ __attribute__((aligned(16))) char lds[4096];
+    const uint32_t l = threadIdx.x;
+    probe_fill_lds(lds, img, l);
+    __syncthreads();
+    const uint32_t off = (uint32_t)addr[l] & (4096u - 8u); // aligned and in bounds
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds + off));
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    out[l * 2 + 0] = w[0];
+    out[l * 2 + 1] = w[1];
+}
+
+// The GEMM kernels' LDS tile format: a 32-row x 128-byte tile is written with
+// their swizzled addressing and read back with their fragment reads.
+__global__ void __launch_bounds__(64) probe_lds_frag(const char *tile, uint32_t *out)
+{
+    __shared__ __attribute__((aligned(16))) char lds[32 * 128];
+    const uint32_t l = threadIdx.x;
+    for (int q = 0; q < 4; ++q) { // 256 chunks of 16 bytes
+        const uint32_t idx = l + 64u * q, row = idx / 8u, cb = (idx % 8u) * 16u;
+        *reinterpret_cast<u32x4 *>(lds + lds_off(row, cb)) =
+            *reinterpret_cast<const u32x4 *>(tile + row * 128u + cb);
+    }
+    __syncthreads();
+    for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 v = frag_read(lds, 0, ks, l);
+        for (int e = 0; e < 4; ++e)
+            out[(l * 4 + ks) * 4 + e] = v[e];
+    }
+}
+
+template <int O>
+__global__ void __launch_bounds__(64) probe_cvt(const float *in, uint16_t *out)
+{
+    const uint32_t l = threadIdx.x;
+    for (int q = 0; q < 4; ++q) {
+        const auto h = Out<O>::from_acc(in[l * 4 + q]);
+        out[l * 4 + q] = __builtin_bit_cast(uint16_t, h);
+    }
+}
+
+} // namespace dmu
+
+using namespace dmu;
+
+extern "C" int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type, int *regs)
+{
+    int mm = 0, nn = 0, kk = 0, t = 0, r = 0;
+    switch (variant) {
+    case DMU_PROBE_MFMA_32x32x16_BF16: mm = 32, nn = 32, kk = 16, t = DMU_BF16, r = 16; break;
+    case DMU_PROBE_MFMA_32x32x16_F16: mm = 32, nn = 32, kk = 16, t = DMU_F16, r = 16; break;
+    case DMU_PROBE_MFMA_16x16x32_BF16: mm = 16, nn = 16, kk = 32, t = DMU_BF16, r = 4; break;
+    case DMU_PROBE_MFMA_16x16x32_F16: mm = 16, nn = 16, kk = 32, t = DMU_F16, r = 4; break;
+    case DMU_PROBE_MFMA_32x32x32_I8: mm = 32, nn = 32, kk = 32, t = DMU_I8, r = 16; break;
+    case DMU_PROBE_MFMA_16x16x64_I8: mm = 16, nn = 16, kk = 64, t = DMU_I8, r = 4; break;
+    case DMU_PROBE_LDS_READ_B128: r = 4; break;
+    case DMU_PROBE_LDS_READ_TR16: r = 2; break;
+    case DMU_PROBE_LDS_FRAG: r = 16; break;
+    case DMU_PROBE_CVT_BF16: t = DMU_F32, r = 2; break; /* 4 halves per lane */
+    case DMU_PROBE_CVT_F16: t = DMU_F32, r = 2; break;
+    default:
+        set_error("dmu_probe_info: unknown probe variant %d", variant);
+        return DMU_ERR_UNSUPPORTED;
+    }
+    if (m) *m = mm;
+    if (n) *n = nn;
+    if (k) *k = kk;
+    if (in_type) *in_type = t;
+    if (regs) *regs = r;
+    return DMU_OK;
+}
+
+extern "C" int dmu_probe(int variant, const void *in0, const void *in1, void *out, void *stream)
+{
+    clear_error();
+    int rc = dmu_probe_info(variant, nullptr, nullptr, nullptr, nullptr, nullptr);
+    if (rc != DMU_OK)
+        return rc;
+    const bool needs_in1 = variant <= DMU_PROBE_LDS_READ_TR16;
+    if (!in0 || !out || (needs_in1 && !in1)) {
+        set_error("dmu_probe: null pointer");
+        return DMU_ERR_INVALID_ARG;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const char *a = static_cast<const char *>(in0), *b = static_cast<const char *>(in1);
+    uint32_t *o = static_cast<uint32_t *>(out);
+    switch (variant) {
+#define DMU_PROBE_MFMA_CASE(V) \
+    case V: hipLaunchKernelGGL(probe_mfma<V>, dim3(1), dim3(64), 0, s, a, b, o); break;
+        DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_32x32x16_BF16)
+        DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_32x32x16_F16)
+        DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_16x16x32_BF16)
+        DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_16x16x32_F16)
+        DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_32x32x32_I8)
+        DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_16x16x64_I8)
+#undef DMU_PROBE_MFMA_CASE
+    case DMU_PROBE_LDS_READ_B128:
+        hipLaunchKernelGGL(probe_lds_b128, dim3(1), dim3(64), 0, s, a, reinterpret_cast<const int32_t *>(b), o);
+        break;
+    case DMU_PROBE_LDS_READ_TR16:
+        hipLaunchKernelGGL(probe_lds_tr16, dim3(1), dim3(64), 0, s, a, reinterpret_cast<const int32_t *>(b), o);
+        break;
+    case DMU_PROBE_LDS_FRAG: hipLaunchKernelGGL(probe_lds_frag, dim3(1), dim3(64), 0, s, a, o); break;
+    case DMU_PROBE_CVT_BF16:
+        hipLaunchKernelGGL(probe_cvt<BF16>, dim3(1), dim3(64), 0, s, reinterpret_cast<const float *>(a),
+                           reinterpret_cast<uint16_t *>(o));
+        break;
+    case DMU_PROBE_CVT_F16:
+        hipLaunchKernelGGL(probe_cvt<F16>, dim3(1), dim3(64), 0, s, reinterpret_cast<const float *>(a),
+                           reinterpret_cast<uint16_t *>(o));
+        break;
+    }
+    return check_launch("dmu_probe");
+}

@@ -1,0 +1,196 @@
+/*
+ * dmu.h -- dense matrix-unit GEMM on AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The library computes the tiled dense product
+ *
+ *     D[b] = A[b] * B[b] + C[b]        for b = 0 .. batch-1
+ *
+ * on the chip's matrix cores (MFMA), with fp16/bf16 inputs and fp32
+ * accumulation, an fp16-output ("fp16 accumulate") variant and an
+ * int8 -> int32 variant.
+ *
+ * Sources for the operation and its conventions:
+ *   - "Tensor Cores, CUTLASS and CuTe", section 2.1 (one matrix instruction is
+ *     D = A*B + C with low-precision inputs and an fp32/int32 accumulator; the
+ *     table of input/accumulator type pairs, including fp16 accumulation and
+ *     int8 -> int32), section 4.1 (the 4096^3 bf16 problem: bf16 in, fp32
+ *     accumulate, bf16 out; "TN" = A row-major M x K, B stored N x K row-major),
+ *     section 4.4 (the host entry point checks device, type, rank and
+ *     contiguity before it reinterprets untyped pointers) and section 7 (the
+ *     strided-batched BLAS form alpha*A*B + beta*C).
+ *   - "hgemm_mma_m16n8k16_mma2x4_warp4x4_kernel" walkthrough, section 1.1
+ *     (C = A x B with A M x K and B K x N, both row-major: "NN").
+ *   - Layout-experiment post (KingOfEgg, RTX 5080), section 3 (D = A x B + C;
+ *     an fp32 accumulator is the floor for long sums).
+ *
+ * Every entry point is a plain C function on plain pointers and sizes.  Device
+ * buffers are owned by the caller; the library allocates no device memory,
+ * keeps no pointer after a call returns, and has no mutable global state other
+ * than a thread-local error message.  All entry points are thread-safe.
+ */
+#ifndef DMU_H
+#define DMU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+    DMU_F16 = 1,  /* IEEE binary16                       */
+    DMU_BF16 = 2, /* bfloat16 (upper half of a binary32) */
+    DMU_F32 = 3,  /* IEEE binary32                       */
+    DMU_I8 = 4,   /* signed 8-bit integer                */
+    DMU_I32 = 5   /* signed 32-bit integer               */
+} dmu_dtype;
+
+/* Storage order of a logical matrix X(r, c) with leading dimension ld (elements):
+ *   DMU_ROW_MAJOR: X(r, c) is at r*ld + c,   ld >= max(1, cols)
+ *   DMU_COL_MAJOR: X(r, c) is at r + c*ld,   ld >= max(1, rows)            */
+typedef enum { DMU_ROW_MAJOR = 0, DMU_COL_MAJOR = 1 } dmu_layout;
+
+/* Return codes.  Argument errors are reported before any HIP call is made. */
+typedef enum {
+    DMU_OK = 0,
+    DMU_ERR_INVALID_ARG = -1, /* bad size, pointer, leading dimension, stride or overlap */
+    DMU_ERR_UNSUPPORTED = -2, /* a type/variant the library does not implement          */
+    DMU_ERR_HIP = -3          /* the HIP runtime reported an error for a launch         */
+} dmu_status;
+
+/*
+ * One (optionally strided-batched) product.
+ *
+ *  M, N, K, batch   sizes, each >= 0.  M, N or batch == 0: nothing is done.
+ *                   K == 0: D = C (or 0 when C is NULL).
+ *  in_type          type of A and B: DMU_F16, DMU_BF16 or DMU_I8.
+ *  acc_type         accumulator: DMU_F32 (fp16/bf16 in), DMU_F16 (fp16 in,
+ *                   "fp16 accumulate") or DMU_I32 (int8 in).
+ *  out_type         type of C and D.  Supported (in, acc, out) triples:
+ *                     (F16,F32,F32) (F16,F32,F16) (F16,F16,F16)
+ *                     (BF16,F32,BF16) (BF16,F32,F32) (I8,I32,I32)
+ *                   For acc_type == DMU_F16 the matrix cores still sum the
+ *                   exact products in fp32 and the result is rounded once to
+ *                   fp16 (gfx950 has no fp16-accumulating matrix
+ *                   instruction); this is at least as accurate as a true fp16
+ *                   accumulation.
+ *  layout_a/_b      storage order of A (logical M x K) and B (logical K x N).
+ *                   Row-major B is the "NN" case, column-major B (B stored as
+ *                   an N x K row-major array) the "TN" case.
+ *  A, lda, stride_a device pointer, leading dimension and batch stride, in
+ *  B, ldb, stride_b elements.  Strides >= 0 (0 broadcasts one matrix to every
+ *                   batch).  Any element-aligned pointer and any leading
+ *                   dimension satisfying the layout rule is accepted; the
+ *                   library picks the widest legal vector access.
+ *  C, ldc, stride_c optional addend (NULL => 0), row-major M x N of out_type,
+ *                   ldc >= N.  C may be the same buffer as D with the same ldc
+ *                   and stride (in-place accumulate), but may not partially
+ *                   overlap it.
+ *  D, ldd, stride_d output, row-major M x N of out_type, ldd >= N.  For
+ *                   batch > 1, stride_d >= (M-1)*ldd + N so batches do not
+ *                   overlap.  D may not overlap A or B.
+ *
+ * Rounding: fp32 -> fp16/bf16 output conversion is round-to-nearest-even;
+ * subnormal inputs and outputs are kept (not flushed).  int32 results wrap
+ * modulo 2^32 (no overflow is possible for K <= 2^17).
+ * M, N, K and batch must each be below 2^31 (larger: DMU_ERR_UNSUPPORTED).
+ */
+typedef struct dmu_gemm_args {
+    int64_t M, N, K, batch;
+    int32_t in_type, acc_type, out_type; /* dmu_dtype  */
+    int32_t layout_a, layout_b;          /* dmu_layout */
+    const void *A;
+    int64_t lda, stride_a;
+    const void *B;
+    int64_t ldb, stride_b;
+    const void *C;
+    int64_t ldc, stride_c;
+    void *D;
+    int64_t ldd, stride_d;
+} dmu_gemm_args;
+
+/*
+ * D = A*B + C as described above, enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream).  Asynchronous: returns once the kernel is launched.
+ * Errors: DMU_ERR_INVALID_ARG / DMU_ERR_UNSUPPORTED before any HIP call (the
+ * message is in dmu_last_error()); DMU_ERR_HIP if the launch fails.  Nothing
+ * is written to D when an error is returned before the launch.
+ */
+int dmu_gemm(const dmu_gemm_args *args, void *stream);
+
+/*
+ * Validate `args` exactly as dmu_gemm does, without touching the GPU.
+ * Returns DMU_OK or the error dmu_gemm would return before launching.
+ */
+int dmu_gemm_check(const dmu_gemm_args *args);
+
+/*
+ * Name of the kernel variant dmu_gemm would launch for `args` (a static
+ * string, e.g. "mfma_256x256_nn_bf16"), or NULL if the arguments are invalid
+ * or the call would launch nothing.  Host-only; no GPU access.
+ */
+const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
+
+/* Static description of a return code. */
+const char *dmu_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none).  The pointer
+ * stays valid until the next call into the library on this thread. */
+const char *dmu_last_error(void);
+
+/*
+ * Single-wavefront layout probes (test support).
+ *
+ * The layout experiment (KingOfEgg, sections 4-7) pins the matrix
+ * instruction's fragment ownership and the shared-memory fragment-load
+ * protocol with one warp and hand-made data before they go into a big
+ * kernel.  These probes do the same for the gfx950 instructions and the LDS
+ * tile format the GEMM kernels use; each runs one wavefront of 64 lanes:
+ *
+ *  variant                  in0 (device)          in1 (device)       out (device)
+ *  DMU_PROBE_MFMA_*         A, m x k row-major    B^T, n x k         raw accumulators,
+ *                           (in_type bits)        row-major          [64 lanes][regs] 32-bit
+ *  DMU_PROBE_LDS_READ_B128  LDS image, 4096 B     int32 byte         [64][16 bytes]
+ *  DMU_PROBE_LDS_READ_TR16  LDS image, 4096 B     address per lane   [64][8 bytes]
+ *  DMU_PROBE_LDS_FRAG       32 x 128-byte tile,   unused             [64][4 K-steps][16 bytes]
+ *                           row-major (logical)
+ *  DMU_PROBE_CVT_BF16/_F16  float32[256]          unused             [256] 16-bit patterns
+ *
+ *  MFMA_*: lane l loads its operand fragments straight from in0/in1 with the
+ *    hypothesised mapping (X[row = l % m][k = (16 bytes / element) * (l / m) + s])
+ *    and issues one MFMA with a zero accumulator; the caller checks every
+ *    (lane, register) against the product.
+ *  LDS_READ_*: the image is copied to LDS; lane l reads at in1[l] (masked to
+ *    an aligned in-bounds address) with ds_read_b128 / ds_read_b64_tr_b16.
+ *  LDS_FRAG: the tile is stored with the GEMM kernels' swizzled LDS writes and
+ *    read back with their fragment reads for K-steps 0..3.
+ *  CVT_*: the GEMM epilogue's fp32 -> bf16 / fp16 conversion.
+ * dmu_probe_info() reports m, n, k, the input type and the number of 32-bit
+ * output words per lane.  `stream` as for dmu_gemm.
+ */
+enum {
+    DMU_PROBE_MFMA_32x32x16_BF16 = 1,
+    DMU_PROBE_MFMA_32x32x16_F16 = 2,
+    DMU_PROBE_MFMA_16x16x32_BF16 = 3,
+    DMU_PROBE_MFMA_16x16x32_F16 = 4,
+    DMU_PROBE_MFMA_32x32x32_I8 = 5,
+    DMU_PROBE_MFMA_16x16x64_I8 = 6,
+    DMU_PROBE_LDS_READ_B128 = 10,
+    DMU_PROBE_LDS_READ_TR16 = 11,
+    DMU_PROBE_LDS_FRAG = 12,
+    DMU_PROBE_CVT_BF16 = 30,
+    DMU_PROBE_CVT_F16 = 31
+};
+
+int dmu_probe(int variant, const void *in0, const void *in1, void *out, void *stream);
+
+/* Shape of a probe variant: instruction m, n, k, input dmu_dtype and the
+ * number of 32-bit output registers per lane.  Host-only. */
+int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type, int *regs_per_lane);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMU_H */

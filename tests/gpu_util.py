@@ -1,0 +1,181 @@
+"""Helpers of the GPU tests: move seeded workloads to the device, call the HIP
+library through its C ABI, and compare with the oracle to the stated bar.
+
+Tolerances (floating point, random inputs):
+  fp32 output:       |D - ref| <= 1e-3 * sqrt(K) * max|A| * max|B|
+  fp16/bf16 output:  |D - ref| <= 2e-2 * |ref| + 1e-3 * sqrt(K) * max|A| * max|B|
+The first is the bound ``1e-3 * sqrt(K)`` for inputs in [-1, 1] rescaled to the
+inputs' actual range (never looser than that bound); the second adds the
+relative 2e-2 allowance for a 16-bit output.  Integer-valued inputs whose sums
+are exact in fp32, and int8, must match bit for bit.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+import dense_matrix_unit_tiled_amd as dmu
+import oracle
+from tests import exact
+from workloads import to_bits as workloads_to_bits  # noqa: F401
+
+_TORCH_DT = None
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def to_dev(arr: np.ndarray):
+    """Raw element bits on cuda:0 (uint16 patterns travel as int16)."""
+    torch = _torch()
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def out_dtype(t: str):
+    torch = _torch()
+    return {"f32": torch.float32, "f16": torch.int16, "bf16": torch.int16, "i32": torch.int32}[t]
+
+
+def from_dev(t, out_t: str) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if out_t in ("f16", "bf16") else a
+
+
+def make_args(p, dA, dB, dD, dC=None):
+    return dmu.gemm_args(p.M, p.N, p.K, dA, p.lda, dB, p.ldb, dD, p.ldd, in_type=p.in_type,
+                         out_type=p.out_type, acc_type=p.acc_type, layout_a=p.layout_a,
+                         layout_b=p.layout_b, batch=p.batch, stride_a=p.stride_a,
+                         stride_b=p.stride_b, C=dC, ldc=p.ldc, stride_c=p.stride_c,
+                         stride_d=p.stride_d)
+
+
+class force_kernel:
+    """Context manager selecting a kernel family through DMU_FORCE_KERNEL."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __enter__(self):
+        self.old = os.environ.get("DMU_FORCE_KERNEL")
+        if self.name is None:
+            os.environ.pop("DMU_FORCE_KERNEL", None)
+        else:
+            os.environ["DMU_FORCE_KERNEL"] = self.name
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("DMU_FORCE_KERNEL", None)
+        else:
+            os.environ["DMU_FORCE_KERNEL"] = self.old
+
+
+def run_dmu(p, force=None, fill=None, return_name=False):
+    """Run one workload on the GPU through dmu_gemm; D as raw bits (oracle format).
+
+    fill: optional bit pattern written to D before the call (to see untouched cells).
+    """
+    torch = _torch()
+    dA, dB = to_dev(p.A), to_dev(p.B)
+    dC = to_dev(p.C) if p.C is not None else None
+    n = max(p.batch * p.stride_d, 1)
+    dD = torch.zeros(n, dtype=out_dtype(p.out_type), device="cuda:0")
+    if fill is not None:
+        dD.fill_(fill)
+    args = make_args(p, dA, dB, dD, dC)
+    with force_kernel(force):
+        name = dmu.dmu_gemm_kernel_name(args)
+        dmu.dmu_gemm(args)
+    torch.cuda.synchronize()
+    out = from_dev(dD, p.out_type)[: p.batch * p.stride_d]
+    return (out, name) if return_name else out
+
+
+def run_oracle(p, nthreads=None):
+    return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, in_type=p.in_type,
+                       out_type=p.out_type, layout_a=p.layout_a, layout_b=p.layout_b,
+                       batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, C=p.C,
+                       ldc=p.ldc, stride_c=p.stride_c, ldd=p.ldd, stride_d=p.stride_d,
+                       nthreads=nthreads)
+
+
+def oracle_at(p, bij):
+    return oracle.gemm_at(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, bij, in_type=p.in_type,
+                          out_type=p.out_type, layout_a=p.layout_a, layout_b=p.layout_b,
+                          batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, C=p.C,
+                          ldc=p.ldc, stride_c=p.stride_c)
+
+
+def values(bits: np.ndarray, t: str) -> np.ndarray:
+    if t == "f16":
+        return exact.f16_values(bits)
+    if t == "bf16":
+        return exact.bf16_values(bits)
+    return np.asarray(bits, dtype=np.float64)
+
+
+def input_absmax(p) -> tuple[float, float]:
+    if p.in_type == "i8":
+        return 128.0, 128.0
+    return float(np.nanmax(np.abs(values(p.A, p.in_type)))), float(np.nanmax(np.abs(values(p.B, p.in_type))))
+
+
+def valid_mask(p) -> np.ndarray:
+    """Elements of the flat D buffer that are part of the product (not ld padding)."""
+    m = np.zeros(max(p.batch * p.stride_d, 1), dtype=bool)
+    for b in range(p.batch):
+        base = b * p.stride_d
+        v = m[base: base + p.M * p.ldd].reshape(p.M, p.ldd)
+        v[:, : p.N] = True
+    return m[: p.batch * p.stride_d]
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, p, where=None):
+    """The parity bar for one workload (see the module docstring)."""
+    if where is not None:
+        got, want = got[where], want[where]
+    if p.out_type == "i32":
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"{bad.size} int32 mismatches, first at {bad[:5]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+        return
+    g, w = values(got, p.out_type), values(want, p.out_type)
+    amax, bmax = input_absmax(p)
+    floor = 1e-3 * math.sqrt(max(p.K, 1)) * amax * bmax
+    tol = floor if p.out_type == "f32" else 2e-2 * np.abs(w) + floor
+    err = np.abs(g - w)
+    bad = np.nonzero(~(err <= tol))[0]
+    assert bad.size == 0, (f"{bad.size}/{g.size} outside tolerance; worst err {np.nanmax(err):.3e} "
+                           f"(floor {floor:.3e}); first {bad[:5]}: got {g[bad[:5]]} want {w[bad[:5]]}")
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, where=None):
+    if where is not None:
+        got, want = got[where], want[where]
+    g = got.view(np.uint32) if got.dtype == np.float32 else got
+    w = want.view(np.uint32) if want.dtype == np.float32 else want
+    bad = np.nonzero(g != w)[0]
+    assert bad.size == 0, f"{bad.size} bit mismatches, first at {bad[:8]}: {got[bad[:8]]} vs {want[bad[:8]]}"
+
+
+def sample_bij(p, n=512, seed=0) -> np.ndarray:
+    """Sampled (b, i, j) covering the corners, tile edges and random interior points."""
+    rng = np.random.default_rng(seed)
+    pts = set()
+    for b in {0, p.batch - 1}:
+        for i in {0, p.M - 1, min(p.M - 1, 255), min(p.M - 1, 256), min(p.M - 1, 127)}:
+            for j in {0, p.N - 1, min(p.N - 1, 255), min(p.N - 1, 256), min(p.N - 1, 31)}:
+                pts.add((b, i, j))
+    while len(pts) < n:
+        pts.add((int(rng.integers(0, p.batch)), int(rng.integers(0, p.M)), int(rng.integers(0, p.N))))
+    return np.array(sorted(pts), dtype=np.int64)
+
+
+def flat_index(p, bij: np.ndarray) -> np.ndarray:
+    return bij[:, 0] * p.stride_d + bij[:, 1] * p.ldd + bij[:, 2]

@@ -1,0 +1,134 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/dmu.h
+declares, and rejects bad arguments before any HIP call (no GPU is touched:
+only validation, kernel selection and static strings are exercised)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_matrix_unit_tiled_amd as dmu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dmu.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmu_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = ctypes.CDLL(dmu.LIB_PATH)
+    names = declared_functions()
+    assert {"dmu_gemm", "dmu_gemm_check", "dmu_gemm_kernel_name", "dmu_status_string",
+            "dmu_last_error", "dmu_probe", "dmu_probe_info"} <= set(names)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_struct_layout_matches_header():
+    # 4 int64 + 5 int32 (+4 pad) + 4 x (pointer + 2 int64)
+    assert ctypes.sizeof(dmu.dmu_gemm_args) == 32 + 24 + 4 * 24
+    assert dmu.dmu_gemm_args.A.offset == 56
+
+
+FAKE = 1 << 40  # device-looking addresses; never dereferenced by validation
+
+
+def args(**kw):
+    base = dict(M=256, N=256, K=256, A=FAKE, lda=256, B=FAKE + (1 << 30), ldb=256,
+                D=FAKE + (2 << 30), ldd=256, in_type="f16", out_type="f32")
+    base.update(kw)
+    return dmu.gemm_args(**base)
+
+
+def test_valid_arguments_pass():
+    assert dmu.dmu_gemm_check(args()) == dmu.DMU_OK
+    assert dmu.dmu_last_error() == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), dmu.DMU_ERR_INVALID_ARG),
+    (dict(K=-5), dmu.DMU_ERR_INVALID_ARG),
+    (dict(lda=255), dmu.DMU_ERR_INVALID_ARG),
+    (dict(ldb=100), dmu.DMU_ERR_INVALID_ARG),
+    (dict(ldd=10), dmu.DMU_ERR_INVALID_ARG),
+    (dict(A=None), dmu.DMU_ERR_INVALID_ARG),
+    (dict(D=None), dmu.DMU_ERR_INVALID_ARG),
+    (dict(out_type="i32"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(in_type="i8", out_type="f32"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(in_type="f32", out_type="f32"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(in_type="bf16", out_type="f16"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(D=FAKE + 100), dmu.DMU_ERR_INVALID_ARG),                 # D overlaps A
+    (dict(batch=2, stride_d=100), dmu.DMU_ERR_INVALID_ARG),        # batches of D overlap
+    (dict(stride_a=-1, batch=2, stride_d=65536), dmu.DMU_ERR_INVALID_ARG),
+    (dict(C=FAKE + (2 << 30) + 4, ldc=256), dmu.DMU_ERR_INVALID_ARG),  # C partially overlaps D
+    (dict(M=1 << 31), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(D=FAKE + (2 << 30) + 1), dmu.DMU_ERR_INVALID_ARG),      # not element aligned
+    (dict(layout_a="row", lda=0, K=0), dmu.DMU_ERR_INVALID_ARG),
+])
+def test_rejections(kw, status):
+    a = args(**kw)
+    assert dmu.dmu_gemm_check(a) == status
+    assert dmu.dmu_last_error() != ""
+    with pytest.raises(dmu.DmuError) as e:
+        dmu.dmu_gemm(a, stream=0)  # rejected before any HIP call
+    assert e.value.status == status
+
+
+def test_in_place_c_equal_d_allowed():
+    d = FAKE + (2 << 30)
+    assert dmu.dmu_gemm_check(args(C=d, ldc=256)) == dmu.DMU_OK
+
+
+def test_bad_layout_code():
+    a = args()
+    a.layout_a = 7
+    assert dmu.dmu_gemm_check(a) == dmu.DMU_ERR_INVALID_ARG
+
+
+def test_empty_problems_launch_nothing():
+    for kw in (dict(M=0), dict(N=0), dict(batch=0)):
+        a = args(**kw)
+        assert dmu.dmu_gemm_check(a) == dmu.DMU_OK
+        assert dmu.dmu_gemm_kernel_name(a) is None
+        assert dmu.dmu_gemm(a, stream=0) == dmu.DMU_OK  # returns before any HIP call
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096, in_type="bf16", out_type="bf16"),
+     "mfma_256x256_k16_t16_bf16_bf16"),
+    (dict(in_type="f16", out_type="f32"), "mfma_128x128_k16_t16_f16_f32"),
+    (dict(M=5000, N=3000, K=2050, lda=2050, layout_b="col", ldb=2050, ldd=3000, in_type="f16",
+          out_type="f16", acc_type="f16"), "mfma_256x256_k4_k4_f16_f16"),
+    (dict(M=8192, N=8192, K=8192, lda=8192, layout_b="col", ldb=8192, ldd=8192, in_type="i8",
+          out_type="i32"), "mfma_256x256_k16_k16_i8_i32"),
+    (dict(M=4096, N=128, K=4096, lda=4096, ldb=128, ldd=128, batch=32, stride_a=4096 * 4096,
+          stride_b=4096 * 128, stride_d=4096 * 128), "mfma_256x128_k16_t16_f16_f32"),
+    (dict(A=FAKE + 2), "mfma_generic64_any_any_f16_f32"),       # 2-byte aligned A
+    (dict(K=255, lda=255, ldb=256), "mfma_generic64_any_any_f16_f32"),  # odd K row-major A
+    (dict(K=0, lda=1), "mfma_generic64_any_any_f16_f32"),
+])
+def test_kernel_selection(kw, expect):
+    assert dmu.dmu_gemm_kernel_name(args(**kw)) == expect
+
+
+def test_force_generic_env(monkeypatch):
+    monkeypatch.setenv("DMU_FORCE_KERNEL", "generic")
+    assert dmu.dmu_gemm_kernel_name(args()) == "mfma_generic64_any_any_f16_f32"
+
+
+def test_status_strings():
+    for s in (dmu.DMU_OK, dmu.DMU_ERR_INVALID_ARG, dmu.DMU_ERR_UNSUPPORTED, dmu.DMU_ERR_HIP):
+        assert dmu.dmu_status_string(s).startswith("DMU_")
+    assert "unknown" in dmu.dmu_status_string(42)
+
+
+def test_probe_info():
+    assert dmu.dmu_probe_info(dmu.DMU_PROBE_MFMA_32x32x16_BF16) == (32, 32, 16, dmu.DMU_BF16, 16)
+    assert dmu.dmu_probe_info(dmu.DMU_PROBE_MFMA_16x16x64_I8) == (16, 16, 64, dmu.DMU_I8, 4)
+    with pytest.raises(dmu.DmuError):
+        dmu.dmu_probe_info(999)
+    with pytest.raises(dmu.DmuError):
+        dmu.dmu_probe(dmu.DMU_PROBE_MFMA_32x32x16_BF16, None, None, None, stream=0)

@@ -1,0 +1,178 @@
+"""Single-wavefront layout probes on the GPU (the gfx950 counterpart of the
+layout experiment, KingOfEgg sections 6-7): every (lane, register) of each
+MFMA variant, the LDS fragment reads and the epilogue conversion.
+
+A failure prints each wrong (lane, register) with the (row, col) the value
+actually belongs to, so a wrong mapping is located at once.
+"""
+import numpy as np
+import pytest
+
+import dense_matrix_unit_tiled_amd as dmu
+import oracle
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+MFMA = [dmu.DMU_PROBE_MFMA_32x32x16_BF16, dmu.DMU_PROBE_MFMA_32x32x16_F16,
+        dmu.DMU_PROBE_MFMA_16x16x32_BF16, dmu.DMU_PROBE_MFMA_16x16x32_F16,
+        dmu.DMU_PROBE_MFMA_32x32x32_I8, dmu.DMU_PROBE_MFMA_16x16x64_I8]
+TNAME = {dmu.DMU_BF16: "bf16", dmu.DMU_F16: "f16", dmu.DMU_I8: "i8"}
+
+
+def acc_owner(m: int, lane: int, r: int):
+    """(row, col) of accumulator register r of lane `lane` (hypothesis under test)."""
+    if m == 32:
+        return 8 * (r // 4) + 4 * (lane // 32) + r % 4, lane % 32
+    return 4 * (lane // 16) + r, lane % 16
+
+
+def run_mfma_probe(variant, A, B):
+    import torch
+
+    m, n, k, t, regs = dmu.dmu_probe_info(variant)
+    tn = TNAME[t]
+    a_bits = np.ascontiguousarray(gu.workloads_to_bits(A, tn))
+    bt_bits = np.ascontiguousarray(gu.workloads_to_bits(B.T.copy(), tn))
+    out = torch.zeros(64 * regs, dtype=torch.int32, device="cuda:0")
+    dmu.dmu_probe(variant, gu.to_dev(a_bits), gu.to_dev(bt_bits), out)
+    torch.cuda.synchronize()
+    raw = out.cpu().numpy().reshape(64, regs)
+    return raw.view(np.float32) if tn != "i8" else raw
+
+
+def check_mfma(variant, A, B):
+    m, n, k, t, regs = dmu.dmu_probe_info(variant)
+    got = run_mfma_probe(variant, A, B)
+    D = A.astype(np.int64) @ B.astype(np.int64)
+    bad = []
+    for lane in range(64):
+        for r in range(regs):
+            i, j = acc_owner(m, lane, r)
+            if got[lane, r] != D[i, j]:
+                owners = list(zip(*np.nonzero(D == got[lane, r])))[:3]
+                bad.append((lane, r, (i, j), got[lane, r], D[i, j], owners))
+    assert not bad, "wrong (lane, reg): " + "; ".join(
+        f"lane {l} reg {r} expected D{ij}={w} got {g} (found at {o})" for l, r, ij, g, w, o in bad[:12])
+
+
+@pytest.mark.parametrize("variant", MFMA)
+def test_mfma_layout_experiment_pattern(variant):
+    """A[i][k] = i, B[k][j] = j  =>  D[i][j] = k * i * j, checked per lane and register."""
+    m, n, k, t, regs = dmu.dmu_probe_info(variant)
+    A = np.repeat(np.arange(m)[:, None], k, axis=1)
+    B = np.repeat(np.arange(n)[None, :], k, axis=0)
+    check_mfma(variant, A, B)
+
+
+@pytest.mark.parametrize("variant", MFMA)
+def test_mfma_k_pairing(variant):
+    """A[i][k] = k, B[k][j] = k: any mismatch between how A and B pair their k
+    slots lowers sum(k^2) (rearrangement inequality), which the i*j pattern cannot see."""
+    m, n, k, t, regs = dmu.dmu_probe_info(variant)
+    kk = np.arange(k) % (64 if t == dmu.DMU_I8 else 256)
+    A = np.repeat(kk[None, :], m, axis=0)
+    B = np.repeat(kk[:, None], n, axis=1)
+    if t == dmu.DMU_I8:
+        A, B = A - 32, B - 32
+    check_mfma(variant, A, B)
+
+
+@pytest.mark.parametrize("variant", MFMA)
+def test_mfma_random_integers(variant):
+    m, n, k, t, regs = dmu.dmu_probe_info(variant)
+    rng = np.random.default_rng(variant)
+    lo, hi = (-128, 128) if t == dmu.DMU_I8 else (-8, 9)
+    check_mfma(variant, rng.integers(lo, hi, (m, k)), rng.integers(lo, hi, (k, n)))
+
+
+@pytest.mark.parametrize("variant", [dmu.DMU_PROBE_MFMA_32x32x16_F16, dmu.DMU_PROBE_MFMA_32x32x16_BF16])
+def test_mfma_keeps_subnormal_inputs(variant):
+    """Subnormal fp16/bf16 inputs times 1 reach the fp32 accumulator unflushed."""
+    import torch
+
+    m, n, k, t, regs = dmu.dmu_probe_info(variant)
+    tn = TNAME[t]
+    a_bits = np.zeros((m, k), dtype=np.uint16)
+    a_bits[:, 0] = np.arange(1, m + 1)  # the m smallest positive subnormals
+    one = 0x3C00 if tn == "f16" else 0x3F80
+    bt_bits = np.zeros((n, k), dtype=np.uint16)
+    bt_bits[:, 0] = one
+    out = torch.zeros(64 * regs, dtype=torch.int32, device="cuda:0")
+    dmu.dmu_probe(variant, gu.to_dev(a_bits), gu.to_dev(bt_bits), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(64, regs).view(np.float32)
+    vals = oracle.decode(tn, a_bits[:, 0])
+    for lane in range(64):
+        for r in range(regs):
+            i, j = acc_owner(m, lane, r)
+            assert got[lane, r] == np.float32(vals[i]), (lane, r, got[lane, r], vals[i])
+
+
+def test_lds_read_b128():
+    import torch
+
+    img = np.arange(2048, dtype=np.uint16)
+    addr = ((np.arange(64) * 37) % 256 * 16).astype(np.int32)
+    out = torch.zeros(64 * 4, dtype=torch.int32, device="cuda:0")
+    dmu.dmu_probe(dmu.DMU_PROBE_LDS_READ_B128, gu.to_dev(img), gu.to_dev(addr), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 8)
+    want = np.stack([img[a // 2: a // 2 + 8] for a in addr])
+    assert np.array_equal(got, want)
+
+
+def test_lds_read_tr16_observed_mapping():
+    """ds_read_b64_tr_b16 with lane l addressing its own 4 elements: records which
+    (source lane, element) each output slot takes.  The hypothesis checked is the
+    transpose of 4 x 4 blocks inside each aligned group of four lanes; on a mismatch
+    the observed table is printed in full."""
+    import torch
+
+    img = np.arange(2048, dtype=np.uint16)
+    addr = (np.arange(64) * 8).astype(np.int32)
+    out = torch.zeros(64 * 2, dtype=torch.int32, device="cuda:0")
+    dmu.dmu_probe(dmu.DMU_PROBE_LDS_READ_TR16, gu.to_dev(img), gu.to_dev(addr), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 4)
+    src = [[(int(v) // 4, int(v) % 4) for v in row] for row in got]
+    want = [[(4 * (l // 4) + e, l % 4) for e in range(4)] for l in range(64)]
+    table = "\n".join(f"lane {l:2d}: {src[l]}" for l in range(64))
+    assert src == want, "observed (src lane, src elem) per output slot:\n" + table
+
+
+def test_lds_fragment_format():
+    """The kernels' swizzled LDS tile writes + fragment reads return, for lane l and
+    K-step ks, bytes 32*ks + 16*(l/32) .. +15 of logical row l % 32."""
+    import torch
+
+    words = np.arange(32 * 64, dtype=np.uint16)  # 32 rows x 64 16-bit words = 128 bytes/row
+    out = torch.zeros(64 * 16, dtype=torch.int32, device="cuda:0")
+    dmu.dmu_probe(dmu.DMU_PROBE_LDS_FRAG, gu.to_dev(words), None, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 4, 8)
+    for lane in range(64):
+        for ks in range(4):
+            w0 = (lane % 32) * 64 + (32 * ks + 16 * (lane // 32)) // 2
+            assert np.array_equal(got[lane, ks], words[w0: w0 + 8]), (lane, ks)
+
+
+@pytest.mark.parametrize("t,variant", [("bf16", dmu.DMU_PROBE_CVT_BF16), ("f16", dmu.DMU_PROBE_CVT_F16)])
+def test_epilogue_conversion_rounds_to_nearest_even(t, variant):
+    import torch
+
+    rng = np.random.default_rng(5)
+    special = [1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -11, 1 + 3 * 2 ** -11, -(1 + 2 ** -8),
+               2.0 ** -24, 1.5 * 2 ** -24, 2.5 * 2 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+               2.0 ** -130, 1.5 * 2 ** -133, 65504.0, 65519.0, 65520.0, 1e30, -1e30,
+               np.inf, -np.inf, 0.0, -0.0, 3.0e38]
+    x = np.concatenate([np.array(special), rng.standard_normal(256 - len(special) - 32) *
+                        2.0 ** rng.integers(-30, 20, 256 - len(special) - 32),
+                        rng.uniform(-1, 1, 32) * 2.0 ** -20]).astype(np.float32)
+    out = torch.zeros(256, dtype=torch.int16, device="cuda:0")
+    dmu.dmu_probe(variant, gu.to_dev(x), None, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    want = oracle.encode(t, x.astype(np.float64))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]

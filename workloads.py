@@ -118,6 +118,69 @@ def _storage(logical: np.ndarray, layout: str, ld: int) -> np.ndarray:
     return out.reshape(-1)
 
 
+def store(logical: np.ndarray, t: str, layout: str, pad: int = 0) -> tuple[np.ndarray, int]:
+    """Raw bits of a logical [batch, R, C] value array in the given layout; returns (bits, ld)."""
+    b, r, c = logical.shape
+    ld = (c if layout == "row" else r) + pad
+    bits = to_bits(np.ascontiguousarray(logical).reshape(-1), t).reshape(b, r, c)
+    return _storage(bits, layout, ld), ld
+
+
+def _slices(cfg, kind, seed, M, N, K, batch):
+    """Per-batch generators of the logical fp64 (or integer) A [M, K] and B [K, N]."""
+    i = np.arange(M)[:, None]
+    j = np.arange(N)[None, :]
+    kk_row = np.arange(K)[None, :]
+    kk_col = np.arange(K)[:, None]
+    if kind == "random":
+        ra, rb = _rng(cfg, 0, seed), _rng(cfg, 1, seed)
+        if cfg in ("c1", "c4s"):
+            return (lambda q: ra.uniform(-1, 1, (M, K))), (lambda q: rb.uniform(-1, 1, (K, N)))
+        if cfg == "c2":
+            s = 1.0 / np.sqrt(K) if K else 1.0
+            return (lambda q: ra.standard_normal((M, K)) * s), (lambda q: rb.standard_normal((K, N)) * s)
+        if cfg == "c3":
+            return (lambda q: ra.uniform(-0.5, 0.5, (M, K))), (lambda q: rb.uniform(-0.5, 0.5, (K, N)))
+        if cfg == "c4o":
+            def softmax_rows(q):  # softmax of N(0,1) logits, rows sum to 1
+                z = ra.standard_normal((M, K))
+                z -= z.max(axis=1, keepdims=True)
+                np.exp(z, out=z)
+                z /= z.sum(axis=1, keepdims=True)
+                return z
+            return softmax_rows, (lambda q: rb.uniform(-1, 1, (K, N)))
+        if cfg == "c5":
+            return (lambda q: ra.integers(-128, 128, (M, K))), (lambda q: rb.integers(-128, 128, (K, N)))
+    elif kind == "structured":
+        if cfg in ("c1", "c2", "c5"):
+            return (lambda q: np.broadcast_to(i % 16, (M, K))), (lambda q: np.broadcast_to(j % 8, (K, N)))
+        if cfg == "c3":
+            return (lambda q: (kk_row % 16 == i % 16).astype(np.float64)), \
+                   (lambda q: np.broadcast_to(j % 8, (K, N)))
+        if cfg == "c4s":
+            return (lambda q: np.broadcast_to((i + q) % 16, (M, K))), \
+                   (lambda q: np.broadcast_to(j % 8, (K, N)))
+        if cfg == "c4o":
+            return (lambda q: (kk_row == (i + q) % K).astype(np.float64)), \
+                   (lambda q: ((kk_col + 3 * q + j) % 64) - 32.0)
+    raise ValueError((cfg, kind))
+
+
+def _store_slices(gen, t, layout, batch, rows, cols, ld):
+    """Raw bits of all batch slices, stored row- or column-major with leading dim ld."""
+    per = (rows if layout == "row" else cols) * ld
+    out = np.zeros(batch * per, dtype=_NP_BITS[t])
+    for q in range(batch):
+        x = np.asarray(gen(q))
+        bits = to_bits(np.ascontiguousarray(x).reshape(-1), t).reshape(rows, cols)
+        dst = out[q * per: (q + 1) * per]
+        if layout == "row":
+            dst.reshape(rows, ld)[:, :cols] = bits
+        else:
+            dst.reshape(cols, ld)[:, :rows] = bits.T
+    return out
+
+
 def make(cfg: str, kind: str = "random", seed: int = 0, *, M=None, N=None, K=None, batch=None,
          pad: int = 0, with_c: bool = False) -> Problem:
     """Build a workload.  Sizes default to the full problem; override to shrink it.
@@ -132,61 +195,11 @@ def make(cfg: str, kind: str = "random", seed: int = 0, *, M=None, N=None, K=Non
     K = fK if K is None else K
     batch = fb if batch is None else batch
     lda, ldb, sa, sb = _layout_params(M, N, K, la, lb, pad)
-    i = np.arange(M)[:, None]
-    j = np.arange(N)[None, :]
-    meta = {"kind": kind, "seed": seed, "cfg": cfg}
-
-    if kind == "random":
-        ra, rb = _rng(cfg, 0, seed), _rng(cfg, 1, seed)
-        if cfg == "c1" or cfg == "c4s":
-            a = ra.uniform(-1, 1, (batch, M, K))
-            b = rb.uniform(-1, 1, (batch, K, N))
-        elif cfg == "c2":
-            s = 1.0 / np.sqrt(K) if K else 1.0
-            a = ra.standard_normal((batch, M, K)) * s
-            b = rb.standard_normal((batch, K, N)) * s
-        elif cfg == "c3":
-            a = ra.uniform(-0.5, 0.5, (batch, M, K))
-            b = rb.uniform(-0.5, 0.5, (batch, K, N))
-        elif cfg == "c4o":
-            a = np.empty((batch, M, K))
-            for q in range(batch):  # softmax rows of N(0,1) logits, one batch at a time
-                z = ra.standard_normal((M, K))
-                z -= z.max(axis=1, keepdims=True)
-                np.exp(z, out=z)
-                z /= z.sum(axis=1, keepdims=True)
-                a[q] = z
-            b = rb.uniform(-1, 1, (batch, K, N))
-        elif cfg == "c5":
-            a = ra.integers(-128, 128, (batch, M, K))
-            b = rb.integers(-128, 128, (batch, K, N))
-        else:
-            raise ValueError(cfg)
-    elif kind == "structured":
-        bidx = np.arange(batch)[:, None, None]
-        kk = np.arange(K)
-        if cfg in ("c1", "c2", "c5"):
-            a = np.broadcast_to((i % 16) + 0 * kk[None, :], (batch, M, K)).astype(np.float64)
-            b = np.broadcast_to((j % 8) + 0 * kk[:, None], (batch, K, N)).astype(np.float64)
-        elif cfg == "c3":
-            a = np.broadcast_to((kk[None, :] % 16 == i % 16).astype(np.float64), (batch, M, K))
-            b = np.broadcast_to((j % 8) + 0.0 * kk[:, None], (batch, K, N))
-        elif cfg == "c4s":
-            a = ((np.arange(M)[None, :, None] + bidx) % 16) + 0.0 * kk[None, None, :]
-            b = np.broadcast_to((j % 8) + 0.0 * kk[:, None], (batch, K, N))
-        elif cfg == "c4o":
-            a = (kk[None, None, :] == (np.arange(M)[None, :, None] + bidx) % K).astype(np.float64)
-            b = ((kk[None, :, None] + 3 * bidx + np.arange(N)[None, None, :]) % 64) - 32.0
-        else:
-            raise ValueError(cfg)
-    else:
-        raise ValueError(kind)
-
-    a = to_bits(np.ascontiguousarray(a).reshape(-1), in_t).reshape(batch, M, K)
-    b = to_bits(np.ascontiguousarray(b).reshape(-1), in_t).reshape(batch, K, N)
-    A = _storage(a, la, lda)
-    B = _storage(b, lb, ldb)
+    ga, gb = _slices(cfg, kind, seed, M, N, K, batch)
+    A = _store_slices(ga, in_t, la, batch, M, K, lda)
+    B = _store_slices(gb, in_t, lb, batch, K, N, ldb)
     ldd = N + pad
+    meta = {"kind": kind, "seed": seed, "cfg": cfg}
     p = Problem(cfg, M, N, K, batch, in_t, acc_t, out_t, la, lb, A, lda, sa if batch > 1 else 0,
                 B, ldb, sb if batch > 1 else 0, ldd=ldd, stride_d=M * ldd, meta=meta)
     if cfg == "c1" and not with_c:
