@@ -1,0 +1,180 @@
+"""Benchmark of the gfx950 GEMM: 4096^3 bf16, A and B row-major, fp32 accumulate,
+bf16 output (the 4096^3 example of "Tensor Cores, CUTLASS and CuTe", sections
+opening and 4.1, here in its NN form).
+
+One step = one D = A*B launch through the C ABI over inputs already resident
+in HBM.  W untimed warm-up steps, then exactly K steps timed with HIP events
+on the launch stream, bracketed by device synchronisation.  Prints one JSON
+line with the throughput, the MFMA roofline of the kernel and the CPU oracle's
+rate on a bounded row slice of the same product.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5]
+                  [--no-cpu-baseline] [--copy-calibration MiB]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (matrix cores), TFLOP/s or TOP/s, and HBM3E bandwidth.
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "i8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD_NAMES = {
+    "c1": "gemm_256x256x256_f16_nn_f32acc_f32out",
+    "c2": "gemm_4096x4096x4096_bf16_nn_f32acc_bf16out",
+    "c3": "gemm_5000x3000x2050_f16_tn_f16out",
+    "c4s": "batched32_gemm_4096x4096x128_f16_tn_f32out",
+    "c4o": "batched32_gemm_4096x128x4096_f16_nn_f32out",
+    "c5": "gemm_8192x8192x8192_i8_tn_i32out",
+}
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources (a stored counter reading is valid only for these)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dense_matrix_unit_tiled_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD_NAMES[workload]}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(p, budget_s: float = 12.0):
+    """The oracle, as it stands, on the host cores over a bounded row slice of the product."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+
+    def run(rows):
+        A = p.A[: rows * p.lda] if p.layout_a == "row" else p.A
+        t0 = time.perf_counter()
+        oracle.gemm(rows, p.N, p.K, A, p.lda, p.B, p.ldb, in_type=p.in_type, out_type=p.out_type,
+                    layout_a=p.layout_a, layout_b=p.layout_b, ldd=p.N, nthreads=threads)
+        return time.perf_counter() - t0
+
+    rows = threads
+    t = run(rows)
+    rows2 = int(min(p.M, max(rows, rows * budget_s / max(t, 1e-3))))
+    rows2 = max(threads, (rows2 // threads) * threads)
+    t2 = run(rows2)
+    flops = 2.0 * rows2 * p.N * p.K
+    return {"value": round(flops / t2 / 1e12, 6), "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows2 - 1} of the {p.M}x{p.N}x{p.K} product "
+                      f"({rows2}x{p.N}x{p.K} MACs, {t2:.1f} s, fp64 sums, {threads} threads)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_matrix_unit_tiled_amd as dmu
+    import workloads
+
+    def to_dev(x):  # raw element bits on the GPU (uint16 patterns travel as int16)
+        x = np.ascontiguousarray(x)
+        return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to("cuda:0")
+
+    p = workloads.make(args.workload, "random", 0)
+    dA, dB = to_dev(p.A), to_dev(p.B)
+    dC = to_dev(p.C) if p.C is not None else None
+    out_dt = {"f32": torch.float32, "f16": torch.int16, "bf16": torch.int16, "i32": torch.int32}
+    dD = torch.zeros(p.batch * p.stride_d, dtype=out_dt[p.out_type], device="cuda:0")
+    a = dmu.gemm_args(p.M, p.N, p.K, dA, p.lda, dB, p.ldb, dD, p.ldd, in_type=p.in_type,
+                      out_type=p.out_type, acc_type=p.acc_type, layout_a=p.layout_a,
+                      layout_b=p.layout_b, batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b,
+                      C=dC, ldc=p.ldc, stride_c=p.stride_c, stride_d=p.stride_d)
+    kernel = dmu.dmu_gemm_kernel_name(a)
+    stream = torch.cuda.current_stream()
+    print(f"# workload {WORKLOAD_NAMES[args.workload]} kernel {kernel}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        dmu.dmu_gemm(a, stream)
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        dmu.dmu_gemm(a, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    print(f"# timed {args.steps} launches: {ms * 1e3:.2f} us each", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flops = float(p.flops)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[p.in_type]
+    traffic = stored_traffic(args.workload, kernel)
+    result = {
+        "metric": "achieved TFLOPS (% of MFMA peak) for 4096³ bf16 GEMM, fp32 accumulate"
+        if args.workload == "c2" else f"achieved {'TOPS' if p.in_type == 'i8' else 'TFLOPS'}",
+        "value": round(tflops, 3),
+        "unit": "TOPS" if p.in_type == "i8" else "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.in_type,
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "M": p.M, "N": p.N, "K": p.K,
+                   "batch": p.batch, "layout_a": p.layout_a, "layout_b": p.layout_b,
+                   "in_type": p.in_type, "acc_type": p.acc_type, "out_type": p.out_type,
+                   "kernel": kernel, "pct_of_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

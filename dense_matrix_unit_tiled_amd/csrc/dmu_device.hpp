@@ -148,6 +148,7 @@ struct GemmParams {
     uint32_t total_tiles;                       // tiles_m * tiles_n * batch
     int32_t a_kc, b_kc;                         // 1: operand is K-contiguous in memory
     int32_t d_vec4;                             // 1: 4-element vector access to C/D is legal
+    int64_t a_bytes, b_bytes;                   // bytes spanned by one batch slice of A / B
 };
 
 // ---------------------------------------------------------------------------

@@ -221,6 +221,10 @@ int validate(const dmu_gemm_args *a, Plan *plan)
     const bool a_kc = a->layout_a == DMU_ROW_MAJOR, b_kc = a->layout_b == DMU_COL_MAJOR;
     int amode = K > 0 ? operand_mode(a_kc, a->A, a->lda, batch > 1 ? a->stride_a : 0, esz, K, M) : -1;
     int bmode = K > 0 ? operand_mode(b_kc, a->B, a->ldb, batch > 1 ? a->stride_b : 0, esz, K, N) : -1;
+    if (amode >= 0 && extent(a->layout_a, M, K, a->lda) * esz >= ((int64_t)1 << 31))
+        amode = -1; // slice too large for one buffer descriptor
+    if (bmode >= 0 && extent(a->layout_b, K, N, a->ldb) * esz >= ((int64_t)1 << 31))
+        bmode = -1;
     int tile = TILE_GENERIC;
     const char *env = getenv("DMU_FORCE_KERNEL");
     const bool force_generic = env && strcmp(env, "generic") == 0;
@@ -271,6 +275,8 @@ int validate(const dmu_gemm_args *a, Plan *plan)
     p.b_kc = b_kc;
     const bool c_vec = !a->C || (((uintptr_t)a->C % (4 * osz)) == 0 && a->ldc % 4 == 0 && p.stride_c % 4 == 0);
     p.d_vec4 = ((uintptr_t)a->D % (4 * osz)) == 0 && a->ldd % 4 == 0 && p.stride_d % 4 == 0 && c_vec;
+    p.a_bytes = extent(a->layout_a, M, K, a->lda) * esz;
+    p.b_bytes = extent(a->layout_b, K, N, a->ldb) * esz;
     return DMU_OK;
 }
 

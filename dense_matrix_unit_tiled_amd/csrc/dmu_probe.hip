@@ -31,8 +31,10 @@ __global__ void __launch_bounds__(64) probe_mfma(const char *a, const char *bt, 
         else
             c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
                                                        0, 0, 0);
-        for (int r = 0; r < 16; ++r)
-            out[l * 16 + r] = __builtin_bit_cast(uint32_t, c[r]);
+        for (int r = 0; r < 16; ++r) {
+            const float v = c[r]; // copy the element out first: a bit_cast of a vector element lvalue mis-lowers
+            out[l * 16 + r] = __builtin_bit_cast(uint32_t, v);
+        }
     } else if (V == DMU_PROBE_MFMA_16x16x32_BF16 || V == DMU_PROBE_MFMA_16x16x32_F16) {
         const u32x4 x = probe_frag(a, 16, 64, l), y = probe_frag(bt, 16, 64, l);
         f32x4 c = {};
@@ -42,8 +44,10 @@ __global__ void __launch_bounds__(64) probe_mfma(const char *a, const char *bt, 
         else
             c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
                                                        0, 0, 0);
-        for (int r = 0; r < 4; ++r)
-            out[l * 4 + r] = __builtin_bit_cast(uint32_t, c[r]);
+        for (int r = 0; r < 4; ++r) {
+            const float v = c[r];
+            out[l * 4 + r] = __builtin_bit_cast(uint32_t, v);
+        }
     } else if (V == DMU_PROBE_MFMA_32x32x32_I8) {
         const u32x4 x = probe_frag(a, 32, 32, l), y = probe_frag(bt, 32, 32, l);
         i32x16 c = {};

@@ -122,23 +122,37 @@ def test_lds_read_b128():
     assert np.array_equal(got, want)
 
 
-def test_lds_read_tr16_observed_mapping():
-    """ds_read_b64_tr_b16 with lane l addressing its own 4 elements: records which
-    (source lane, element) each output slot takes.  The hypothesis checked is the
-    transpose of 4 x 4 blocks inside each aligned group of four lanes; on a mismatch
-    the observed table is printed in full."""
+def test_lds_read_tr16_mapping():
+    """ds_read_b64_tr_b16: within each group of 16 lanes, the 16 addressed 4-element
+    rows R[j] (j = source lane in the group) are read transposed: output lane i gets
+    element i % 4 of rows i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.  So if lane j
+    addresses X[k0 + j / 4][n0 + 4 * (j % 4)], output lane i holds X[k0 .. k0+3][n0 + i]:
+    four consecutive k of one column, the operand layout of a K x N row-major tile."""
     import torch
 
     img = np.arange(2048, dtype=np.uint16)
-    addr = (np.arange(64) * 8).astype(np.int32)
     out = torch.zeros(64 * 2, dtype=torch.int32, device="cuda:0")
+    # (a) lane j addresses its own 4 elements: the raw permutation
+    addr = (np.arange(64) * 8).astype(np.int32)
     dmu.dmu_probe(dmu.DMU_PROBE_LDS_READ_TR16, gu.to_dev(img), gu.to_dev(addr), out)
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint16).reshape(64, 4)
     src = [[(int(v) // 4, int(v) % 4) for v in row] for row in got]
-    want = [[(4 * (l // 4) + e, l % 4) for e in range(4)] for l in range(64)]
+    want = [[(16 * (l // 16) + l % 16 // 4 + 4 * e, l % 4) for e in range(4)] for l in range(64)]
     table = "\n".join(f"lane {l:2d}: {src[l]}" for l in range(64))
     assert src == want, "observed (src lane, src elem) per output slot:\n" + table
+    # (b) the operand use: a k x n row-major tile of 16-bit words (32 x 64 = the 4 KiB image)
+    X = np.arange(32 * 64, dtype=np.uint16).reshape(32, 64)
+    g = np.arange(64) // 16
+    j = np.arange(64) % 16
+    k0, n0 = 4 * g, 0
+    addr = (((k0 + j // 4) * 64 + n0 + 4 * (j % 4)) * 2).astype(np.int32)
+    dmu.dmu_probe(dmu.DMU_PROBE_LDS_READ_TR16, gu.to_dev(X.reshape(-1)), gu.to_dev(addr), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 4)
+    for lane in range(64):
+        kk = 4 * (lane // 16)
+        assert np.array_equal(got[lane], X[kk:kk + 4, lane % 16]), lane
 
 
 def test_lds_fragment_format():
