@@ -10,6 +10,7 @@ rate on a bounded row slice of the same product.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5]
                   [--no-cpu-baseline] [--copy-calibration MiB]
+  python bench.py --summarize DIR [--workload W]   (rocprofv3 output -> profiles/)
 """
 from __future__ import annotations
 
@@ -57,6 +58,37 @@ def stored_traffic(workload: str, kernel: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def profile_commands(workload: str, d: str) -> dict:
+    """The rocprofv3 runs whose output --summarize reads (run from the repository root)."""
+    bench = f"python3 bench.py --workload {workload}"
+    small = f"{bench} --steps 5 --warmup 2 --no-cpu-baseline --copy-calibration 256"
+    sq = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+          "SQ_INSTS_LDS SQ_INSTS_MFMA GRBM_GUI_ACTIVE")
+    return {
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
+                 f"{bench} --steps 50 --warmup 10 --no-cpu-baseline",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- {small}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- {small}",
+        "sq": f"rocprofv3 --pmc {sq} --output-format csv -d {d}/sq -o run -- {small}",
+    }
+
+
+def kernel_for(workload: str) -> str:
+    """Name of the kernel variant the workload's call selects (host-side query, no GPU)."""
+    import dense_matrix_unit_tiled_amd as dmu
+    import workloads
+
+    M, N, K, batch, in_t, out_t, acc_t, la, lb = workloads.FULL[workload]
+    lda, ldb, sa, sb = workloads._layout_params(M, N, K, la, lb)
+    base = 1 << 40  # aligned stand-in addresses: only validation and selection run
+    a = dmu.gemm_args(M, N, K, base, lda, base + (1 << 36), ldb, base + (2 << 36), N, in_type=in_t,
+                      out_type=out_t, acc_type=acc_t, layout_a=la, layout_b=lb, batch=batch,
+                      stride_a=sa if batch > 1 else 0, stride_b=sb if batch > 1 else 0,
+                      stride_d=M * N if batch > 1 else 0,
+                      C=(base + (3 << 36)) if workload == "c1" else None, ldc=N if workload == "c1" else 0)
+    return dmu.dmu_gemm_kernel_name(a)
+
+
 def cpu_baseline(p, budget_s: float = 12.0):
     """The oracle, as it stands, on the host cores over a bounded row slice of the product."""
     import numpy as np
@@ -92,7 +124,18 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="summarize rocprofv3 output under DIR into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize:
+        from dense_matrix_unit_tiled_amd import profiling
+
+        kernel = kernel_for(args.workload)
+        res = profiling.summarize(args.summarize, os.path.join(ROOT, "profiles"), WORKLOAD_NAMES[args.workload],
+                                  kernel, source_digest(),
+                                  profile_commands(args.workload, "gpurun_out/prof_" + args.workload))
+        print(json.dumps(res))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
               file=sys.stderr)

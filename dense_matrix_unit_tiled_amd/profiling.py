@@ -1,0 +1,142 @@
+"""Summaries of rocprofv3 output for the benchmark (host-side tooling, no GPU work).
+
+``bench.py --summarize DIR`` reads the CSV files that these rocprofv3 runs of
+``bench.py`` wrote under DIR and writes short text summaries into ``profiles/``:
+
+  kernel trace   rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run
+                     -- python3 bench.py --workload W --steps 50 --warmup 10 --no-cpu-baseline
+  HBM traffic    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run
+                     -- python3 bench.py --workload W --steps 5 --warmup 2 --no-cpu-baseline
+                        --copy-calibration 256
+                 (the same with WRITE_SIZE into DIR/write)
+  matrix cores   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_LDS_BANK_CONFLICT
+                     SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_MFMA GRBM_GUI_ACTIVE
+                     --output-format csv -d DIR/sq -o run -- python3 bench.py ... (as above)
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+counter reads for a plain device-to-device copy of 256 MiB (the
+``--copy-calibration`` leg): factor = copied bytes / counter bytes.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import json
+import os
+from collections import defaultdict
+
+COPY_MIB = 256
+
+
+def _rows(pattern: str):
+    out = []
+    for f in glob.glob(pattern, recursive=True):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def _counter_means(rows):
+    """{(kernel name, counter): mean value per dispatch}"""
+    acc = defaultdict(list)
+    for r in rows:
+        acc[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _pick(means, counter, pred):
+    vals = [v for (k, c), v in means.items() if c == counter and pred(k)]
+    return vals[0] if vals else None
+
+
+def is_gemm(name: str) -> bool:
+    return "dmu::gemm_" in name
+
+
+def is_copy(name: str) -> bool:
+    return "copyBuffer" in name
+
+
+def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, source_digest: str,
+              commands: dict) -> dict:
+    """Write profiles/<label>_<workload>_*.md and traffic_<workload>.json; return the figures."""
+    os.makedirs(profiles, exist_ok=True)
+    result = {"workload": workload_name, "kernel": kernel_label, "source_digest": source_digest}
+
+    # kernel trace statistics
+    stats = _rows(os.path.join(d, "trace", "**", "*kernel_stats.csv"))
+    if stats:
+        lines = [f"# Kernel trace: {workload_name}", "",
+                 "Command (from the repository root on the GPU host):", "",
+                 "```", commands["trace"], "```", "",
+                 "| kernel | calls | average (us) | min (us) | max (us) | share |",
+                 "|---|---|---|---|---|---|"]
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+            name = r["Name"]
+            if len(name) > 90:
+                name = name[:87] + "..."
+            lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+            if is_gemm(r["Name"]):
+                result["avg_us"] = float(r["AverageNs"]) / 1e3
+        open(os.path.join(profiles, f"{kernel_label}_{workload_name}_kernel_trace.md"), "w").write(
+            "\n".join(lines) + "\n")
+
+    # HBM traffic, calibrated with the plain copy
+    fetch = _counter_means(_rows(os.path.join(d, "fetch", "**", "*counter_collection.csv")))
+    write = _counter_means(_rows(os.path.join(d, "write", "**", "*counter_collection.csv")))
+    if fetch and write:
+        copy_bytes = COPY_MIB * (1 << 20)
+        f_copy = _pick(fetch, "FETCH_SIZE", is_copy)
+        w_copy = _pick(write, "WRITE_SIZE", is_copy)
+        f_gemm = _pick(fetch, "FETCH_SIZE", is_gemm)
+        w_gemm = _pick(write, "WRITE_SIZE", is_gemm)
+        f_factor = copy_bytes / (f_copy * 1024)
+        w_factor = copy_bytes / (w_copy * 1024)
+        fetch_b = f_gemm * 1024 * f_factor
+        write_b = w_gemm * 1024 * w_factor
+        result.update({"fetch_kib_per_dispatch": f_gemm, "write_kib_per_dispatch": w_gemm,
+                       "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+                       "fetch_factor": f_factor, "write_factor": w_factor,
+                       "traffic_bytes_per_launch": fetch_b + write_b,
+                       "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b})
+        json.dump(result, open(os.path.join(profiles, f"traffic_{workload_name}.json"), "w"), indent=1)
+        md = [f"# HBM traffic: {workload_name}", "",
+              "Commands (from the repository root on the GPU host):", "", "```",
+              commands["fetch"], commands["write"], "```", "",
+              f"Calibration: a plain device copy of {COPY_MIB} MiB reads FETCH_SIZE = {f_copy:.0f} KiB "
+              f"and WRITE_SIZE = {w_copy:.0f} KiB, so the factors are {f_factor:.3f} (fetch) and "
+              f"{w_factor:.3f} (write).", "",
+              "| per GEMM launch | counter (KiB) | calibrated bytes |", "|---|---|---|",
+              f"| FETCH_SIZE | {f_gemm:.0f} | {fetch_b / 1e6:.1f} MB |",
+              f"| WRITE_SIZE | {w_gemm:.0f} | {write_b / 1e6:.1f} MB |",
+              f"| total | | {(fetch_b + write_b) / 1e6:.1f} MB |", "",
+              f"Kernel source digest: `{source_digest}`."]
+        open(os.path.join(profiles, f"traffic_{workload_name}.md"), "w").write("\n".join(md) + "\n")
+
+    # matrix-core and LDS counters
+    sq = _counter_means(_rows(os.path.join(d, "sq", "**", "*counter_collection.csv")))
+    if sq:
+        get = lambda c: _pick(sq, c, is_gemm)
+        busy = get("SQ_VALU_MFMA_BUSY_CYCLES")
+        grbm = get("GRBM_GUI_ACTIVE")
+        conflict, active = get("SQ_LDS_BANK_CONFLICT"), get("SQ_LDS_IDX_ACTIVE")
+        md = [f"# Matrix-core and LDS counters: {workload_name}", "",
+              "Command (from the repository root on the GPU host):", "", "```", commands["sq"], "```", "",
+              "| counter (per GEMM dispatch, summed over the chip) | value |", "|---|---|"]
+        for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                  "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"):
+            v = get(c)
+            if v is not None:
+                md.append(f"| {c} | {v:.4g} |")
+        if busy and grbm:
+            # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs
+            util = busy / (grbm / 8 * 1024)
+            md += ["", f"MFMA busy fraction = MFMA_BUSY / (GUI_ACTIVE / 8 XCDs x 1024 SIMDs) = {util:.3f}."]
+            result["mfma_busy_fraction"] = util
+        if conflict is not None and active:
+            md += [f"LDS bank-conflict cycles / LDS active cycles = {conflict / active:.3f}."]
+            result["lds_conflict_fraction"] = conflict / active
+        open(os.path.join(profiles, f"{kernel_label}_{workload_name}_counters.md"), "w").write("\n".join(md) + "\n")
+    return result
