@@ -68,16 +68,16 @@ const char *const COMBO_NAMES[] = {"f16_f32", "f16_f16", "bf16_bf16", "bf16_f32"
 
 // Names of every kernel variant, built once (thread-safe static init).
 struct NameTable {
-    char at[4][3][3][5][48];
+    char at[NUM_TILE_CFGS][3][3][5][48];
 };
 
 const NameTable &kernel_names()
 {
     static const NameTable table = [] {
-        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64"};
+        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64", "256x256w4"};
         static const char *const MODE_NAMES[] = {"k16", "k4", "t16"};
         NameTable t;
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < NUM_TILE_CFGS; ++a)
             for (int x = 0; x < 3; ++x)
                 for (int y = 0; y < 3; ++y)
                     for (int c = 0; c < 5; ++c)
@@ -237,6 +237,7 @@ int validate(const dmu_gemm_args *a, Plan *plan)
         else
             tile = TILE_128x128;
         if (env && strcmp(env, "256x256") == 0) tile = TILE_256x256;
+        if (env && strcmp(env, "256x256w4") == 0) tile = TILE_256x256_W4;
         if (env && strcmp(env, "256x128") == 0) tile = TILE_256x128;
         if (env && strcmp(env, "128x128") == 0) tile = TILE_128x128;
     }
