@@ -43,9 +43,9 @@ enum Dt { F16 = 1, BF16 = 2, F32 = 3, I8 = 4, I32 = 5 };
 
 // Operand load modes of the tiled kernel.
 enum Mode {
-    KC16 = 0, // K contiguous in memory, 16-byte vectors
-    KC4 = 1,  // K contiguous in memory, 4-byte vectors
-    MC16 = 2  // M (or N) contiguous in memory, 16-byte vectors, transposed on the way to LDS
+    KC16 = 0, // K contiguous, 16-byte-aligned rows, K a multiple of 16 bytes
+    KCD = 1,  // K contiguous, 4-byte-aligned rows, any K: 16-byte loads, K tail masked
+    MC16 = 2  // M (or N) contiguous, 16-byte-aligned rows, M (N) a multiple of 8
 };
 
 // Bytes of one element of a type code.

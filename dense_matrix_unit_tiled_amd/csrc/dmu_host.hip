@@ -75,7 +75,7 @@ const NameTable &kernel_names()
 {
     static const NameTable table = [] {
         static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64", "256x256w4"};
-        static const char *const MODE_NAMES[] = {"k16", "k4", "t16"};
+        static const char *const MODE_NAMES[] = {"k16", "kd", "t16"};
         NameTable t;
         for (int a = 0; a < NUM_TILE_CFGS; ++a)
             for (int x = 0; x < 3; ++x)
@@ -118,8 +118,8 @@ int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, in
     if (kc) {
         if (aligned(p, ld, stride, esz, 16) && (K * esz) % 16 == 0)
             return KC16;
-        if (aligned(p, ld, stride, esz, 4) && (K * esz) % 4 == 0)
-            return KC4;
+        if (aligned(p, ld, stride, esz, 4))
+            return KCD;
         return -1;
     }
     if (esz == 2 && aligned(p, ld, stride, esz, 16) && mn % 8 == 0)

@@ -14,7 +14,7 @@ void clear_error();
 // DMU_OK, or DMU_ERR_HIP with the runtime's message when the last launch failed.
 int check_launch(const char *what);
 
-// Kernel shapes of the tiled kernel (gemm_mfma) and the fallback (gemm_generic).
+// Kernel shapes of the tiled kernel (gemm_tiled) and the fallback (gemm_generic).
 enum TileCfg {
     TILE_256x256 = 0,    // 8 wavefronts 2 x 4, 128 x 64 each (two per SIMD)
     TILE_256x128 = 1,    // 4 wavefronts 2 x 2, 128 x 64 each

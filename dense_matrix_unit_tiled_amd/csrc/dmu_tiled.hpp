@@ -1,4 +1,5 @@
-// The tiled kernel (gemm_tiled) for operands whose rows allow 16-byte loads.
+// The tiled kernel (gemm_tiled) for operands whose rows are at least 4-byte
+// aligned (K-contiguous) or 16-byte aligned (M/N-contiguous).
 //
 // A workgroup of 64*WGM*WGN threads (WGM x WGN wavefronts) computes a BM x BN
 // tile of D; each wavefront owns a (BM/WGM) x (BN/WGN) block of 32 x 32 MFMA
@@ -80,7 +81,7 @@ __device__ __forceinline__ uint32_t swz_t(uint32_t k) { return ((k & 3u) << 1) ^
 // swizzle(row), into physical chunk l%8.  Eight consecutive lanes read one
 // whole 128-byte row segment.
 // ---------------------------------------------------------------------------
-template <int R, int NW> struct KcStage {
+template <int R, int NW, bool MASK> struct KcStage {
     static constexpr int NL = R / (8 * NW);
     static_assert(NL * 8 * NW == R, "whole 1 KiB transfers per wavefront");
     uint32_t base[NL]; // byte offset at K-tile 0, or OOB
@@ -97,11 +98,24 @@ template <int R, int NW> struct KcStage {
             base[i] = (int64_t)row < rows_valid ? (uint32_t)(row * ld_bytes + cb[i]) : OOB;
         }
     }
-    // K-tile kt: bytes kt*128 .. +127 of each row (k_bytes = K * element size)
+    // K-tile kt: bytes kt*128 .. +127 of each row (k_bytes = K * element size).
+    // MASK: rows are only 4-byte aligned and K * element size need not be a
+    // multiple of 16, so the vector that straddles the end of a row also holds
+    // bytes of the next row; they are cleared here (the range check of the
+    // buffer descriptor already zeroes whatever lies past the slice).
     __device__ __forceinline__ u32x4 load(int i, __amdgpu_buffer_rsrc_t r, int kt, uint32_t k_bytes, uint32_t) const
     {
         const uint32_t kb0 = (uint32_t)kt * 128u;
-        return load16(r, (base[i] != OOB && kb0 + cb[i] < k_bytes) ? base[i] + kb0 : OOB);
+        u32x4 x = load16(r, (base[i] != OOB && kb0 + cb[i] < k_bytes) ? base[i] + kb0 : OOB);
+        if constexpr (MASK) {
+            const int32_t rem = (int32_t)k_bytes - (int32_t)(kb0 + cb[i]); // bytes of the vector inside the row
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int32_t vb = rem - 4 * d;
+                x[d] &= vb >= 4 ? 0xffffffffu : (vb <= 0 ? 0u : ((1u << (8 * vb)) - 1u));
+            }
+        }
+        return x;
     }
     static __device__ __forceinline__ u32x4 frag(const char *tile, uint32_t row0, uint32_t ks, uint32_t lane)
     {
@@ -241,7 +255,8 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
 }
 
 template <int MODE, int R, int NW> struct StageOf;
-template <int R, int NW> struct StageOf<KC16, R, NW> { typedef KcStage<R, NW> type; };
+template <int R, int NW> struct StageOf<KC16, R, NW> { typedef KcStage<R, NW, false> type; };
+template <int R, int NW> struct StageOf<KCD, R, NW> { typedef KcStage<R, NW, true> type; };
 template <int R, int NW> struct StageOf<MC16, R, NW> { typedef McStage<R, NW> type; };
 
 template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
@@ -253,8 +268,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     constexpr int WTM = BM / WGM, WTN = BN / WGN; // wavefront tile
     constexpr int MT = WTM / 32, NT = WTN / 32;   // MFMA tiles per wavefront
     constexpr int ABYTES = BM * 128, STAGE = (BM + BN) * 128;
-    static_assert(AMODE == KC16 || E == 2, "transposed operands are 16-bit");
-    static_assert(BMODE == KC16 || E == 2, "transposed operands are 16-bit");
+    static_assert(AMODE != MC16 || E == 2, "transposed operands are 16-bit");
+    static_assert(BMODE != MC16 || E == 2, "transposed operands are 16-bit");
     typedef typename Mfma<T>::acc_t acc_t;
     typedef typename StageOf<AMODE, BM, NW>::type ATile;
     typedef typename StageOf<BMODE, BN, NW>::type BTile;
@@ -272,18 +287,22 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     // row (K-contiguous) or column (M/N-contiguous) to the end of the batch slice.
     const char *Ab = p.A + (int64_t)tc.b * p.stride_a * E;
     const char *Bb = p.B + (int64_t)tc.b * p.stride_b * E;
-    const int64_t a_start = AMODE == KC16 ? m0 * p.lda * E : m0 * E;
-    const int64_t b_start = BMODE == KC16 ? n0 * p.ldb * E : n0 * E;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)(p.a_bytes - a_start));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)(p.b_bytes - b_start));
+    const int64_t a_start = AMODE != MC16 ? m0 * p.lda * E : m0 * E;
+    const int64_t b_start = BMODE != MC16 ? n0 * p.ldb * E : n0 * E;
+    // The range check works per dword, and a slice may end inside one (4-byte
+    // aligned rows, odd byte counts): the byte counts are rounded up to whole
+    // dwords so that the straddling dword keeps its valid head; its tail is
+    // cleared by the K-tail mask, and a dword never crosses a page.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)((p.a_bytes - a_start + 3) & ~3ll));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)((p.b_bytes - b_start + 3) & ~3ll));
 
     ATile ta;
     BTile tb;
     ta.init(p.lda * E, p.M - m0, wave, lane);
     tb.init(p.ldb * E, p.N - n0, wave, lane);
     // per-operand K extent and K-tile step for the loads
-    const uint32_t a_kdim = AMODE == KC16 ? (uint32_t)p.K * E : (uint32_t)p.K;
-    const uint32_t b_kdim = BMODE == KC16 ? (uint32_t)p.K * E : (uint32_t)p.K;
+    const uint32_t a_kdim = AMODE != MC16 ? (uint32_t)p.K * E : (uint32_t)p.K;
+    const uint32_t b_kdim = BMODE != MC16 ? (uint32_t)p.K * E : (uint32_t)p.K;
     const uint32_t a_step = (uint32_t)(64 * p.lda * E), b_step = (uint32_t)(64 * p.ldb * E);
 
     u32x4 sa[NA], sb[NB]; // the next K-tile between its global loads and its LDS writes

@@ -101,7 +101,7 @@ def test_empty_problems_launch_nothing():
      "mfma_256x256_k16_t16_bf16_bf16"),
     (dict(in_type="f16", out_type="f32"), "mfma_128x128_k16_t16_f16_f32"),
     (dict(M=5000, N=3000, K=2050, lda=2050, layout_b="col", ldb=2050, ldd=3000, in_type="f16",
-          out_type="f16", acc_type="f16"), "mfma_256x256_k4_k4_f16_f16"),
+          out_type="f16", acc_type="f16"), "mfma_256x256_kd_kd_f16_f16"),
     (dict(M=8192, N=8192, K=8192, lda=8192, layout_b="col", ldb=8192, ldd=8192, in_type="i8",
           out_type="i32"), "mfma_256x256_k16_k16_i8_i32"),
     (dict(M=4096, N=128, K=4096, lda=4096, ldb=128, ldd=128, batch=32, stride_a=4096 * 4096,

@@ -270,3 +270,15 @@ def test_fp16_subnormal_outputs_exact():
     got = gu.run_dmu(p)
     gu.assert_bits_equal(got, gu.run_oracle(p))
     assert np.any((got & 0x7C00) == 0) and np.any(got != 0)
+
+
+@pytest.mark.parametrize("cfg,K,pad", [("c3", 2049, 3), ("c3", 2050, 0), ("c3", 131, 1), ("c5", 65, 3),
+                                       ("c5", 130, 2), ("c5", 4097, 3), ("c3", 65, 3)])
+def test_dword_aligned_rows_masked_k_tail(cfg, K, pad):
+    """Rows only 4-byte aligned and K not a multiple of 16 bytes: the tiled kernel's
+    16-byte loads straddle row ends and must clear the next row's bytes."""
+    p = workloads.make(cfg, "random", 13, M=300, N=200, K=K, pad=pad)
+    got, name = gu.run_dmu(p, return_name=True)
+    assert "_kd_" in name, name
+    gu.assert_close(got, gu.run_oracle(p), p, where=gu.valid_mask(p))
+    gu.assert_bits_equal(got, gu.run_dmu(p, force="generic"), where=gu.valid_mask(p))
