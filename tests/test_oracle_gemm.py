@@ -143,16 +143,19 @@ def test_int8_extremes():
     assert D[0] == -(2 ** 31)
 
 
-def test_gemm_at_matches_full_product():
-    p = workloads.make("c3", "random", 3, M=70, N=33, K=130, with_c=True)
-    full = run_oracle(p).reshape(p.M, p.ldd)
+@pytest.mark.parametrize("cfg,batch", [("c3", 1), ("c5", 3), ("c4s", 2)])
+def test_gemm_at_matches_full_product(cfg, batch):
+    p = workloads.make(cfg, "random", 3, M=70, N=33, K=130, batch=batch, with_c=True)
+    full = run_oracle(p)
     rng = np.random.default_rng(0)
-    bij = np.stack([np.zeros(200, dtype=np.int64), rng.integers(0, p.M, 200),
-                    rng.integers(0, p.N, 200)], axis=1)
+    bij = np.stack([rng.integers(0, p.batch, 300), rng.integers(0, p.M, 300),
+                    rng.integers(0, p.N, 300)], axis=1)
     got = oracle.gemm_at(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, bij, in_type=p.in_type,
                          out_type=p.out_type, layout_a=p.layout_a, layout_b=p.layout_b,
-                         C=p.C, ldc=p.ldc)
-    assert np.array_equal(got, full[bij[:, 1], bij[:, 2]])
+                         batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b,
+                         C=p.C, ldc=p.ldc, stride_c=p.stride_c)
+    want = full[bij[:, 0] * p.stride_d + bij[:, 1] * p.ldd + bij[:, 2]]
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
 
 
 def test_thread_count_does_not_change_result():
@@ -178,3 +181,25 @@ def test_rejects_bad_arguments():
     with pytest.raises(ValueError):  # buffer too small for the stated shape
         oracle.gemm(4, 4, 4, np.zeros(8, np.uint16), 4, np.zeros(16, np.uint16), 4,
                     in_type="f16", out_type="f32")
+
+
+@pytest.mark.parametrize("t,terms,want", [
+    # bf16: 1 + 2^-8 is the midpoint between 1 and 1 + 2^-7; the 2^-30 term puts the
+    # exact sum above it (round up), but an fp32 intermediate would drop that term
+    # (fp32 spacing at 1 is 2^-23) and round the tie to even (down to 1).
+    ("bf16", [1.0, 2.0 ** -8, 2.0 ** -30], 0x3F81),
+    # fp16: 1 + 2^-11 is the midpoint between 1 and 1 + 2^-10; 2^-24 is itself a tie
+    # of fp32 at 1 and would be lost through an fp32 intermediate.
+    ("f16", [1.0, 2.0 ** -11, 2.0 ** -24], 0x3C01),
+])
+def test_single_rounding_of_the_fp64_sum(t, terms, want):
+    """The sum is rounded once, from fp64, to the 16-bit output type (no fp32 stage)."""
+    K = len(terms)
+    A = workloads.to_bits(np.array(terms), t)
+    B = workloads.to_bits(np.ones(K), t)
+    assert np.array_equal(oracle.decode(t, A), terms)  # the terms are exact in t
+    D = oracle.gemm(1, 1, K, A, K, B, 1, in_type=t, out_type=t)
+    assert int(D[0]) == want
+    # and with the k order reversed the result is the same (the fp64 sum is exact here)
+    D = oracle.gemm(1, 1, K, A[::-1].copy(), K, B, 1, in_type=t, out_type=t)
+    assert int(D[0]) == want

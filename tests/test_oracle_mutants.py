@@ -1,0 +1,109 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case below plants one mistake in a copy of ``oracle/oracle.c`` (a dropped
+term, a wrong sign, index or stride, a transposed operand, a wrong rounding
+rule, a wrong codec constant), builds that copy into a temporary library, and
+runs the oracle pin suite (tests/test_oracle_gemm.py, tests/test_oracle_codecs.py)
+against it in a child process.  The suite must fail for every mutant; a mutant
+that survives is a mistake the pins would not see.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, exact text in oracle.c, replacement)
+MUTANTS = [
+    ("A transposed", "load_fp(j->A, j->in_type, oa + at(j->layout_a, i, k, j->lda))",
+     "load_fp(j->A, j->in_type, oa + at(j->layout_a, k, i, j->lda))"),
+    ("B transposed", "accf[c] += a * load_fp(j->B, j->in_type, ob + at(j->layout_b, k, c, j->ldb))",
+     "accf[c] += a * load_fp(j->B, j->in_type, ob + at(j->layout_b, c, k, j->ldb))"),
+    ("int B transposed", "load_int(j->B, OR_I8, ob + at(j->layout_b, k, c, j->ldb))",
+     "load_int(j->B, OR_I8, ob + at(j->layout_b, c, k, j->ldb))"),
+    ("selected elements: A transposed", "load_fp(A, in_type, oa + at(layout_a, i, k, lda))",
+     "load_fp(A, in_type, oa + at(layout_a, k, i, lda))"),
+    ("selected elements: batch stride of B ignored", "ob = b * stride_b,", "ob = 0 * stride_b,"),
+    ("selected elements: C dropped", "acc += load_fp(C, out_type", "acc += 0.0 * load_fp(C, out_type"),
+    ("selected elements: int k dropped", "for (int64_t k = 0; k < K; ++k)\n                acc += load_int",
+     "for (int64_t k = 1; k < K; ++k)\n                acc += load_int"),
+    ("column-major ignored", "r * ld + c : r + c * ld", "r * ld + c : r * ld + c"),
+    ("C dropped", "v += load_fp(j->C", "v += 0.0 * load_fp(j->C"),
+    ("int C subtracted", "v += load_int(j->C", "v -= load_int(j->C"),
+    ("last k dropped", "for (int64_t k = 0; k < j->K; ++k) {\n                const double",
+     "for (int64_t k = 0; k + 1 < j->K; ++k) {\n                const double"),
+    ("first int k dropped", "for (int64_t k = 0; k < j->K; ++k) {\n                const int64_t",
+     "for (int64_t k = 1; k < j->K; ++k) {\n                const int64_t"),
+    ("product sign", "accf[c] += a * load_fp", "accf[c] -= a * load_fp"),
+    ("fp32 accumulator", "accf[c] += a * load_fp(j->B, j->in_type, ob + at(j->layout_b, k, c, j->ldb));",
+     "accf[c] = (float)(accf[c] + a * load_fp(j->B, j->in_type, ob + at(j->layout_b, k, c, j->ldb)));"),
+    ("fp32 intermediate before 16-bit output", "store_out(j->D, j->out_type, od + i * j->ldd + c, v);",
+     "store_out(j->D, j->out_type, od + i * j->ldd + c, (double)(float)v);"),
+    ("ties away from zero", "(frac == 0.5 && fmod(r, 2.0) != 0.0)", "(frac == 0.5)"),
+    ("truncation", "if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))", "if (0)"),
+    ("subnormal outputs flushed", "return sign_bit | n;", "return sign_bit;"),
+    ("overflow limit off by one", "if (e > emax)", "if (e > emax + 1)"),
+    ("fp16 subnormal scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("fp16 exponent bias", "e - 25); /* (1024+m)", "e - 24); /* (1024+m)"),
+    ("bf16 exponent bias", "e - 134); /* (128+m)", "e - 133); /* (128+m)"),
+    ("bf16 mantissa width", "m = h & 0x7f;", "m = h & 0x3f;"),
+    ("batch stride of A ignored", "const int64_t oa = b * j->stride_a", "const int64_t oa = 0 * j->stride_a"),
+    ("batch stride of B ignored", "ob = b * j->stride_b;", "ob = 0 * j->stride_b;"),
+    ("batch stride of C ignored", "const int64_t oc = b * j->stride_c", "const int64_t oc = 0 * j->stride_c"),
+    ("ldc taken as N", "v += load_fp(j->C, j->out_type, oc + i * j->ldc + c);",
+     "v += load_fp(j->C, j->out_type, oc + i * j->N + c);"),
+    ("int8 read unsigned", "(int64_t)((const int8_t *)p)[idx]", "(int64_t)((const uint8_t *)p)[idx]"),
+    ("int32 saturates", "static int32_t wrap_i32(int64_t v) { return (int32_t)(uint32_t)(uint64_t)v; }",
+     "static int32_t wrap_i32(int64_t v) { return v > INT32_MAX ? INT32_MAX : "
+     "(v < INT32_MIN ? INT32_MIN : (int32_t)v); }"),
+]
+
+RUNNER = (
+    "import sys, pytest, oracle\n"
+    "oracle.LIB_PATH = sys.argv[1]\n"
+    "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '--no-header',\n"
+    "                      'tests/test_oracle_gemm.py', 'tests/test_oracle_codecs.py']))\n"
+)
+
+
+def _build_mutant(tmp, idx, old, new):
+    src = open(SRC).read()
+    if old is not None:
+        assert src.count(old) == 1, f"mutation site not unique or missing: {old!r}"
+        src = src.replace(old, new)
+    path_c = os.path.join(tmp, f"mutant{idx}.c")
+    path_so = os.path.join(tmp, f"mutant{idx}.so")
+    open(path_c, "w").write(src)
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+                    "-shared", "-pthread", "-o", path_so, path_c, "-lm"], check=True)
+    return path_so
+
+
+def _run_pins(lib):
+    r = subprocess.run([sys.executable, "-c", RUNNER, lib], cwd=ROOT, capture_output=True,
+                       text=True, timeout=600)
+    return r.returncode, r.stdout[-2000:] + r.stderr[-2000:]
+
+
+@pytest.fixture(scope="module")
+def outcomes(tmp_path_factory):
+    tmp = str(tmp_path_factory.mktemp("mutants"))
+    libs = [_build_mutant(tmp, i, old, new) for i, (_, old, new) in enumerate(MUTANTS)]
+    libs.append(_build_mutant(tmp, len(MUTANTS), None, None))  # unmutated control
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        return list(ex.map(_run_pins, libs))
+
+
+def test_unmutated_copy_passes(outcomes):
+    rc, out = outcomes[-1]
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("idx", range(len(MUTANTS)), ids=[m[0] for m in MUTANTS])
+def test_pins_fail_on_mutant(outcomes, idx):
+    rc, out = outcomes[idx]
+    assert rc == 1, f"mutant '{MUTANTS[idx][0]}' survived the pins (exit {rc}):\n{out}"
