@@ -18,8 +18,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libdmu.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed fp32 VALU ops are disabled for all device code (see DESIGN notes on the
-# code generation policy); the host pass warns that it does not know the feature.
+# Packed fp32 VALU instructions are disabled for all device code: this library
+# does not use them, and hipcc -O3 would otherwise form them from plain float
+# code.  The host pass warns that it does not know the feature.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-munsafe-fp-atomics", "-ffp-contract=fast"]

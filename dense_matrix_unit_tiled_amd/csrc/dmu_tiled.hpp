@@ -36,9 +36,10 @@
 //
 // The K-tile body is an explicit issue schedule: every MFMA is followed by a
 // few of the memory instructions the wavefront owes (next K-step's fragment
-// reads, next K-tile's global loads in K-steps 0-1 and LDS writes in K-steps
-// 2-3), with scheduling barriers so that the compiler keeps that order and the
-// matrix core never waits behind a burst of memory instructions.
+// reads; in K-steps 0-2 the LDS writes of the next K-tile, each followed by the
+// global load of the K-tile after it into the same staging registers), with
+// scheduling barriers so that the compiler keeps that order and the matrix
+// core never waits behind a burst of memory instructions.
 #pragma once
 
 #include "dmu_device.hpp"
@@ -254,6 +255,28 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
     }
 }
 
+// Fragment that the MFMA sequence q = 0 .. MT*NT-1 (A fragment q / NT, B
+// fragment q % NT) needs idx-th: A fragments are 0..MT-1, B fragments MT.. .
+template <int MT, int NT> __device__ constexpr int first_use(int idx)
+{
+    unsigned seen_a = 0, seen_b = 0;
+    int n = 0;
+    for (int q = 0; q < MT * NT; ++q) {
+        const int a = q / NT, b = q % NT;
+        if (!((seen_a >> a) & 1u)) {
+            if (n++ == idx)
+                return a;
+            seen_a |= 1u << a;
+        }
+        if (!((seen_b >> b) & 1u)) {
+            if (n++ == idx)
+                return MT + b;
+            seen_b |= 1u << b;
+        }
+    }
+    return -1;
+}
+
 template <int MODE, int R, int NW> struct StageOf;
 template <int R, int NW> struct StageOf<KC16, R, NW> { typedef KcStage<R, NW, false> type; };
 template <int R, int NW> struct StageOf<KCD, R, NW> { typedef KcStage<R, NW, true> type; };
@@ -318,8 +341,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         else
             *reinterpret_cast<u32x4 *>(stage + ABYTES + (wave * NB + (c - NA)) * 1024 + lane * 16) = sb[c - NA];
     };
-    // Fragment f (0..MT-1: A rows; MT..MT+NT-1: B columns) of K-step ks.
+    // The f-th fragment read of K-step ks, in the order of first use by the
+    // MFMA sequence (fragment g: 0..MT-1 A rows, MT..MT+NT-1 B columns).
     auto read_one = [&](int f, const char *stage, int ks, u32x4 *af, u32x4 *bf) {
+        f = first_use<MT, NT>(f);
         if (f < MT)
             af[f] = ATile::frag(stage, wm * WTM + f * 32, ks, lane);
         else
@@ -348,16 +373,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
             store_one(c, smem);
+#pragma unroll
+        for (int c = 0; c < NLD; ++c)
+            load_one(c, 1);
         stage_barrier();
 #pragma unroll
         for (int f = 0; f < NF; ++f)
             read_one(f, smem, 0, af[0], bfr[0]);
     }
 
-    // After the last K-tile the same schedule runs on "K-tile nk", which lies
-    // wholly past K: the buffer range check turns its loads into zeros, so the
-    // body needs no branches (branches around the loads make the compiler
+    // Staging registers run one K-tile ahead of the LDS stages: in K-tile kt,
+    // register c is written to the free stage (K-tile kt+1) and at once
+    // reloaded with K-tile kt+2, so every global load has a whole K-tile of
+    // MFMAs to arrive.  Near the end the same schedule runs on K-tiles that lie
+    // wholly past K: the buffer range check turns their loads into zeros, so
+    // the body needs no branches (branches around the loads make the compiler
     // drain the memory counters at every join).
+    constexpr int SLOTS = 3 * MN; // MFMAs of K-steps 0-2 carry the copies
     for (int kt = 0; kt < nk; ++kt) {
         const char *cur = smem + (kt & 1) * STAGE;
         char *nxt = smem + ((kt + 1) & 1) * STAGE;
@@ -371,28 +403,22 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
 #pragma unroll
                 for (int f = q * NF / MN; f < (q + 1) * NF / MN; ++f)
                     read_one(f, cur, ks + 1, af[n], bfr[n]);
-                if (ks < 2) { // global loads [slot*NLD/(2 MN), (slot+1)*NLD/(2 MN)) of K-tile kt+1
-                    const int slot = ks * MN + q;
+                // staging registers [slot*NLD/SLOTS, (slot+1)*NLD/SLOTS): K-tile kt+1 to
+                // LDS, then the loads of K-tile kt+2
+                const int slot = ks * MN + q;
 #pragma unroll
-                    for (int ci = slot * NLD / (2 * MN); ci < (slot + 1) * NLD / (2 * MN); ++ci)
-                        load_one(ci, kt + 1);
-                } else { // LDS writes, first two thirds
-#pragma unroll
-                    for (int ci = q * NLD / (3 * MN / 2); ci < (q + 1) * NLD / (3 * MN / 2); ++ci)
-                        store_one(ci, nxt);
+                for (int ci = slot * NLD / SLOTS; ci < (slot + 1) * NLD / SLOTS; ++ci) {
+                    store_one(ci, nxt);
+                    load_one(ci, kt + 2);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // K-step 3: half of its MFMAs with the remaining LDS writes, the stage
-        // hand-over, then the other half with the first reads of K-tile kt+1.
+        // K-step 3: half of its MFMAs, the stage hand-over, then the other half
+        // with the first fragment reads of K-tile kt+1.
 #pragma unroll
         for (int q = 0; q < MN / 2; ++q) {
             acc[q / NT][q % NT] = Mfma<T>::step(bfr[1][q % NT], af[1][q / NT], acc[q / NT][q % NT]);
-            const int slot = MN + q;
-#pragma unroll
-            for (int ci = slot * NLD / (3 * MN / 2); ci < (slot + 1) * NLD / (3 * MN / 2); ++ci)
-                store_one(ci, nxt);
             __builtin_amdgcn_sched_barrier(0);
         }
         stage_barrier();
