@@ -8,6 +8,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -21,19 +22,46 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code: this library
 # does not use them, and hipcc -O3 would otherwise form them from plain float
 # code.  The host pass warns that it does not know the feature.
+#
+# The kernels index register arrays only with indices that are constant after
+# full unrolling; a loop the compiler declines to unroll would turn such an
+# array into scratch memory.  The unroll threshold is therefore raised, a loop
+# that stays rolled is an error, and the per-kernel resource report is checked:
+# a kernel with scratch memory or VGPR spills fails the build (SGPR spills go
+# to VGPR lanes, not to memory; they are listed in _build/resource_usage.txt).
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-munsafe-fp-atomics", "-ffp-contract=fast"]
+                "-munsafe-fp-atomics", "-ffp-contract=fast",
+                "-mllvm", "-pragma-unroll-threshold=1000000", "-Werror=pass-failed",
+                "-Rpass-analysis=kernel-resource-usage"]
+
+_REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill|VGPRs|AGPRs|"
+                     r"Occupancy \[waves/SIMD\]):\s*(\S+)")
 
 
-def _compile(src: str) -> str:
+def resource_usage(text: str) -> list:
+    """[{kernel, VGPRs, AGPRs, ScratchSize, ...}] from the compiler's resource remarks."""
+    out = []
+    for key, val in _REMARK.findall(text):
+        if key == "Function Name":
+            out.append({"kernel": val})
+        elif out:
+            out[-1][key.split(" [")[0]] = int(val)
+    return out
+
+
+def _compile(src: str) -> tuple:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
     cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed for {src}")
-    return obj
+    usage = resource_usage(r.stderr)
+    bad = [u for u in usage if u.get("ScratchSize", 0) or u.get("VGPRs Spill", 0)]
+    if bad:
+        raise RuntimeError(f"{src}: kernels with scratch memory or spills: {bad}")
+    return obj, usage
 
 
 def build(jobs: int | None = None) -> str:
@@ -41,7 +69,12 @@ def build(jobs: int | None = None) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(len(srcs), max(1, len(os.sched_getaffinity(0))), 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        results = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in results]
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as fh:
+        for _, usage in results:
+            for u in usage:
+                fh.write(" ".join(f"{k}={v}" for k, v in u.items()) + "\n")
     tmp = LIB_PATH + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                    check=True)

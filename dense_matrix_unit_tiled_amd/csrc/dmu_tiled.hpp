@@ -256,25 +256,12 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
 }
 
 // Fragment that the MFMA sequence q = 0 .. MT*NT-1 (A fragment q / NT, B
-// fragment q % NT) needs idx-th: A fragments are 0..MT-1, B fragments MT.. .
+// fragment q % NT) needs idx-th: A 0 with B 0, then B 1 .. NT-1 (with A 0),
+// then A 1 .. MT-1.  A fragments are numbered 0..MT-1, B fragments MT.. .
+// (A closed form, so that it folds to a constant in every unrolled loop.)
 template <int MT, int NT> __device__ constexpr int first_use(int idx)
 {
-    unsigned seen_a = 0, seen_b = 0;
-    int n = 0;
-    for (int q = 0; q < MT * NT; ++q) {
-        const int a = q / NT, b = q % NT;
-        if (!((seen_a >> a) & 1u)) {
-            if (n++ == idx)
-                return a;
-            seen_a |= 1u << a;
-        }
-        if (!((seen_b >> b) & 1u)) {
-            if (n++ == idx)
-                return MT + b;
-            seen_b |= 1u << b;
-        }
-    }
-    return -1;
+    return idx == 0 ? 0 : (idx <= NT ? MT + idx - 1 : idx - NT);
 }
 
 template <int MODE, int R, int NW> struct StageOf;
