@@ -20,6 +20,7 @@ from .build import LIB_PATH, build
 
 TYPES = {"f16": 1, "bf16": 2, "f32": 3, "i8": 4, "i32": 5}
 LAYOUTS = {"row": 0, "col": 1}
+ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2}
 _NP_IN = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32, "i8": np.int8, "i32": np.int32}
 
 _lib = None
@@ -38,6 +39,11 @@ def _load():
     lib.oracle_gemm.restype = i32
     lib.oracle_gemm_at.argtypes = common + [i64, vp, vp]
     lib.oracle_gemm_at.restype = i32
+    ep = [vp, i64, vp, i64, vp, i64, i32]
+    lib.oracle_gemm_ex.argtypes = common + ep + [vp, i64, i64, i32]
+    lib.oracle_gemm_ex.restype = i32
+    lib.oracle_gemm_at_ex.argtypes = common + ep + [i64, vp, vp]
+    lib.oracle_gemm_at_ex.restype = i32
     lib.oracle_decode_array.argtypes = [i32, vp, vp, i64]
     lib.oracle_decode_array.restype = None
     lib.oracle_encode_array.argtypes = [i32, vp, vp, i64]
@@ -78,7 +84,7 @@ def _common(M, N, K, A, lda, B, ldb, in_type, out_type, layout_a, layout_b, batc
             stride_a, stride_b, C, ldc, stride_c):
     if in_type not in ("f16", "bf16", "f32", "i8"):
         raise ValueError(f"unsupported input type {in_type}")
-    acc_t = "i32" if in_type == "i8" else out_type
+    acc_t = out_type  # C has the output type
     span = lambda s, e: 0 if batch == 0 or e == 0 else (batch - 1) * s + e
     A = _prep(A, in_type, span(stride_a, _extent(layout_a, M, K, lda)), "A")
     B = _prep(B, in_type, span(stride_b, _extent(layout_b, K, N, ldb)), "B")
@@ -88,33 +94,59 @@ def _common(M, N, K, A, lda, B, ldb, in_type, out_type, layout_a, layout_b, batc
     return args, (A, B, C)
 
 
+def _epilogue(M, N, batch, row_scale, stride_rs, col_scale, stride_cs, bias, stride_bias, act):
+    def vec(x, n, stride, name):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        need = 0 if batch == 0 or n == 0 else (batch - 1) * stride + n
+        if x.size < need:
+            raise ValueError(f"{name}: holds {x.size} values, needs {need}")
+        return x
+    rs = vec(row_scale, M, stride_rs, "row_scale")
+    cs = vec(col_scale, N, stride_cs, "col_scale")
+    bs = vec(bias, N, stride_bias, "bias")
+    return (_ptr(rs), stride_rs, _ptr(cs), stride_cs, _ptr(bs), stride_bias, ACTS[act]), (rs, cs, bs)
+
+
 def gemm(M, N, K, A, lda, B, ldb, *, in_type, out_type, layout_a="row", layout_b="row",
          batch=1, stride_a=0, stride_b=0, C=None, ldc=0, stride_c=0, ldd=None, stride_d=None,
-         nthreads=None):
-    """Full D (flat, batch*stride_d elements; row-major M x N with leading dim ldd)."""
+         nthreads=None, row_scale=None, stride_rs=0, col_scale=None, stride_cs=0, bias=None,
+         stride_bias=0, act="none"):
+    """Full D (flat, batch*stride_d elements; row-major M x N with leading dim ldd).
+
+    row_scale (M per batch), col_scale (N per batch), bias (N per batch; all
+    float32) and act ("none", "relu", "gelu_tanh") form the optional epilogue.
+    """
     ldd = N if ldd is None else ldd
     stride_d = M * ldd if stride_d is None else stride_d
     args, keep = _common(M, N, K, A, lda, B, ldb, in_type, out_type, layout_a, layout_b, batch,
                          stride_a, stride_b, C, ldc, stride_c)
+    ep, keep_ep = _epilogue(M, N, batch, row_scale, stride_rs, col_scale, stride_cs, bias,
+                            stride_bias, act)
     D = np.zeros(max(batch * stride_d, 1), dtype=_NP_IN[out_type])
-    st = _load().oracle_gemm(*args, _ptr(D), ldd, stride_d, nthreads or default_threads())
+    st = _load().oracle_gemm_ex(*args, *ep, _ptr(D), ldd, stride_d, nthreads or default_threads())
     if st:
         raise ValueError(f"oracle_gemm rejected its arguments (code {st})")
-    del keep
+    del keep, keep_ep
     return D[: batch * stride_d]
 
 
 def gemm_at(M, N, K, A, lda, B, ldb, bij, *, in_type, out_type, layout_a="row",
-            layout_b="row", batch=1, stride_a=0, stride_b=0, C=None, ldc=0, stride_c=0):
+            layout_b="row", batch=1, stride_a=0, stride_b=0, C=None, ldc=0, stride_c=0,
+            row_scale=None, stride_rs=0, col_scale=None, stride_cs=0, bias=None, stride_bias=0,
+            act="none"):
     """D[b](i,j) for each row (b, i, j) of the integer array ``bij`` (shape [n, 3])."""
     args, keep = _common(M, N, K, A, lda, B, ldb, in_type, out_type, layout_a, layout_b, batch,
                          stride_a, stride_b, C, ldc, stride_c)
+    ep, keep_ep = _epilogue(M, N, batch, row_scale, stride_rs, col_scale, stride_cs, bias,
+                            stride_bias, act)
     bij = np.ascontiguousarray(bij, dtype=np.int64).reshape(-1, 3)
     out = np.zeros(max(len(bij), 1), dtype=_NP_IN[out_type])
-    st = _load().oracle_gemm_at(*args, len(bij), _ptr(bij), _ptr(out))
+    st = _load().oracle_gemm_at_ex(*args, *ep, len(bij), _ptr(bij), _ptr(out))
     if st:
         raise ValueError(f"oracle_gemm_at rejected its arguments (code {st})")
-    del keep
+    del keep, keep_ep
     return out[: len(bij)]
 
 

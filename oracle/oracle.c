@@ -29,6 +29,22 @@
  * summed exactly in int64, C (int32) is added, and the result is narrowed to
  * int32 by two's-complement wrap-around.
  *
+ * Optional fused epilogue ("Tensor Cores, CUTLASS and CuTe", section 5: the
+ * scaled-mm epilogue multiplies the accumulator by a per-column and a per-row
+ * scale before the bf16 conversion; section 7: the bias + ReLU / tanh-GELU
+ * epilogue of the fused linear layer):
+ *
+ *     D[b](i,j) = round_out( act( rs[b](i) * cs[b](j) * P + bias[b](j) + C[b](i,j) ) )
+ *
+ * where P is the product sum above (for int8 inputs: the int32 accumulator,
+ * i.e. the exact sum narrowed by wrap-around, then taken as a real number),
+ * rs / cs / bias default to 1 / 1 / 0 when absent, and act is the identity,
+ * ReLU (x > 0 ? x : +0) or the tanh form of GELU,
+ * 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), evaluated through the
+ * identity 0.5 (1 + tanh u) = 1 / (1 + e^(-2u)).  All of it is evaluated in
+ * fp64 and rounded once.  int8 inputs may then have fp32, fp16 or bf16 output
+ * (dequantisation); int32 output takes no epilogue.
+ *
  * An "fp16 accumulate" request is the same computation with fp16 C and D: the
  * exact sum is rounded once to fp16 (no matrix instruction of the target chip
  * accumulates in fp16; the result is the best fp16 answer).
@@ -48,6 +64,7 @@
 
 enum { OR_F16 = 1, OR_BF16 = 2, OR_F32 = 3, OR_I8 = 4, OR_I32 = 5 };
 enum { OR_ROW = 0, OR_COL = 1 };
+enum { OR_ACT_NONE = 0, OR_ACT_RELU = 1, OR_ACT_GELU_TANH = 2 };
 
 /* ------------------------------------------------------------------ */
 /* Codecs                                                              */
@@ -192,6 +209,11 @@ typedef struct {
     const void *B; int64_t ldb, stride_b;
     const void *C; int64_t ldc, stride_c;
     void *D; int64_t ldd, stride_d;
+    /* epilogue (NULL / OR_ACT_NONE: absent) */
+    const float *rs; int64_t stride_rs;
+    const float *cs; int64_t stride_cs;
+    const float *bias; int64_t stride_bias;
+    int act;
     /* work split: rows [row_begin, row_end) of the flattened (batch*M) range */
     int64_t row_begin, row_end;
     int status;
@@ -207,14 +229,42 @@ static int check_args(const job_t *j)
         if (j->out_type != OR_F16 && j->out_type != OR_BF16 && j->out_type != OR_F32)
             return 2;
     } else if (j->in_type == OR_I8) {
-        if (j->out_type != OR_I32)
+        if (j->out_type == OR_I32) {
+            if (j->rs || j->cs || j->bias || j->act != OR_ACT_NONE)
+                return 2; /* integer output takes no epilogue */
+        } else if (j->out_type != OR_F16 && j->out_type != OR_BF16 && j->out_type != OR_F32) {
             return 2;
+        }
     } else {
         return 2;
     }
+    if (j->act < OR_ACT_NONE || j->act > OR_ACT_GELU_TANH)
+        return 3;
     if ((j->layout_a != OR_ROW && j->layout_a != OR_COL) || (j->layout_b != OR_ROW && j->layout_b != OR_COL))
         return 3;
     return 0;
+}
+
+/* The epilogue on one value: p is the product sum (fp64, exact for int8). */
+static double epilogue(const job_t *j, int64_t b, int64_t i, int64_t c, double p, double addend)
+{
+    double v = p;
+    if (j->rs)
+        v *= (double)j->rs[b * j->stride_rs + i];
+    if (j->cs)
+        v *= (double)j->cs[b * j->stride_cs + c];
+    if (j->bias)
+        v += (double)j->bias[b * j->stride_bias + c];
+    v += addend;
+    if (j->act == OR_ACT_RELU)
+        v = v > 0.0 ? v : 0.0;
+    else if (j->act == OR_ACT_GELU_TANH) {
+        /* 0.5 (1 + tanh u) written as the equal 1 / (1 + e^(-2u)): the sum
+         * 1 + tanh u cancels for strongly negative u, the quotient does not */
+        const double u = sqrt(2.0 / acos(-1.0)) * (v + 0.044715 * v * v * v);
+        v = v / (1.0 + exp(-2.0 * u));
+    }
+    return v;
 }
 
 /* One output row (b, i): the i-k-j order, accumulating a whole row at once. */
@@ -241,10 +291,8 @@ static void *gemm_rows(void *arg)
                     accf[c] += a * load_fp(j->B, j->in_type, ob + at(j->layout_b, k, c, j->ldb));
             }
             for (int64_t c = 0; c < j->N; ++c) {
-                double v = accf[c];
-                if (j->C)
-                    v += load_fp(j->C, j->out_type, oc + i * j->ldc + c);
-                store_out(j->D, j->out_type, od + i * j->ldd + c, v);
+                const double addend = j->C ? load_fp(j->C, j->out_type, oc + i * j->ldc + c) : 0.0;
+                store_out(j->D, j->out_type, od + i * j->ldd + c, epilogue(j, b, i, c, accf[c], addend));
             }
         } else {
             for (int64_t c = 0; c < j->N; ++c)
@@ -255,10 +303,16 @@ static void *gemm_rows(void *arg)
                     acci[c] += a * load_int(j->B, OR_I8, ob + at(j->layout_b, k, c, j->ldb));
             }
             for (int64_t c = 0; c < j->N; ++c) {
-                int64_t v = acci[c];
-                if (j->C)
-                    v += load_int(j->C, OR_I32, oc + i * j->ldc + c);
-                ((int32_t *)j->D)[od + i * j->ldd + c] = wrap_i32(v);
+                if (j->out_type == OR_I32) {
+                    int64_t v = acci[c];
+                    if (j->C)
+                        v += load_int(j->C, OR_I32, oc + i * j->ldc + c);
+                    ((int32_t *)j->D)[od + i * j->ldd + c] = wrap_i32(v);
+                } else { /* dequantisation: the int32 accumulator as a real number */
+                    const double addend = j->C ? load_fp(j->C, j->out_type, oc + i * j->ldc + c) : 0.0;
+                    store_out(j->D, j->out_type, od + i * j->ldd + c,
+                              epilogue(j, b, i, c, (double)wrap_i32(acci[c]), addend));
+                }
             }
         }
     }
@@ -271,6 +325,10 @@ static void *gemm_rows(void *arg)
     int64_t M, int64_t N, int64_t K, int64_t batch, int in_type, int out_type, int layout_a,     \
         int layout_b, const void *A, int64_t lda, int64_t stride_a, const void *B, int64_t ldb, \
         int64_t stride_b, const void *C, int64_t ldc, int64_t stride_c
+
+#define EPILOGUE_ARGS                                                                          \
+    const float *rs, int64_t stride_rs, const float *cs, int64_t stride_cs, const float *bias, \
+        int64_t stride_bias, int act
 
 static job_t make_job(ORACLE_ARGS)
 {
@@ -290,11 +348,15 @@ static job_t make_job(ORACLE_ARGS)
  * contiguous blocks over `nthreads` threads; each output element is computed
  * by one thread with the summation order stated above.
  */
-int oracle_gemm(ORACLE_ARGS, void *D, int64_t ldd, int64_t stride_d, int nthreads)
+int oracle_gemm_ex(ORACLE_ARGS, EPILOGUE_ARGS, void *D, int64_t ldd, int64_t stride_d, int nthreads)
 {
     job_t base = make_job(M, N, K, batch, in_type, out_type, layout_a, layout_b, A, lda, stride_a,
                           B, ldb, stride_b, C, ldc, stride_c);
     base.D = D; base.ldd = ldd; base.stride_d = stride_d;
+    base.rs = rs; base.stride_rs = stride_rs;
+    base.cs = cs; base.stride_cs = stride_cs;
+    base.bias = bias; base.stride_bias = stride_bias;
+    base.act = act;
     int st = check_args(&base);
     if (st)
         return st;
@@ -340,13 +402,17 @@ int oracle_gemm(ORACLE_ARGS, void *D, int64_t ldd, int64_t stride_d, int nthread
 /*
  * Selected elements only: out[s] = D[b](i,j) for (b,i,j) = bij[3s..3s+2],
  * each a single k-ordered dot product (the same sum, in the same order, as
- * oracle_gemm).  `out` holds values of out_type.  Used at sizes where the full
- * product is too slow for a CPU.
+ * the full product) followed by the same epilogue.  `out` holds values of
+ * out_type.  Used at sizes where the full product is too slow for a CPU.
  */
-int oracle_gemm_at(ORACLE_ARGS, int64_t nsample, const int64_t *bij, void *out)
+int oracle_gemm_at_ex(ORACLE_ARGS, EPILOGUE_ARGS, int64_t nsample, const int64_t *bij, void *out)
 {
     job_t j = make_job(M, N, K, batch, in_type, out_type, layout_a, layout_b, A, lda, stride_a, B,
                        ldb, stride_b, C, ldc, stride_c);
+    j.rs = rs; j.stride_rs = stride_rs;
+    j.cs = cs; j.stride_cs = stride_cs;
+    j.bias = bias; j.stride_bias = stride_bias;
+    j.act = act;
     int st = check_args(&j);
     if (st)
         return st;
@@ -360,18 +426,39 @@ int oracle_gemm_at(ORACLE_ARGS, int64_t nsample, const int64_t *bij, void *out)
             for (int64_t k = 0; k < K; ++k)
                 acc += load_fp(A, in_type, oa + at(layout_a, i, k, lda)) *
                        load_fp(B, in_type, ob + at(layout_b, k, c, ldb));
+            double addend = 0.0;
             if (C)
-                acc += load_fp(C, out_type, oc + i * ldc + c);
-            store_out(out, out_type, s, acc);
+                addend += load_fp(C, out_type, oc + i * ldc + c);
+            store_out(out, out_type, s, epilogue(&j, b, i, c, acc, addend));
         } else {
             int64_t acc = 0;
             for (int64_t k = 0; k < K; ++k)
                 acc += load_int(A, OR_I8, oa + at(layout_a, i, k, lda)) *
                        load_int(B, OR_I8, ob + at(layout_b, k, c, ldb));
-            if (C)
-                acc += load_int(C, OR_I32, oc + i * ldc + c);
-            ((int32_t *)out)[s] = wrap_i32(acc);
+            if (out_type == OR_I32) {
+                if (C)
+                    acc += load_int(C, OR_I32, oc + i * ldc + c);
+                ((int32_t *)out)[s] = wrap_i32(acc);
+            } else {
+                const double addend = C ? load_fp(C, out_type, oc + i * ldc + c) : 0.0;
+                store_out(out, out_type, s, epilogue(&j, b, i, c, (double)wrap_i32(acc), addend));
+            }
         }
     }
     return 0;
+}
+
+/* The product without an epilogue. */
+int oracle_gemm(ORACLE_ARGS, void *D, int64_t ldd, int64_t stride_d, int nthreads)
+{
+    return oracle_gemm_ex(M, N, K, batch, in_type, out_type, layout_a, layout_b, A, lda, stride_a, B, ldb,
+                          stride_b, C, ldc, stride_c, NULL, 0, NULL, 0, NULL, 0, OR_ACT_NONE, D, ldd,
+                          stride_d, nthreads);
+}
+
+int oracle_gemm_at(ORACLE_ARGS, int64_t nsample, const int64_t *bij, void *out)
+{
+    return oracle_gemm_at_ex(M, N, K, batch, in_type, out_type, layout_a, layout_b, A, lda, stride_a, B,
+                             ldb, stride_b, C, ldc, stride_c, NULL, 0, NULL, 0, NULL, 0, OR_ACT_NONE,
+                             nsample, bij, out);
 }

@@ -9,6 +9,7 @@ mantissa bit (IEEE 754 roundTiesToEven).
 from __future__ import annotations
 
 import bisect
+from decimal import Decimal, localcontext
 from fractions import Fraction
 from functools import lru_cache
 
@@ -87,8 +88,63 @@ def exact_value(bits, t: str) -> Fraction:
     return Fraction(int(bits))
 
 
-def brute_gemm(p):
-    """Exact D of a (tiny) workload: rational sums for floats, Python ints for int8.
+@lru_cache(maxsize=None)
+def _pi60() -> Decimal:
+    """pi to 60 digits by Machin's formula, 16 atan(1/5) - 4 atan(1/239)."""
+    with localcontext() as ctx:
+        ctx.prec = 70
+        def atan_inv(n):
+            s, term, k, n2 = Decimal(0), Decimal(1) / n, 0, n * n
+            while term != 0:
+                s += term / (2 * k + 1) if k % 2 == 0 else -term / (2 * k + 1)
+                term /= n2
+                k += 1
+            return s
+        return +(16 * atan_inv(5) - 4 * atan_inv(239))
+
+
+def gelu_tanh(x: Fraction) -> Fraction:
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) to 60 significant digits, with
+    tanh from exponentials in Python's decimal module (no libm)."""
+    with localcontext() as ctx:
+        ctx.prec = 60
+        d = Decimal(x.numerator) / Decimal(x.denominator)
+        u = (2 / _pi60()).sqrt() * (d + Decimal("0.044715") * d * d * d)
+        # 0.5 (1 + tanh u) = e^(2u) / (1 + e^(2u)) = 1 / (1 + e^(-2u)); the exponent taken
+        # is never positive, so neither form overflows or cancels
+        if u < 0:
+            e = (2 * u).exp()
+            s = e / (1 + e)
+        else:
+            s = 1 / (1 + (-2 * u).exp())
+        g = Fraction(d * s)
+    if g == 0 and x < 0:
+        # e^(2u) underflowed: the value is negative and below any fp32 subnormal
+        return Fraction(-1, 10 ** 400)
+    return g
+
+
+def apply_epilogue(v: Fraction, ep, b: int, i: int, j: int, addend: Fraction) -> Fraction:
+    """rs(i) * cs(j) * v + bias(j) + addend, then the activation (exact rationals)."""
+    if ep is not None:
+        if ep.row_scale is not None:
+            v *= Fraction(float(ep.row_scale[b * ep.stride_rs + i]))
+        if ep.col_scale is not None:
+            v *= Fraction(float(ep.col_scale[b * ep.stride_cs + j]))
+        if ep.bias is not None:
+            v += Fraction(float(ep.bias[b * ep.stride_bias + j]))
+    v += addend
+    act = "none" if ep is None else ep.act
+    if act == "relu":
+        v = v if v > 0 else Fraction(0)
+    elif act == "gelu_tanh":
+        v = gelu_tanh(v)
+    return v
+
+
+def brute_gemm(p, ep=None):
+    """Exact D of a (tiny) workload: rational sums for floats, Python ints for int8,
+    followed by the epilogue ``ep`` (a workloads.Epilogue, or None).
 
     Reads operands element by element from the raw storage with the BLAS-convention
     addressing, independently of the oracle's loops.
@@ -101,21 +157,27 @@ def brute_gemm(p):
         off = b * p.stride_b + (k * p.ldb + j if p.layout_b == "row" else k + j * p.ldb)
         return exact_value(p.B[off], p.in_type)
 
-    c_t = "i32" if p.in_type == "i8" else p.out_type
+    def wrap32(v):
+        v = int(v) & 0xFFFFFFFF
+        return v - (1 << 32) if v >= (1 << 31) else v
+
+    c_t = p.out_type
     out = np.zeros(p.batch * p.stride_d, dtype={"f32": np.float32, "f16": np.uint16,
                                                 "bf16": np.uint16, "i32": np.int32}[p.out_type])
     for b in range(p.batch):
         for i in range(p.M):
             for j in range(p.N):
                 s = sum((a_at(b, i, k) * b_at(b, k, j) for k in range(p.K)), Fraction(0))
-                if p.C is not None:
-                    s += exact_value(p.C[b * p.stride_c + i * p.ldc + j], c_t)
+                c = exact_value(p.C[b * p.stride_c + i * p.ldc + j], c_t) if p.C is not None else 0
                 o = b * p.stride_d + i * p.ldd + j
                 if p.out_type == "i32":
-                    v = int(s) & 0xFFFFFFFF
-                    out[o] = v - (1 << 32) if v >= (1 << 31) else v
-                elif p.out_type == "f32":
-                    out[o] = round32(s)
+                    out[o] = wrap32(s + c)
+                    continue
+                if p.in_type == "i8":
+                    s = Fraction(wrap32(s))  # the int32 accumulator
+                v = apply_epilogue(s, ep, b, i, j, Fraction(c))
+                if p.out_type == "f32":
+                    out[o] = round32(v)
                 else:
-                    out[o] = round16(s, p.out_type)
+                    out[o] = round16(v, p.out_type)
     return out

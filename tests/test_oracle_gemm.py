@@ -175,9 +175,15 @@ def test_empty_and_k_zero():
 
 
 def test_rejects_bad_arguments():
+    with pytest.raises(ValueError):  # integer output takes no epilogue
+        oracle.gemm(2, 2, 2, np.zeros(4, np.int8), 2, np.zeros(4, np.int8), 2,
+                    in_type="i8", out_type="i32", act="relu")
     with pytest.raises(ValueError):
         oracle.gemm(2, 2, 2, np.zeros(4, np.int8), 2, np.zeros(4, np.int8), 2,
-                    in_type="i8", out_type="f32")
+                    in_type="i8", out_type="i32", bias=np.zeros(2, np.float32))
+    with pytest.raises(ValueError):  # fp16 inputs cannot give int32 output
+        oracle.gemm(2, 2, 2, np.zeros(4, np.uint16), 2, np.zeros(4, np.uint16), 2,
+                    in_type="f16", out_type="i32")
     with pytest.raises(ValueError):  # buffer too small for the stated shape
         oracle.gemm(4, 4, 4, np.zeros(8, np.uint16), 4, np.zeros(16, np.uint16), 4,
                     in_type="f16", out_type="f32")

@@ -3,7 +3,8 @@
 Each case below plants one mistake in a copy of ``oracle/oracle.c`` (a dropped
 term, a wrong sign, index or stride, a transposed operand, a wrong rounding
 rule, a wrong codec constant), builds that copy into a temporary library, and
-runs the oracle pin suite (tests/test_oracle_gemm.py, tests/test_oracle_codecs.py)
+runs the oracle pin suite (tests/test_oracle_gemm.py, tests/test_oracle_codecs.py,
+tests/test_oracle_epilogue.py)
 against it in a child process.  The suite must fail for every mutant; a mutant
 that survives is a mistake the pins would not see.
 """
@@ -28,11 +29,13 @@ MUTANTS = [
     ("selected elements: A transposed", "load_fp(A, in_type, oa + at(layout_a, i, k, lda))",
      "load_fp(A, in_type, oa + at(layout_a, k, i, lda))"),
     ("selected elements: batch stride of B ignored", "ob = b * stride_b,", "ob = 0 * stride_b,"),
-    ("selected elements: C dropped", "acc += load_fp(C, out_type", "acc += 0.0 * load_fp(C, out_type"),
+    ("selected elements: C dropped", "addend += load_fp(C, out_type", "addend += 0.0 * load_fp(C, out_type"),
+    ("selected elements: epilogue skipped", "store_out(out, out_type, s, epilogue(&j, b, i, c, acc, addend));",
+     "store_out(out, out_type, s, acc + addend);"),
     ("selected elements: int k dropped", "for (int64_t k = 0; k < K; ++k)\n                acc += load_int",
      "for (int64_t k = 1; k < K; ++k)\n                acc += load_int"),
     ("column-major ignored", "r * ld + c : r + c * ld", "r * ld + c : r * ld + c"),
-    ("C dropped", "v += load_fp(j->C", "v += 0.0 * load_fp(j->C"),
+    ("C dropped", "epilogue(j, b, i, c, accf[c], addend)", "epilogue(j, b, i, c, accf[c], 0.0)"),
     ("int C subtracted", "v += load_int(j->C", "v -= load_int(j->C"),
     ("last k dropped", "for (int64_t k = 0; k < j->K; ++k) {\n                const double",
      "for (int64_t k = 0; k + 1 < j->K; ++k) {\n                const double"),
@@ -41,8 +44,8 @@ MUTANTS = [
     ("product sign", "accf[c] += a * load_fp", "accf[c] -= a * load_fp"),
     ("fp32 accumulator", "accf[c] += a * load_fp(j->B, j->in_type, ob + at(j->layout_b, k, c, j->ldb));",
      "accf[c] = (float)(accf[c] + a * load_fp(j->B, j->in_type, ob + at(j->layout_b, k, c, j->ldb)));"),
-    ("fp32 intermediate before 16-bit output", "store_out(j->D, j->out_type, od + i * j->ldd + c, v);",
-     "store_out(j->D, j->out_type, od + i * j->ldd + c, (double)(float)v);"),
+    ("fp32 intermediate before 16-bit output", "od + i * j->ldd + c, epilogue(j, b, i, c, accf[c], addend));",
+     "od + i * j->ldd + c, (double)(float)epilogue(j, b, i, c, accf[c], addend));"),
     ("ties away from zero", "(frac == 0.5 && fmod(r, 2.0) != 0.0)", "(frac == 0.5)"),
     ("truncation", "if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))", "if (0)"),
     ("subnormal outputs flushed", "return sign_bit | n;", "return sign_bit;"),
@@ -54,9 +57,23 @@ MUTANTS = [
     ("batch stride of A ignored", "const int64_t oa = b * j->stride_a", "const int64_t oa = 0 * j->stride_a"),
     ("batch stride of B ignored", "ob = b * j->stride_b;", "ob = 0 * j->stride_b;"),
     ("batch stride of C ignored", "const int64_t oc = b * j->stride_c", "const int64_t oc = 0 * j->stride_c"),
-    ("ldc taken as N", "v += load_fp(j->C, j->out_type, oc + i * j->ldc + c);",
-     "v += load_fp(j->C, j->out_type, oc + i * j->N + c);"),
+    ("ldc taken as N", "oc + i * j->ldc + c) : 0.0;\n                store_out(j->D, j->out_type, od + i * j->ldd + c, epilogue(j, b, i, c, accf[c]",
+     "oc + i * j->N + c) : 0.0;\n                store_out(j->D, j->out_type, od + i * j->ldd + c, epilogue(j, b, i, c, accf[c]"),
     ("int8 read unsigned", "(int64_t)((const int8_t *)p)[idx]", "(int64_t)((const uint8_t *)p)[idx]"),
+    ("row scale indexed by column", "v *= (double)j->rs[b * j->stride_rs + i];",
+     "v *= (double)j->rs[b * j->stride_rs + c];"),
+    ("column scale indexed by row", "v *= (double)j->cs[b * j->stride_cs + c];",
+     "v *= (double)j->cs[b * j->stride_cs + i];"),
+    ("bias indexed by row", "v += (double)j->bias[b * j->stride_bias + c];",
+     "v += (double)j->bias[b * j->stride_bias + i];"),
+    ("batch stride of the column scale ignored", "j->cs[b * j->stride_cs + c]", "j->cs[0 * j->stride_cs + c]"),
+    ("bias subtracted", "v += (double)j->bias[", "v -= (double)j->bias["),
+    ("ReLU keeps negatives", "v = v > 0.0 ? v : 0.0;", "v = v > 0.0 ? v : 0.1 * v;"),
+    ("GELU cubic coefficient", "(v + 0.044715 * v * v * v)", "(v + 0.0447 * v * v * v)"),
+    ("GELU without the sqrt(2/pi) factor", "sqrt(2.0 / acos(-1.0)) * (v", "(v"),
+    ("GELU logistic of u instead of 2u", "v = v / (1.0 + exp(-2.0 * u));", "v = v / (1.0 + exp(-u));"),
+    ("dequantisation without wrap-around", "epilogue(j, b, i, c, (double)wrap_i32(acci[c]), addend)",
+     "epilogue(j, b, i, c, (double)acci[c], addend)"),
     ("int32 saturates", "static int32_t wrap_i32(int64_t v) { return (int32_t)(uint32_t)(uint64_t)v; }",
      "static int32_t wrap_i32(int64_t v) { return v > INT32_MAX ? INT32_MAX : "
      "(v < INT32_MIN ? INT32_MIN : (int32_t)v); }"),
@@ -66,7 +83,8 @@ RUNNER = (
     "import sys, pytest, oracle\n"
     "oracle.LIB_PATH = sys.argv[1]\n"
     "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '--no-header',\n"
-    "                      'tests/test_oracle_gemm.py', 'tests/test_oracle_codecs.py']))\n"
+    "                      'tests/test_oracle_gemm.py', 'tests/test_oracle_codecs.py',\n"
+    "                      'tests/test_oracle_epilogue.py']))\n"
 )
 
 

@@ -208,7 +208,7 @@ def make(cfg: str, kind: str = "random", seed: int = 0, *, M=None, N=None, K=Non
         p.ldc, p.stride_c = ldd, (M * ldd if batch > 1 else 0)
     if with_c:
         rc = _rng(cfg, 2, seed)
-        c_t = "i32" if in_t == "i8" else out_t
+        c_t = out_t
         if c_t == "i32":
             cv = rc.integers(-1000, 1000, batch * M * ldd)
         else:
@@ -222,3 +222,69 @@ def make(cfg: str, kind: str = "random", seed: int = 0, *, M=None, N=None, K=Non
 
 def shrink(p: Problem, **kw) -> Problem:
     return replace(p, **kw)
+
+
+def with_output(p: Problem, out_t: str, seed: int = 0) -> Problem:
+    """The same inputs with another output type (int8 -> fp32/fp16/bf16 dequantisation,
+    or the other float output of a float problem); a C operand is redrawn in that type."""
+    q = replace(p, out_type=out_t, meta=dict(p.meta, out=out_t))
+    if p.C is not None:
+        rc = _rng(p.meta.get("cfg", p.name), 3, seed)
+        n = p.batch * p.M * p.ldc if p.batch > 1 else p.M * p.ldc
+        cv = rc.uniform(-1, 1, n)
+        if p.meta.get("kind") == "structured":
+            cv = np.round(cv * 8)
+        q.C = to_bits(cv, out_t) if out_t != "i32" else rc.integers(-1000, 1000, n).astype(np.int32)
+    return q
+
+
+@dataclass
+class Epilogue:
+    """Operands of the fused epilogue: per-row and per-column scales and a per-column
+    bias (float32, one vector per batch slice at the given stride), and an activation."""
+
+    row_scale: Optional[np.ndarray]
+    stride_rs: int
+    col_scale: Optional[np.ndarray]
+    stride_cs: int
+    bias: Optional[np.ndarray]
+    stride_bias: int
+    act: str
+
+    def kwargs(self) -> dict:
+        return dict(row_scale=self.row_scale, stride_rs=self.stride_rs, col_scale=self.col_scale,
+                    stride_cs=self.stride_cs, bias=self.bias, stride_bias=self.stride_bias,
+                    act=self.act)
+
+
+def make_epilogue(p: Problem, seed: int = 0, act: str = "none", row: bool = True, col: bool = True,
+                  bias: bool = True, exact: bool = False) -> Epilogue:
+    """Seeded epilogue operands for problem p.
+
+    exact=True draws powers of two for the scales and small integers for the bias, so
+    that with integer-valued products every epilogue step is exact in fp32.  Otherwise
+    the scales are the per-row / per-column dequantisation factors of an int8 problem
+    (about 1/127 of a unit range) or O(1) factors for float problems, and the bias is
+    O(1).  Batched problems get a padded stride per vector (M + 3, N + 5).
+    """
+    rng = np.random.default_rng([77, seed, p.M, p.N, p.batch])
+    sr = p.M + 3 if p.batch > 1 else 0
+    sc = p.N + 5 if p.batch > 1 else 0
+    nr = (p.batch - 1) * sr + p.M if p.batch else 0
+    nc = (p.batch - 1) * sc + p.N if p.batch else 0
+
+    def scales(n):
+        if exact:
+            return (2.0 ** rng.integers(-3, 4, n)).astype(np.float32)
+        if p.in_type == "i8":
+            return rng.uniform(0.5 / 127, 2.0 / 127, n).astype(np.float32)
+        return rng.uniform(0.5, 2.0, n).astype(np.float32)
+
+    rs = scales(nr) if row else None
+    cs = scales(nc) if col else None
+    if bias:
+        bv = rng.integers(-8, 9, nc) if exact else rng.uniform(-1, 1, nc)
+        bv = bv.astype(np.float32)
+    else:
+        bv = None
+    return Epilogue(rs, sr, cs, sc, bv, sc, act)
