@@ -4,9 +4,9 @@
 ``bench.py`` wrote under DIR and writes short text summaries into ``profiles/``:
 
   kernel trace   rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run
-                     -- python3 bench.py --workload W --steps 50 --warmup 10 --no-cpu-baseline
+                     -- python3 bench.py --workload W --steps 200 --warmup 1000 --no-cpu-baseline
   HBM traffic    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run
-                     -- python3 bench.py --workload W --steps 5 --warmup 2 --no-cpu-baseline
+                     -- python3 bench.py --workload W --steps 100 --warmup 1000 --no-cpu-baseline
                         --copy-calibration 256
                  (the same with WRITE_SIZE into DIR/write)
   matrix cores   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_LDS_BANK_CONFLICT
@@ -16,6 +16,11 @@
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
 counter reads for a plain device-to-device copy of 256 MiB (the
 ``--copy-calibration`` leg): factor = copied bytes / counter bytes.
+
+The GPU raises its shader clock only after a few hundred back-to-back
+launches, so the figures that depend on time or clock (the kernel's average
+duration, the matrix-core busy fraction) are taken over the last dispatches
+of each run -- the ones the benchmark times -- not over the warm-up.
 """
 from __future__ import annotations
 
@@ -36,12 +41,26 @@ def _rows(pattern: str):
     return out
 
 
-def _counter_means(rows):
-    """{(kernel name, counter): mean value per dispatch}"""
+def _counter_means(rows, last: int = 0):
+    """{(kernel name, counter): mean value per dispatch} (over the last `last` dispatches if > 0)"""
     acc = defaultdict(list)
     for r in rows:
-        acc[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+        acc[(r["Kernel_Name"], r["Counter_Name"])].append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    out = {}
+    for k, v in acc.items():
+        vals = [x for _, x in sorted(v)]
+        if last:
+            vals = vals[-last:]
+        out[k] = sum(vals) / len(vals)
+    return out
+
+
+def _timed_average_us(rows, timed: int):
+    """Average duration (us) of the last `timed` GEMM dispatches of a per-dispatch kernel trace."""
+    d = sorted((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+               for r in rows if is_gemm(r["Kernel_Name"]))
+    d = [x for _, x in d][-timed:]
+    return (sum(d) / len(d), len(d)) if d else (None, 0)
 
 
 def _pick(means, counter, pred):
@@ -58,7 +77,7 @@ def is_copy(name: str) -> bool:
 
 
 def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, source_digest: str,
-              commands: dict) -> dict:
+              commands: dict, timed: int = 200, counted: int = 100) -> dict:
     """Write profiles/<label>_<workload>_*.md and traffic_<workload>.json; return the figures."""
     os.makedirs(profiles, exist_ok=True)
     result = {"workload": workload_name, "kernel": kernel_label, "source_digest": source_digest}
@@ -79,13 +98,18 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['Percentage']):.1f}% |")
             if is_gemm(r["Name"]):
-                result["avg_us"] = float(r["AverageNs"]) / 1e3
+                result["avg_us_all_dispatches"] = float(r["AverageNs"]) / 1e3
+        avg, n = _timed_average_us(_rows(os.path.join(d, "trace", "**", "*kernel_trace.csv")), timed)
+        if avg is not None:
+            result["avg_us"] = avg
+            lines += ["", f"GEMM dispatches timed by the benchmark (the last {n}, after the warm-up that "
+                          f"raises the clock): average {avg:.2f} us."]
         open(os.path.join(profiles, f"{kernel_label}_{workload_name}_kernel_trace.md"), "w").write(
             "\n".join(lines) + "\n")
 
     # HBM traffic, calibrated with the plain copy
-    fetch = _counter_means(_rows(os.path.join(d, "fetch", "**", "*counter_collection.csv")))
-    write = _counter_means(_rows(os.path.join(d, "write", "**", "*counter_collection.csv")))
+    fetch = _counter_means(_rows(os.path.join(d, "fetch", "**", "*counter_collection.csv")), counted)
+    write = _counter_means(_rows(os.path.join(d, "write", "**", "*counter_collection.csv")), counted)
     if fetch and write:
         copy_bytes = COPY_MIB * (1 << 20)
         f_copy = _pick(fetch, "FETCH_SIZE", is_copy)
@@ -116,7 +140,7 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
         open(os.path.join(profiles, f"traffic_{workload_name}.md"), "w").write("\n".join(md) + "\n")
 
     # matrix-core and LDS counters
-    sq = _counter_means(_rows(os.path.join(d, "sq", "**", "*counter_collection.csv")))
+    sq = _counter_means(_rows(os.path.join(d, "sq", "**", "*counter_collection.csv")), counted)
     if sq:
         get = lambda c: _pick(sq, c, is_gemm)
         busy = get("SQ_VALU_MFMA_BUSY_CYCLES")
