@@ -6,23 +6,24 @@
 // warp tile of the "hgemm_mma_m16n8k16_mma2x4_warp4x4_kernel" walkthrough
 // (sections 2-3) and of section 4.2 of "Tensor Cores, CUTLASS and CuTe".
 //
-// MFMA fragment ownership on gfx950 (64 lanes, l = lane id), as pinned by the
-// single-wavefront probes (the gfx950 counterpart of the layout experiment,
-// KingOfEgg sections 4-7):
-//   v_mfma_f32_32x32x16_{bf16,f16}: operand X (A or B^T) lane l holds
-//       X[row = l % 32][k = 8 * (l / 32) + s], s = 0..7  (16 contiguous bytes)
-//     accumulator register r of lane l holds
-//       D[row = 8 * (r / 4) + 4 * (l / 32) + r % 4][col = l % 32]
-//   v_mfma_i32_32x32x32_i8: the same with 16 int8 per lane, k = 16*(l/32)+s.
-// Both operands are "row of X with contiguous k", so the kernels keep every
-// tile K-contiguous in LDS, one 128-byte row per M (or N) index per K-tile
-// (64 fp16/bf16 or 128 int8 values), and read one 16-byte fragment per lane
-// with ds_read_b128.
+// The kernels run on the 16 x 16 matrix instructions.  Fragment ownership on
+// gfx950 (64 lanes, l = lane id), as pinned by the single-wavefront probes (the
+// gfx950 counterpart of the layout experiment, KingOfEgg sections 4-7):
+//   v_mfma_f32_16x16x32_{bf16,f16}: operand X (A or B^T) lane l holds
+//       X[row = l % 16][k = 8 (l / 16) + s], s = 0..7  (16 contiguous bytes)
+//     accumulator register r of lane l holds D[row = 4 (l / 16) + r][col = l % 16]
+//   v_mfma_i32_16x16x64_i8: the same with 16 int8 per lane, k = 16 (l / 16) + s.
+// Both operands are "row of X with contiguous k", so the kernels keep operand
+// tiles in LDS as rows of 128 bytes (one K-tile: 64 fp16/bf16 or 128 int8
+// values, two K-steps) and read one 16-byte fragment per lane.  The 32 x 32
+// instructions (also pinned by the probes) draw markedly more power per
+// operation: under a sustained load the chip holds a clock about a fifth lower
+// for them, which is why the kernels do not use them.
 //
 // The kernels issue MFMA(srcA = B-fragment, srcB = A-fragment), i.e. they
-// compute D^T tile by tile.  Lane l then owns, for each group g = r / 4, four
-// consecutive columns n = 8g + 4(l/32) + 0..3 of row m = l % 32, so the
-// epilogue writes 4 contiguous output elements per register group.
+// compute D^T tile by tile: lane l then owns row m = l % 16 and the four
+// consecutive columns n = 4 (l / 16) + 0..3 of each 16 x 16 tile, so the
+// epilogue writes 4 contiguous output elements per tile.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,62 +53,70 @@ enum Mode {
 __host__ __device__ constexpr int dt_bytes(int t) { return (t == F32 || t == I32) ? 4 : (t == I8 ? 1 : 2); }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout.  A tile of R rows (M or N indices) x 128 bytes (one K-tile)
-// is stored row after row; the eight 16-byte chunks of a row are permuted by
-// an XOR swizzle so that both the fragment reads (32 consecutive rows, same
-// chunk) and the transposing writes (rows 8 apart, same chunk) spread over all
-// eight chunk positions.  This plays the role of the chunk XOR swizzle of
-// "Tensor Cores, CUTLASS and CuTe" section 3.5, re-derived for 128-byte rows
-// and for the two access patterns used here.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t swz_chunk(uint32_t row, uint32_t chunk)
-{
-    return chunk ^ ((row ^ (row >> 3)) & 7u);
-}
-
-__device__ __forceinline__ uint32_t lds_off(uint32_t row, uint32_t byte_in_row)
-{
-    return row * 128u + (swz_chunk(row, byte_in_row >> 4) << 4) + (byte_in_row & 15u);
-}
-
-// ---------------------------------------------------------------------------
-// MFMA wrappers: one 32 x 32 x (16 fp16/bf16 | 32 int8) step, 16-byte operands.
+// MFMA wrappers: one 16 x 16 x (32 fp16/bf16 | 64 int8) step, 16-byte operands.
 // ---------------------------------------------------------------------------
 template <int T> struct Mfma;
 
 template <> struct Mfma<BF16> {
-    typedef f32x16 acc_t;
+    typedef f32x4 acc_t;
     static __device__ __forceinline__ acc_t step(u32x4 x, u32x4 y, acc_t c)
     {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x),
-                                                       __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y),
+                                                       c, 0, 0, 0);
     }
 };
 template <> struct Mfma<F16> {
-    typedef f32x16 acc_t;
+    typedef f32x4 acc_t;
     static __device__ __forceinline__ acc_t step(u32x4 x, u32x4 y, acc_t c)
     {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x),
-                                                      __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
+                                                      0, 0, 0);
     }
 };
 template <> struct Mfma<I8> {
-    typedef i32x16 acc_t;
+    typedef i32x4 acc_t;
     static __device__ __forceinline__ acc_t step(u32x4 x, u32x4 y, acc_t c)
     {
-        return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, x),
-                                                     __builtin_bit_cast(i32x4, y), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, x), __builtin_bit_cast(i32x4, y), c, 0,
+                                                     0, 0);
     }
 };
 
-// Fragment of X rows [row0, row0+32) for K-step ks (0..3) of the K-tile held
-// in the LDS tile at `tile`: lane l reads row row0 + l%32, bytes
-// 32*ks + 16*(l/32) .. +15 of that row.
-__device__ __forceinline__ u32x4 frag_read(const char *tile, uint32_t row0, uint32_t ks, uint32_t lane)
+// ---------------------------------------------------------------------------
+// Buffer loads.  A buffer descriptor (base, size in bytes) lets every
+// out-of-range vector read as zeros with no branch: the range check covers the
+// lane offset plus the instruction's scalar offset.
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Lane offset that the range check always rejects (slices are < 2^31 bytes).
+constexpr uint32_t OOB = 0x80000000u;
+
+// `base` and `bytes` must be the same in every lane: they are taken from the
+// first active lane, so that the descriptor lives in scalar registers even where
+// the compiler cannot prove that on its own (it would otherwise wrap every load
+// in a loop over the distinct descriptors of the wavefront).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
-    const uint32_t row = row0 + (lane & 31u);
-    return *reinterpret_cast<const u32x4 *>(tile + lds_off(row, ks * 32u + ((lane >> 5) << 4)));
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    base = (const void *)(((uint64_t)hi << 32) | lo);
+    bytes = __builtin_amdgcn_readfirstlane(bytes);
+    // word 3 = 0x00020000: raw (untyped) 32-bit data format, the gfx9-family setting
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// 16 bytes at base + voff + soff (voff per lane, soff uniform).
+__device__ __forceinline__ u32x4 load16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// End of a K-tile: this wavefront's LDS accesses have completed, then all
+// wavefronts meet.  One asm statement with a memory clobber, so that no memory
+// access is moved across the barrier.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // Output conversion (round to nearest even, subnormals kept).
@@ -184,48 +193,6 @@ __device__ __forceinline__ TileCoord tile_of(const GemmParams &p, uint32_t wg)
     c.tm = (int32_t)(first_m + u % rows);
     c.tn = (int32_t)(u / rows);
     return c;
-}
-
-// ---------------------------------------------------------------------------
-// Epilogue for one 32 x 32 MFMA tile computed as D^T (see the header comment):
-// lane l owns row m = m0 + l%32 and columns n0 + 8g + 4(l/32) + 0..3, g = 0..3,
-// with values acc[4g .. 4g+3].  D = convert(acc + C), masked at the M/N edges.
-// ---------------------------------------------------------------------------
-template <int O, class AccV>
-__device__ __forceinline__ void store_tile(const GemmParams &p, const AccV &acc, int64_t m, int64_t n0,
-                                           uint32_t lane, const char *Cb, char *Db)
-{
-    typedef typename Out<O>::t ot;
-    if (m >= p.M)
-        return;
-    const ot *Crow = Cb ? reinterpret_cast<const ot *>(Cb) + m * p.ldc : nullptr;
-    ot *Drow = reinterpret_cast<ot *>(Db) + m * p.ldd;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + 8 * g + 4 * (lane >> 5);
-        if (p.d_vec4 && n + 3 < p.N) {
-            typedef ot ov4 __attribute__((ext_vector_type(4)));
-            ov4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                auto a = acc[4 * g + e];
-                if (Crow)
-                    a += Out<O>::to_acc(Crow[n + e]);
-                v[e] = Out<O>::from_acc(a);
-            }
-            *reinterpret_cast<ov4 *>(Drow + n) = v;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (n + e < p.N) {
-                    auto a = acc[4 * g + e];
-                    if (Crow)
-                        a += Out<O>::to_acc(Crow[n + e]);
-                    Drow[n + e] = Out<O>::from_acc(a);
-                }
-            }
-        }
-    }
 }
 
 } // namespace dmu

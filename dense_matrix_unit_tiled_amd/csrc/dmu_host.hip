@@ -74,7 +74,7 @@ struct NameTable {
 const NameTable &kernel_names()
 {
     static const NameTable table = [] {
-        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64", "256x256w4"};
+        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64"};
         static const char *const MODE_NAMES[] = {"k16", "kd", "t16"};
         NameTable t;
         for (int a = 0; a < NUM_TILE_CFGS; ++a)
@@ -237,7 +237,6 @@ int validate(const dmu_gemm_args *a, Plan *plan)
         else
             tile = TILE_128x128;
         if (env && strcmp(env, "256x256") == 0) tile = TILE_256x256;
-        if (env && strcmp(env, "256x256w4") == 0) tile = TILE_256x256_W4;
         if (env && strcmp(env, "256x128") == 0) tile = TILE_256x128;
         if (env && strcmp(env, "128x128") == 0) tile = TILE_128x128;
     }

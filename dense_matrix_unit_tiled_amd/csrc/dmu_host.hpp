@@ -14,14 +14,14 @@ void clear_error();
 // DMU_OK, or DMU_ERR_HIP with the runtime's message when the last launch failed.
 int check_launch(const char *what);
 
-// Kernel shapes of the tiled kernel (gemm_tiled) and the fallback (gemm_generic).
+// Kernel shapes of the tiled kernel (gemm_tiled, 8 wavefronts) and the
+// fallback (gemm_generic).
 enum TileCfg {
-    TILE_256x256 = 0,    // 8 wavefronts 2 x 4, 128 x 64 each (two per SIMD)
-    TILE_256x128 = 1,    // 4 wavefronts 2 x 2, 128 x 64 each
-    TILE_128x128 = 2,    // 4 wavefronts 2 x 2, 64 x 64 each
-    TILE_GENERIC = 3,    // 64 x 64, element loads
-    TILE_256x256_W4 = 4, // 4 wavefronts 2 x 2, 128 x 128 each (one per SIMD)
-    NUM_TILE_CFGS = 5
+    TILE_256x256 = 0, // wavefronts 2 x 4, 128 x 64 each
+    TILE_256x128 = 1, // wavefronts 4 x 2, 64 x 64 each
+    TILE_128x128 = 2, // wavefronts 2 x 4, 64 x 32 each
+    TILE_GENERIC = 3, // 64 x 64, element loads
+    NUM_TILE_CFGS = 4
 };
 
 struct LaunchCfg {
@@ -31,13 +31,10 @@ struct LaunchCfg {
 };
 
 inline int tile_bm(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_128x128 ? 128 : 256); }
-inline int tile_bn(int tile)
-{
-    return tile == TILE_GENERIC ? 64 : ((tile == TILE_256x256 || tile == TILE_256x256_W4) ? 256 : 128);
-}
+inline int tile_bn(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_256x256 ? 256 : 128); }
 
 // One launcher per (input type, output type); each returns hipSuccess or the
-// launch error.  The grid is p.total_tiles workgroups of 256 threads.
+// launch error.  The grid is p.total_tiles workgroups.
 hipError_t launch_f16_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 hipError_t launch_f16_f16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 hipError_t launch_bf16_bf16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);

@@ -5,8 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/dmu.h"
-#include "dmu_device.hpp"
 #include "dmu_host.hpp"
+#include "dmu_tiled.hpp"
 
 namespace dmu {
 
@@ -99,23 +99,57 @@ __global__ void __launch_bounds__(64) probe_lds_tr16(const char *img, const int3
     out[l * 2 + 1] = w[1];
 }
 
-// The GEMM kernels' LDS tile format: a 32-row x 128-byte tile is written with
-// their swizzled addressing and read back with their fragment reads.
+// The tiled kernel's K-contiguous LDS format: a 32-row x 128-byte tile is
+// written with the kernel's staging writes (transfer q, lane l -> LDS bytes
+// 1024 q + 16 l, carrying row 8q + l/8, logical chunk (l%8) ^ (l/8)) and read
+// back with its fragment reads for row blocks 0 and 16, K-steps 0 and 1.
+// Output per lane: [row block][K-step][16 bytes].
 __global__ void __launch_bounds__(64) probe_lds_frag(const char *tile, uint32_t *out)
 {
-    __shared__ __attribute__((aligned(16))) char lds[32 * 128];
+    typedef KcTile<32, 1, false> Tile;
+    __shared__ __attribute__((aligned(1024))) char lds[Tile::BYTES];
     const uint32_t l = threadIdx.x;
-    for (int q = 0; q < 4; ++q) { // 256 chunks of 16 bytes
-        const uint32_t idx = l + 64u * q, row = idx / 8u, cb = (idx % 8u) * 16u;
-        *reinterpret_cast<u32x4 *>(lds + lds_off(row, cb)) =
-            *reinterpret_cast<const u32x4 *>(tile + row * 128u + cb);
+    for (int q = 0; q < Tile::NL; ++q) {
+        const uint32_t row = 8 * q + l / 8, chunk = (l % 8) ^ (l / 8);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + row * 128u + chunk * 16u);
+        Tile t;
+        t.init(128, 0, l);
+        t.store(q, lds, 0, l, v);
     }
     __syncthreads();
-    for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 v = frag_read(lds, 0, ks, l);
-        for (int e = 0; e < 4; ++e)
-            out[(l * 4 + ks) * 4 + e] = v[e];
+    for (int rb = 0; rb < 2; ++rb)
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 v = Tile::frag(lds, 16 * rb, ks, l);
+            for (int e = 0; e < 4; ++e)
+                out[((l * 2 + rb) * 2 + ks) * 4 + e] = v[e];
+        }
+}
+
+// The tiled kernel's M/N-contiguous 16-bit LDS format: a 64 K-row x 128-value
+// tile (row-major, 256 bytes per K-row) is written with the kernel's staging
+// writes of all eight wavefronts' transfers and read back with its transposing
+// fragment reads for column blocks 0, 16, .., 112 and K-steps 0 and 1.
+// Output per lane: [column block][K-step][8 16-bit values].
+__global__ void __launch_bounds__(64) probe_lds_frag_t(const char *tile, uint32_t *out)
+{
+    typedef McTile<128, 8> Tile;
+    __shared__ __attribute__((aligned(1024))) char lds[Tile::BYTES];
+    const uint32_t l = threadIdx.x;
+    for (uint32_t w = 0; w < 8; ++w) {
+        Tile t;
+        t.init(256, 128, w, l);
+        for (int i = 0; i < Tile::NL; ++i) {
+            const uint32_t k = (w * Tile::NL + i) * Tile::RPI + l / Tile::CPR, chunk = l % Tile::CPR;
+            t.store(i, lds, w, l, *reinterpret_cast<const u32x4 *>(tile + k * 256u + chunk * 16u));
+        }
     }
+    __syncthreads();
+    for (int cb = 0; cb < 8; ++cb)
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 v = Tile::frag(lds, 16 * cb, ks, l);
+            for (int e = 0; e < 4; ++e)
+                out[((l * 8 + cb) * 2 + ks) * 4 + e] = v[e];
+        }
 }
 
 template <int O>
@@ -145,6 +179,7 @@ extern "C" int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type,
     case DMU_PROBE_LDS_READ_B128: r = 4; break;
     case DMU_PROBE_LDS_READ_TR16: r = 2; break;
     case DMU_PROBE_LDS_FRAG: r = 16; break;
+    case DMU_PROBE_LDS_FRAG_T: r = 64; break;
     case DMU_PROBE_CVT_BF16: t = DMU_F32, r = 2; break; /* 4 halves per lane */
     case DMU_PROBE_CVT_F16: t = DMU_F32, r = 2; break;
     default:
@@ -190,6 +225,7 @@ extern "C" int dmu_probe(int variant, const void *in0, const void *in1, void *ou
         hipLaunchKernelGGL(probe_lds_tr16, dim3(1), dim3(64), 0, s, a, reinterpret_cast<const int32_t *>(b), o);
         break;
     case DMU_PROBE_LDS_FRAG: hipLaunchKernelGGL(probe_lds_frag, dim3(1), dim3(64), 0, s, a, o); break;
+    case DMU_PROBE_LDS_FRAG_T: hipLaunchKernelGGL(probe_lds_frag_t, dim3(1), dim3(64), 0, s, a, o); break;
     case DMU_PROBE_CVT_BF16:
         hipLaunchKernelGGL(probe_cvt<BF16>, dim3(1), dim3(64), 0, s, reinterpret_cast<const float *>(a),
                            reinterpret_cast<uint16_t *>(o));

@@ -1,45 +1,46 @@
-// The tiled kernel (gemm_tiled) for operands whose rows are at least 4-byte
-// aligned (K-contiguous) or 16-byte aligned (M/N-contiguous).
+// The tiled kernel (gemm_tiled).
 //
-// A workgroup of 64*WGM*WGN threads (WGM x WGN wavefronts) computes a BM x BN
-// tile of D; each wavefront owns a (BM/WGM) x (BN/WGN) block of 32 x 32 MFMA
-// tiles.  K is walked in K-tiles of 128 bytes per row (64 fp16/bf16 or 128
-// int8 values), each split into 4 MFMA K-steps.  Three-level tiling
+// A workgroup of 8 wavefronts (WGM x WGN) computes a BM x BN tile of D; each
+// wavefront owns an (BM/WGM) x (BN/WGN) block of 16 x 16 MFMA tiles.  K is
+// walked in K-tiles of 128 bytes per row (64 fp16/bf16 or 128 int8 values),
+// each two K-steps of the 16 x 16 instructions.  Three-level tiling
 // (workgroup, wavefront, instruction) as in the
 // "hgemm_mma_m16n8k16_mma2x4_warp4x4_kernel" walkthrough (sections 2-6) and
 // "Tensor Cores, CUTLASS and CuTe" section 4.2, re-sized for 64-lane
-// wavefronts, 32 x 32 instructions, 160 KiB of LDS, and -- with 8 wavefronts
-// -- two wavefronts per SIMD, so that one covers the other's memory waits.
+// wavefronts, 160 KiB of LDS and two wavefronts per SIMD, so that one covers
+// the other's memory waits.
 //
 // Data path of one K-tile:
-//   global -> VGPR   buffer_load_dwordx4 through a buffer descriptor: every
-//                    out-of-range vector (rows past M/N, the K tail, the
-//                    K-tile after the last) reads as zeros without a branch.
+//   global -> VGPR   buffer_load_dwordx4 through one buffer descriptor per
+//                    operand: every out-of-range vector (rows past M/N, the K
+//                    tail, K-tiles past K) reads as zeros without a branch.
 //   VGPR -> LDS      ds_write_b128 into the other half of a double-buffered
-//                    stage ring; each load/write pair moves 1 KiB, lane l
-//                    handling bytes 16 l .. 16 l + 15 of it.
-//   LDS -> VGPR      MFMA operand fragments.  A K-contiguous operand is kept
-//                    as R rows x 128 bytes and read with one ds_read_b128 per
-//                    fragment (dmu_device.hpp).  An M/N-contiguous 16-bit
-//                    operand (row-major B, column-major A) is kept as it lies
-//                    in memory, 64 K-rows x R values, and read with two
-//                    ds_read_b64_tr_b16 per fragment: within each group of 16
-//                    lanes that instruction transposes the 16 addressed
-//                    4-value rows (pinned by the layout probe), so if lane j
-//                    of the group addresses X[k0 + j/4][n0 + 4(j%4) .. +3],
-//                    lane i receives X[k0 .. k0+3][n0 + i].  This replaces the
-//                    transposing shared-memory load of the pages (ldmatrix
-//                    .trans, layout experiment section 5; walkthrough 5.3).
-// Both LDS formats are XOR-swizzled in 16-byte chunks.  One barrier per
-// K-tile hands a stage over (the stage ring of "Tensor Cores, CUTLASS and
-// CuTe" section 4.3, two stages deep here).
+//                    stage ring (the stage ring of "Tensor Cores, CUTLASS and
+//                    CuTe" section 4.3, two stages deep here); one barrier per
+//                    K-tile hands a stage over.
+//   LDS -> VGPR      MFMA operand fragments: ds_read_b128 from a K-contiguous
+//                    tile, or two ds_read_b64_tr_b16 from an M/N-contiguous
+//                    16-bit tile (row-major B, column-major A) -- within each
+//                    group of 16 lanes that instruction transposes the 16
+//                    addressed 4-value rows (pinned by the layout probe).  This
+//                    replaces the transposing shared-memory load of the pages
+//                    (ldmatrix .trans, layout experiment section 5;
+//                    walkthrough 5.3).
 //
-// The K-tile body is an explicit issue schedule: every MFMA is followed by a
-// few of the memory instructions the wavefront owes (next K-step's fragment
-// reads; in K-steps 0-2 the LDS writes of the next K-tile, each followed by the
-// global load of the K-tile after it into the same staging registers), with
-// scheduling barriers so that the compiler keeps that order and the matrix
-// core never waits behind a burst of memory instructions.
+// A K-step's MFMAs cover the wavefront's MT x NT block of 16 x 16 tiles in two
+// halves of its tile rows, each half walked column by column, issued as
+// MFMA(srcA = B-fragment, srcB = A-fragment), i.e. D^T per tile (dmu_device.hpp).
+//
+// Register plan (the budget is 256 per lane with two wavefronts per SIMD):
+// every fragment is single-buffered and is reloaded for the next K-step right
+// after its last use in this one.  In the two-half order an A fragment's last
+// use comes half a K-step before its next first use and a B fragment's last
+// use comes a little less than half a K-step before, so every reload has a
+// dozen or more MFMAs to arrive.  The K-tile body is an explicit issue
+// schedule (scheduling barriers keep the order): after each MFMA come the
+// fragment reads it frees registers for, and a share of the staging copies
+// (the next K-tile's LDS writes, each followed by the global load of the
+// K-tile after it into the same registers).
 #pragma once
 
 #include "dmu_device.hpp"
@@ -48,68 +49,51 @@
 
 namespace dmu {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// Offset that the buffer range check always rejects (slices are < 2^31 bytes).
-constexpr uint32_t OOB = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    // word 3 = 0x00020000: raw (untyped) 32-bit data format, the gfx9-family setting
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-
-// End of a K-tile: this wavefront's LDS accesses have completed, then all
-// wavefronts meet.  One asm statement with a memory clobber, so that no memory
-// access is moved across the barrier.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Chunk swizzle of the transposed (K-row) tile: rows 0..3 of a group of four
-// use chunk pairs shifted by 0, 2, 4, 6 so that one 16-lane transposed read
-// (4 rows x 32 contiguous bytes) touches eight different chunks; rows k and
-// k + 8 additionally land in opposite 128-byte halves.
-__device__ __forceinline__ uint32_t swz_t(uint32_t k) { return ((k & 3u) << 1) ^ (((k >> 3) & 1u) << 3); }
-
 // ---------------------------------------------------------------------------
-// K-contiguous operand, R rows x 128 bytes per K-tile, NW wavefronts.
-// Transfer i of wavefront w (i < NL = R/(8 NW)) moves rows 8q .. 8q+7,
-// q = w*NL + i: lane l fetches row 8q + l/8, logical chunk (l%8) ^
-// swizzle(row), into physical chunk l%8.  Eight consecutive lanes read one
-// whole 128-byte row segment.
+// Global -> register loads.  Each operand has one buffer descriptor, from this
+// tile's first row (K-contiguous) or column (M/N-contiguous) to the end of the
+// batch slice; a load's address is that base + a per-lane offset (one register
+// per operand) + a uniform offset in the instruction's scalar offset field
+// (transfer and K-tile).  The range check covers both offsets, so rows or
+// K-rows past the matrix read as zeros, and so does a lane offset of OOB.
 // ---------------------------------------------------------------------------
-template <int R, int NW, bool MASK> struct KcStage {
-    static constexpr int NL = R / (8 * NW);
+// ---------------------------------------------------------------------------
+// K-contiguous operand (A row-major, B column-major): R rows of one K-tile
+// (128 bytes), the eight 16-byte chunks of row r permuted by XOR with r mod 8
+// (measured on gfx950: conflict-free for the 16 x 16 fragment reads, while a
+// padded pitch is not).  Row r0 + (l % 16) of a fragment has r mod 8 = l mod 8
+// for every 16-aligned r0, so each fragment address is one of two per-lane
+// bases (K-step 0 or 1) plus a constant.
+// ---------------------------------------------------------------------------
+template <int R, int NW, bool MASK> struct KcTile {
+    static constexpr int NL = R / (8 * NW); // 1 KiB transfers per wavefront
     static_assert(NL * 8 * NW == R, "whole 1 KiB transfers per wavefront");
-    uint32_t base[NL]; // byte offset at K-tile 0, or OOB
-    uint32_t cb[NL];   // byte of the chunk within a K-tile row
+    static constexpr uint32_t BYTES = R * 128;
+    uint32_t voff;  // lane offset within a transfer: row l / 8, logical chunk (l % 8) ^ (l / 8)
+    uint32_t cb;    // byte of that chunk within a K-tile row
+    uint32_t first; // byte offset of the wavefront's first row
+    uint32_t xstep; // bytes between the first rows of consecutive transfers
 
-    __device__ __forceinline__ void init(int64_t ld_bytes, int64_t rows_valid, uint32_t wave, uint32_t lane)
+    // Transfer i of wavefront w moves rows 8q .. 8q+7 (q = w NL + i) into LDS
+    // bytes 1024 q .. +1023: lane l carries row 8q + l / 8, logical chunk
+    // (l % 8) ^ (l / 8), to physical chunk l % 8.
+    __device__ __forceinline__ void init(int64_t ld_bytes, uint32_t wave, uint32_t lane)
     {
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const uint32_t q = wave * NL + i;
-            const uint32_t row = 8 * q + lane / 8;
-            const uint32_t chunk = (lane % 8) ^ ((row ^ (row >> 3)) & 7u);
-            cb[i] = chunk * 16;
-            base[i] = (int64_t)row < rows_valid ? (uint32_t)(row * ld_bytes + cb[i]) : OOB;
-        }
+        cb = ((lane & 7u) ^ (lane >> 3)) * 16;
+        voff = (lane >> 3) * (uint32_t)ld_bytes + cb;
+        first = 8 * wave * NL * (uint32_t)ld_bytes;
+        xstep = 8 * (uint32_t)ld_bytes;
     }
     // K-tile kt: bytes kt*128 .. +127 of each row (k_bytes = K * element size).
     // MASK: rows are only 4-byte aligned and K * element size need not be a
     // multiple of 16, so the vector that straddles the end of a row also holds
-    // bytes of the next row; they are cleared here (the range check of the
-    // buffer descriptor already zeroes whatever lies past the slice).
-    __device__ __forceinline__ u32x4 load(int i, __amdgpu_buffer_rsrc_t r, int kt, uint32_t k_bytes, uint32_t) const
+    // bytes of the next row; they are cleared here.
+    __device__ __forceinline__ u32x4 load(int i, __amdgpu_buffer_rsrc_t r, int kt, uint32_t k_bytes) const
     {
         const uint32_t kb0 = (uint32_t)kt * 128u;
-        u32x4 x = load16(r, (base[i] != OOB && kb0 + cb[i] < k_bytes) ? base[i] + kb0 : OOB);
+        u32x4 x = load16s(r, kb0 + cb < k_bytes ? voff : OOB, first + (uint32_t)i * xstep + kb0);
         if constexpr (MASK) {
-            const int32_t rem = (int32_t)k_bytes - (int32_t)(kb0 + cb[i]); // bytes of the vector inside the row
+            const int32_t rem = (int32_t)k_bytes - (int32_t)(kb0 + cb);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const int32_t vb = rem - 4 * d;
@@ -118,55 +102,83 @@ template <int R, int NW, bool MASK> struct KcStage {
         }
         return x;
     }
-    static __device__ __forceinline__ u32x4 frag(const char *tile, uint32_t row0, uint32_t ks, uint32_t lane)
+    __device__ __forceinline__ void store(int i, char *tile, uint32_t wave, uint32_t lane, u32x4 v) const
     {
-        return frag_read(tile, row0, ks, lane);
+        *reinterpret_cast<u32x4 *>(tile + (wave * NL + i) * 1024 + lane * 16) = v;
+    }
+    // Rows [r0, r0 + 16) (r0 a multiple of 16), K-step ks (0, 1): lane l reads
+    // row r0 + l % 16, logical bytes 64 ks + 16 (l / 16) .. +15 of the K-tile.
+    static __device__ __forceinline__ u32x4 frag(const char *tile, uint32_t r0, uint32_t ks, uint32_t lane)
+    {
+        const uint32_t chunk = (4 * ks + (lane >> 4)) ^ (lane & 7u);
+        return *reinterpret_cast<const u32x4 *>(tile + (r0 + (lane & 15u)) * 128 + chunk * 16);
     }
 };
 
 // ---------------------------------------------------------------------------
-// M/N-contiguous 16-bit operand: 64 K-rows x R values (2R bytes per row).
-// Transfer i of wavefront w moves rows q*RPI .. +RPI-1 (q = w*NL + i, RPI =
-// 512/R rows of 2R bytes); lane l fetches row q*RPI + l/CPR, logical chunk
-// (l%CPR) ^ swz_t(row) (CPR = R/8 chunks per row), into physical chunk l%CPR.
+// M/N-contiguous 16-bit operand (B row-major, A column-major): the 64 K-rows of
+// a K-tile, R values (2R bytes) each, row pitch 2R + 32 bytes, K-rows with bit
+// 3 clear in a first region and those with bit 3 set in a second one that
+// starts 128 bytes past a multiple of 256.  A transposing read by 16 lanes
+// covers four consecutive K-rows x 32 bytes, which the 32-byte row shift puts
+// on four different 32-byte bank groups; the two 16-lane groups that read
+// K-rows k and k + 8 land in opposite 128-byte halves (measured on gfx950:
+// conflict-free; without the region split, two-way conflicts).  Each fragment
+// address is one per-lane base plus a constant.
 // ---------------------------------------------------------------------------
-template <int R, int NW> struct McStage {
+template <int R> __device__ __forceinline__ constexpr uint32_t mc_row_off(uint32_t k)
+{
+    constexpr uint32_t P = 2 * R + 32;
+    return ((k >> 3) & 1u) * (32 * P + 128) + ((k & 7u) | ((k >> 4) << 3)) * P;
+}
+
+template <int R, int NW> struct McTile {
     static_assert(R == 128 || R == 256, "transposed tile of 128 or 256 values");
-    static constexpr int CPR = R / 8;
-    static constexpr int RPI = 64 / CPR;
+    static constexpr int CPR = R / 8;   // 16-byte chunks per K-row
+    static constexpr int RPI = 64 / CPR; // K-rows per 1 KiB transfer
     static constexpr int NL = R / (8 * NW);
     static_assert(NL * 8 * NW == R, "whole 1 KiB transfers per wavefront");
-    uint32_t base[NL]; // (k*ld + n) bytes at K-tile 0, or OOB
-    uint32_t krow[NL]; // K-row within the K-tile
+    static constexpr uint32_t BYTES = 64 * (2 * R + 32) + 128;
+    uint32_t voff;     // K-row l / CPR, chunk l % CPR; OOB for columns past N
+    uint32_t wofs[NL]; // LDS byte offset of each staging write
+    uint32_t first;    // byte offset of the wavefront's first K-row
+    uint32_t xstep;    // bytes between the first K-rows of consecutive transfers
+    uint32_t kstep;    // bytes per K-tile (64 K-rows)
 
+    // Transfer i of wavefront w moves K-rows q RPI .. +RPI-1 (q = w NL + i):
+    // lane l carries K-row q RPI + l / CPR, chunk l % CPR.
     __device__ __forceinline__ void init(int64_t ld_bytes, int64_t mn_valid, uint32_t wave, uint32_t lane)
     {
+        const uint32_t chunk = lane % CPR;
+        voff = (int64_t)(8 * chunk) < mn_valid ? (lane / CPR) * (uint32_t)ld_bytes + chunk * 16 : OOB;
+        first = wave * NL * RPI * (uint32_t)ld_bytes;
+        xstep = RPI * (uint32_t)ld_bytes;
+        kstep = 64 * (uint32_t)ld_bytes;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const uint32_t q = wave * NL + i;
-            const uint32_t k = q * RPI + lane / CPR;
-            const uint32_t chunk = (lane % CPR) ^ swz_t(k);
-            krow[i] = k;
-            base[i] = (int64_t)(8 * chunk) < mn_valid ? (uint32_t)(k * ld_bytes + chunk * 16) : OOB;
-        }
+        for (int i = 0; i < NL; ++i)
+            wofs[i] = mc_row_off<R>((wave * NL + i) * RPI + lane / CPR) + chunk * 16;
     }
-    // K-tile kt: K-rows kt*64 .. +63 (k_rows = K; tile_step = 64 * ld bytes)
-    __device__ __forceinline__ u32x4 load(int i, __amdgpu_buffer_rsrc_t r, int kt, uint32_t k_rows,
-                                          uint32_t tile_step) const
+    // K-tile kt: K-rows kt*64 .. +63; K-rows past K lie past the slice end.
+    __device__ __forceinline__ u32x4 load(int i, __amdgpu_buffer_rsrc_t r, int kt, uint32_t) const
     {
-        const uint32_t k0 = (uint32_t)kt * 64u;
-        return load16(r, (base[i] != OOB && k0 + krow[i] < k_rows) ? base[i] + (uint32_t)kt * tile_step : OOB);
+        return load16s(r, voff, first + (uint32_t)i * xstep + (uint32_t)kt * kstep);
     }
-    // Operand fragment of columns [c0, c0+32) at K-step ks: lane l gets column
-    // c0 + l%32, k = 16ks + 8(l/32) + 0..7.
+    __device__ __forceinline__ void store(int i, char *tile, uint32_t, uint32_t, u32x4 v) const
+    {
+        *reinterpret_cast<u32x4 *>(tile + wofs[i]) = v;
+    }
+    // Columns [c0, c0 + 16), K-step ks: lane l gets column c0 + l % 16 and
+    // k = 32 ks + 8 (l / 16) + 0..7, by two transposing reads (k .. k+3, then
+    // k+4 .. k+7).  Lane j of each 16-lane group g addresses
+    // X[32 ks + 8 g + j / 4][c0 + 4 (j % 4)]; the probe pins that lane i of the
+    // group then receives X[32 ks + 8 g .. +3][c0 + i].
     static __device__ __forceinline__ u32x4 frag(const char *tile, uint32_t c0, uint32_t ks, uint32_t lane)
     {
+        constexpr uint32_t P = 2 * R + 32;
         const uint32_t g = lane >> 4, j = lane & 15u;
-        const uint32_t n = c0 + 16 * (g & 1u) + 4 * (j & 3u);
-        const uint32_t chunk = n >> 3, inner = (n & 7u) * 2;
-        const uint32_t k = 16 * ks + 8 * (g >> 1) + (j >> 2);
-        const uint32_t a0 = k * (2 * R) + ((chunk ^ swz_t(k)) << 4) + inner;
-        const uint32_t a1 = (k + 4) * (2 * R) + ((chunk ^ swz_t(k + 4)) << 4) + inner;
+        const uint32_t k = 32 * ks + 8 * g + (j >> 2);
+        const uint32_t a0 = mc_row_off<R>(k) + (c0 + 4 * (j & 3u)) * 2;
+        const uint32_t a1 = a0 + 4 * P; // k + 4: same region, four rows on
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(tile + a0));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(tile + a1));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -174,55 +186,51 @@ template <int R, int NW> struct McStage {
     }
 };
 
+template <int MODE, int R, int NW> struct TileOf;
+template <int R, int NW> struct TileOf<KC16, R, NW> { typedef KcTile<R, NW, false> type; };
+template <int R, int NW> struct TileOf<KCD, R, NW> { typedef KcTile<R, NW, true> type; };
+template <int R, int NW> struct TileOf<MC16, R, NW> { typedef McTile<R, NW> type; };
+
 // ---------------------------------------------------------------------------
-// Epilogue through LDS.  A wavefront owns (32 MT) x (32 NT) results; lane l
-// holds, per 32 x 32 MFMA tile and register group g, four consecutive columns
-// of one row (the D^T orientation, dmu_device.hpp).  Written straight to
-// memory that is 32 rows x 16 bytes per store instruction; here each 32-row
-// stripe is first parked in the wavefront's own LDS area as fp32, then read
-// back row-contiguous so that each store instruction writes two full rows of
-// 32 NT values (whole cache lines), with C added and the result converted on
-// the way out (the shared-memory route to wide stores that the walkthrough's
-// section 7.5 and "Tensor Cores, CUTLASS and CuTe" section 4.5 point to).
+// Epilogue through LDS for 16 x 16 tiles: each 16-row stripe of the
+// wavefront's results is parked in its own LDS area and read back
+// row-contiguous, so that every store instruction writes whole rows of 16 NT
+// values (C added, RNE conversion, M/N masking on the way out).
 // ---------------------------------------------------------------------------
 template <int O, int MT, int NT, class AccT>
 __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&acc)[MT][NT], char *lds,
-                                             int64_t m_base, int64_t n_base, uint32_t lane, const char *Cb, char *Db)
+                                               int64_t m_base, int64_t n_base, uint32_t lane, const char *Cb,
+                                               char *Db)
 {
     typedef typename Out<O>::t ot;
     typedef decltype(acc[0][0][0]) sref;
     typedef typename std::remove_const<typename std::remove_reference<sref>::type>::type st; // float or int
     typedef st st4 __attribute__((ext_vector_type(4)));
-    constexpr int COLS = 32 * NT;
+    typedef ot ov4 __attribute__((ext_vector_type(4)));
+    constexpr int COLS = 16 * NT;
     constexpr int PITCH = COLS * 4 + 16; // bytes per parked row (+16 spreads rows over the banks)
+    constexpr int LPR = COLS / 4;        // lanes per row on the way out
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
-        // park: lane l writes 4 values of row l%32 per (ni, g)
 #pragma unroll
-        for (int ni = 0; ni < NT; ++ni)
+        for (int ni = 0; ni < NT; ++ni) {
+            st4 v;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t col = ni * 32 + 8 * g + 4 * (lane >> 5);
-                st4 v;
+            for (int e = 0; e < 4; ++e)
+                v[e] = acc[mi][ni][e];
+            *reinterpret_cast<st4 *>(lds + (lane & 15u) * PITCH + (ni * 16 + 4 * (lane >> 4)) * 4) = v;
+        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = acc[mi][ni][4 * g + e];
-                *reinterpret_cast<st4 *>(lds + (lane & 31u) * PITCH + col * 4) = v;
-            }
-        // read back row-contiguous: lanes 0..31 and 32..63 take two rows
-        constexpr int LPR = COLS / 4; // lanes per row
-#pragma unroll 4
-        for (int it = 0; it < 32 * LPR / 64; ++it) {
+        for (int it = 0; it < 16 * LPR / 64; ++it) {
             const uint32_t idx = it * 64 + lane;
             const uint32_t row = idx / LPR, col = (idx % LPR) * 4;
             const st4 v = *reinterpret_cast<const st4 *>(lds + row * PITCH + col * 4);
-            const int64_t m = m_base + mi * 32 + row, n = n_base + col;
+            const int64_t m = m_base + mi * 16 + row, n = n_base + col;
             if (m >= p.M)
                 continue;
             const ot *Crow = Cb ? reinterpret_cast<const ot *>(Cb) + m * p.ldc : nullptr;
             ot *Drow = reinterpret_cast<ot *>(Db) + m * p.ldd;
             if (p.d_vec4 && n + 3 < p.N) {
-                typedef ot ov4 __attribute__((ext_vector_type(4)));
                 ov4 o;
                 if (Crow) {
                     const ov4 c = *reinterpret_cast<const ov4 *>(Crow + n);
@@ -255,35 +263,24 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
     }
 }
 
-// Fragment that the MFMA sequence q = 0 .. MT*NT-1 (A fragment q / NT, B
-// fragment q % NT) needs idx-th: A 0 with B 0, then B 1 .. NT-1 (with A 0),
-// then A 1 .. MT-1.  A fragments are numbered 0..MT-1, B fragments MT.. .
-// (A closed form, so that it folds to a constant in every unrolled loop.)
-template <int MT, int NT> __device__ constexpr int first_use(int idx)
-{
-    return idx == 0 ? 0 : (idx <= NT ? MT + idx - 1 : idx - NT);
-}
-
-template <int MODE, int R, int NW> struct StageOf;
-template <int R, int NW> struct StageOf<KC16, R, NW> { typedef KcStage<R, NW, false> type; };
-template <int R, int NW> struct StageOf<KCD, R, NW> { typedef KcStage<R, NW, true> type; };
-template <int R, int NW> struct StageOf<MC16, R, NW> { typedef McStage<R, NW> type; };
-
 template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
 __global__ void __launch_bounds__(64 * WGM * WGN)
-    __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4))) gemm_tiled(GemmParams p)
+    __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tiled(GemmParams p)
 {
     constexpr int E = T == I8 ? 1 : 2;
     constexpr int NW = WGM * WGN;
+    static_assert(NW == 8, "eight wavefronts, two per SIMD");
     constexpr int WTM = BM / WGM, WTN = BN / WGN; // wavefront tile
-    constexpr int MT = WTM / 32, NT = WTN / 32;   // MFMA tiles per wavefront
-    constexpr int ABYTES = BM * 128, STAGE = (BM + BN) * 128;
+    constexpr int MT = WTM / 16, NT = WTN / 16;   // MFMA tiles per wavefront
+    constexpr int MN = MT * NT;
+    static_assert(MT % 2 == 0, "a K-step runs in two halves of the tile rows");
     static_assert(AMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(BMODE != MC16 || E == 2, "transposed operands are 16-bit");
     typedef typename Mfma<T>::acc_t acc_t;
-    typedef typename StageOf<AMODE, BM, NW>::type ATile;
-    typedef typename StageOf<BMODE, BN, NW>::type BTile;
+    typedef typename TileOf<AMODE, BM, NW>::type ATile;
+    typedef typename TileOf<BMODE, BN, NW>::type BTile;
     constexpr int NA = ATile::NL, NB = BTile::NL;
+    constexpr uint32_t ABYTES = (ATile::BYTES + 255) & ~255u, STAGE = (ABYTES + BTile::BYTES + 255) & ~255u;
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
@@ -293,49 +290,39 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     const TileCoord tc = tile_of(p, blockIdx.x);
     const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
 
-    // Buffer descriptors cover this tile's part of each operand, from its first
-    // row (K-contiguous) or column (M/N-contiguous) to the end of the batch slice.
+    // Each operand's descriptor starts at this tile's first row (K-contiguous)
+    // or column (M/N-contiguous) and ends with the batch slice.
     const char *Ab = p.A + (int64_t)tc.b * p.stride_a * E;
     const char *Bb = p.B + (int64_t)tc.b * p.stride_b * E;
     const int64_t a_start = AMODE != MC16 ? m0 * p.lda * E : m0 * E;
     const int64_t b_start = BMODE != MC16 ? n0 * p.ldb * E : n0 * E;
-    // The range check works per dword, and a slice may end inside one (4-byte
-    // aligned rows, odd byte counts): the byte counts are rounded up to whole
-    // dwords so that the straddling dword keeps its valid head; its tail is
-    // cleared by the K-tail mask, and a dword never crosses a page.
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)((p.a_bytes - a_start + 3) & ~3ll));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)((p.b_bytes - b_start + 3) & ~3ll));
 
     ATile ta;
     BTile tb;
-    ta.init(p.lda * E, p.M - m0, wave, lane);
-    tb.init(p.ldb * E, p.N - n0, wave, lane);
-    // per-operand K extent and K-tile step for the loads
-    const uint32_t a_kdim = AMODE != MC16 ? (uint32_t)p.K * E : (uint32_t)p.K;
-    const uint32_t b_kdim = BMODE != MC16 ? (uint32_t)p.K * E : (uint32_t)p.K;
-    const uint32_t a_step = (uint32_t)(64 * p.lda * E), b_step = (uint32_t)(64 * p.ldb * E);
+    if constexpr (AMODE == MC16)
+        ta.init(p.lda * E, p.M - m0, wave, lane);
+    else
+        ta.init(p.lda * E, wave, lane);
+    if constexpr (BMODE == MC16)
+        tb.init(p.ldb * E, p.N - n0, wave, lane);
+    else
+        tb.init(p.ldb * E, wave, lane);
+    const uint32_t k_bytes = (uint32_t)p.K * E;
 
     u32x4 sa[NA], sb[NB]; // the next K-tile between its global loads and its LDS writes
     auto load_one = [&](int c, int kt) {
         if (c < NA)
-            sa[c] = ta.load(c, ra, kt, a_kdim, a_step);
+            sa[c] = ta.load(c, ra, kt, k_bytes);
         else
-            sb[c - NA] = tb.load(c - NA, rb, kt, b_kdim, b_step);
+            sb[c - NA] = tb.load(c - NA, rb, kt, k_bytes);
     };
     auto store_one = [&](int c, char *stage) {
         if (c < NA)
-            *reinterpret_cast<u32x4 *>(stage + (wave * NA + c) * 1024 + lane * 16) = sa[c];
+            ta.store(c, stage, wave, lane, sa[c]);
         else
-            *reinterpret_cast<u32x4 *>(stage + ABYTES + (wave * NB + (c - NA)) * 1024 + lane * 16) = sb[c - NA];
-    };
-    // The f-th fragment read of K-step ks, in the order of first use by the
-    // MFMA sequence (fragment g: 0..MT-1 A rows, MT..MT+NT-1 B columns).
-    auto read_one = [&](int f, const char *stage, int ks, u32x4 *af, u32x4 *bf) {
-        f = first_use<MT, NT>(f);
-        if (f < MT)
-            af[f] = ATile::frag(stage, wm * WTM + f * 32, ks, lane);
-        else
-            bf[f - MT] = BTile::frag(stage + ABYTES, wn * WTN + (f - MT) * 32, ks, lane);
+            tb.store(c - NA, stage + ABYTES, wave, lane, sb[c - NA]);
     };
 
     acc_t acc[MT][NT];
@@ -345,13 +332,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         for (int j = 0; j < NT; ++j)
             acc[i][j] = acc_t{};
 
-    const int nk = (int)(((int64_t)p.K * E + 127) / 128);
-    constexpr int NLD = NA + NB, MN = MT * NT, NF = MT + NT;
+    u32x4 af[MT], bfr[NT];
+    auto read_a = [&](int i, const char *stage, int ks) { af[i] = ATile::frag(stage, wm * WTM + i * 16, ks, lane); };
+    auto read_b = [&](int j, const char *stage, int ks) {
+        bfr[j] = BTile::frag(stage + ABYTES, wn * WTN + j * 16, ks, lane);
+    };
 
-    // Fragment registers: a double buffer over the K-steps, carried across
-    // K-tiles (K-step 0 of the next K-tile is read while the last MFMAs of the
-    // current one run).
-    u32x4 af[2][MT], bfr[2][NT];
+    const int nk = (int)(((int64_t)p.K * E + 127) / 128);
+    constexpr int NLD = NA + NB;
 
     if (nk > 0) {
 #pragma unroll
@@ -365,68 +353,97 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
             load_one(c, 1);
         stage_barrier();
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
-            read_one(f, smem, 0, af[0], bfr[0]);
+        for (int i = 0; i < MT; ++i)
+            read_a(i, smem, 0);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            read_b(j, smem, 0);
     }
 
-    // Staging registers run one K-tile ahead of the LDS stages: in K-tile kt,
-    // register c is written to the free stage (K-tile kt+1) and at once
-    // reloaded with K-tile kt+2, so every global load has a whole K-tile of
-    // MFMAs to arrive.  Near the end the same schedule runs on K-tiles that lie
-    // wholly past K: the buffer range check turns their loads into zeros, so
-    // the body needs no branches (branches around the loads make the compiler
-    // drain the memory counters at every join).
-    constexpr int SLOTS = 3 * MN; // MFMAs of K-steps 0-2 carry the copies
+    // MFMA order within a K-step: two halves of the tile rows, each walked
+    // column by column -- slot q is tile (row_of(q), col_of(q)).  Every fragment
+    // is reloaded right after its last use; the order leaves at least
+    // min(MN/2 + MT/2, MN/2 - MT/2 + 1) MFMAs between a reload and the next use.
+    constexpr int HM = MT / 2, HALF = MN / 2;
+    auto row_of = [](int q) { return (q / HALF) * HM + (q % HALF) % HM; };
+    auto col_of = [](int q) { return (q % HALF) / HM; };
+    auto last_a = [](int i) { return (i / HM) * HALF + (NT - 1) * HM + i % HM; }; // slot of A_i's last use
+    auto last_b = [](int j) { return HALF + j * HM + HM - 1; };                  // slot of B_j's last use
+
+    // Staging copies (K-tile kt+1 to the free stage, then the loads of K-tile
+    // kt+2 into the same registers) ride on the MFMAs of K-step 0 and of the
+    // first half of K-step 1, ahead of the stage hand-over.  K-tiles past K
+    // read as zeros through the range check, so the body is branch-free.
+    constexpr int SLOTS = MN + HALF;
     for (int kt = 0; kt < nk; ++kt) {
         const char *cur = smem + (kt & 1) * STAGE;
         char *nxt = smem + ((kt + 1) & 1) * STAGE;
+        // K-step 0; each fragment of K-step 1 is read right after its last use.
 #pragma unroll
-        for (int ks = 0; ks < 3; ++ks) {
-            const int c = ks & 1, n = c ^ 1;
+        for (int q = 0; q < MN; ++q) {
+            const int i = row_of(q), j = col_of(q);
+            acc[i][j] = Mfma<T>::step(bfr[j], af[i], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0); // reads below reuse the registers this MFMA reads
+            if (q == last_b(j))
+                read_b(j, cur, 1);
+            if (q == last_a(i))
+                read_a(i, cur, 1);
 #pragma unroll
-            for (int q = 0; q < MN; ++q) {
-                acc[q / NT][q % NT] = Mfma<T>::step(bfr[c][q % NT], af[c][q / NT], acc[q / NT][q % NT]);
-                // fragments [q*NF/MN, (q+1)*NF/MN) of the next K-step
-#pragma unroll
-                for (int f = q * NF / MN; f < (q + 1) * NF / MN; ++f)
-                    read_one(f, cur, ks + 1, af[n], bfr[n]);
-                // staging registers [slot*NLD/SLOTS, (slot+1)*NLD/SLOTS): K-tile kt+1 to
-                // LDS, then the loads of K-tile kt+2
-                const int slot = ks * MN + q;
-#pragma unroll
-                for (int ci = slot * NLD / SLOTS; ci < (slot + 1) * NLD / SLOTS; ++ci) {
-                    store_one(ci, nxt);
-                    load_one(ci, kt + 2);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int ci = q * NLD / SLOTS; ci < (q + 1) * NLD / SLOTS; ++ci) {
+                store_one(ci, nxt);
+                load_one(ci, kt + 2);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // K-step 3: half of its MFMAs, the stage hand-over, then the other half
-        // with the first fragment reads of K-tile kt+1.
+        // K-step 1, first half: the remaining staging copies.
 #pragma unroll
-        for (int q = 0; q < MN / 2; ++q) {
-            acc[q / NT][q % NT] = Mfma<T>::step(bfr[1][q % NT], af[1][q / NT], acc[q / NT][q % NT]);
+        for (int q = 0; q < HALF; ++q) {
+            const int i = row_of(q), j = col_of(q);
+            acc[i][j] = Mfma<T>::step(bfr[j], af[i], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            const int slot = MN + q;
+#pragma unroll
+            for (int ci = slot * NLD / SLOTS; ci < (slot + 1) * NLD / SLOTS; ++ci) {
+                store_one(ci, nxt);
+                load_one(ci, kt + 2);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         stage_barrier();
+        // Second half: K-step 0 of K-tile kt+1 from the other stage -- first the
+        // A fragments of the rows already done, one per MFMA, then each
+        // remaining fragment right after its last use.
 #pragma unroll
-        for (int q = MN / 2; q < MN; ++q) {
-            acc[q / NT][q % NT] = Mfma<T>::step(bfr[1][q % NT], af[1][q / NT], acc[q / NT][q % NT]);
-            const int h = q - MN / 2; // fragments [h*NF/(MN/2), (h+1)*NF/(MN/2)) of K-step 0, K-tile kt+1
-#pragma unroll
-            for (int f = h * NF / (MN / 2); f < (h + 1) * NF / (MN / 2); ++f)
-                read_one(f, nxt, 0, af[0], bfr[0]);
+        for (int q = HALF; q < MN; ++q) {
+            const int i = row_of(q), j = col_of(q), h = q - HALF;
+            acc[i][j] = Mfma<T>::step(bfr[j], af[i], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (h < HM)
+                read_a(h, nxt, 0);
+            if (q == last_b(j))
+                read_b(j, nxt, 0);
+            if (q == last_a(i))
+                read_a(i, nxt, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // Every wavefront is past the last barrier and reads no stage any more:
-    // each parks its results in its own part of the stages.
-    const char *Cb = p.C ? p.C + (int64_t)tc.b * p.stride_c * dt_bytes(O) : nullptr;
-    char *Db = p.D + (int64_t)tc.b * p.stride_d * dt_bytes(O);
-    constexpr int PARK = 32 * (32 * NT * 4 + 16);
+    // each parks its results in its own part of the stages.  The tile
+    // coordinates and lane are derived afresh from opaque copies of the ids, so
+    // that the compiler does not keep the values of the prologue alive (in
+    // registers the loop needs) across the K loop.
+    uint32_t wg2 = blockIdx.x, tid2 = threadIdx.x;
+    asm volatile("" : "+s"(wg2));
+    asm volatile("" : "+v"(tid2));
+    const TileCoord te = tile_of(p, wg2);
+    const uint32_t lane2 = tid2 & 63u, wave2 = __builtin_amdgcn_readfirstlane(tid2 >> 6);
+    const char *Cb = p.C ? p.C + (int64_t)te.b * p.stride_c * dt_bytes(O) : nullptr;
+    char *Db = p.D + (int64_t)te.b * p.stride_d * dt_bytes(O);
+    constexpr int PARK = 16 * (16 * NT * 4 + 16);
     static_assert(NW * PARK <= 2 * STAGE, "parking area fits in the stages");
-    store_staged<O, MT, NT>(p, acc, smem + wave * PARK, m0 + wm * WTM, n0 + wn * WTN, lane, Cb, Db);
+    store_staged<O, MT, NT>(p, acc, smem + wave2 * PARK, (int64_t)te.tm * BM + (wave2 / WGN) * WTM,
+                              (int64_t)te.tn * BN + (wave2 % WGN) * WTN, lane2, Cb, Db);
 }
 
 } // namespace dmu

@@ -153,8 +153,10 @@ const char *dmu_last_error(void);
  *                           (in_type bits)        row-major          [64 lanes][regs] 32-bit
  *  DMU_PROBE_LDS_READ_B128  LDS image, 4096 B     int32 byte         [64][16 bytes]
  *  DMU_PROBE_LDS_READ_TR16  LDS image, 4096 B     address per lane   [64][8 bytes]
- *  DMU_PROBE_LDS_FRAG       32 x 128-byte tile,   unused             [64][4 K-steps][16 bytes]
- *                           row-major (logical)
+ *  DMU_PROBE_LDS_FRAG       32 x 128-byte tile,   unused             [64][2 row blocks][2 K-steps]
+ *                           row-major (logical)                      [16 bytes]
+ *  DMU_PROBE_LDS_FRAG_T     64 x 128 16-bit tile, unused             [64][8 column blocks][2 K-steps]
+ *                           row-major (logical)                      [8 16-bit values]
  *  DMU_PROBE_CVT_BF16/_F16  float32[256]          unused             [256] 16-bit patterns
  *
  *  MFMA_*: lane l loads its operand fragments straight from in0/in1 with the
@@ -163,8 +165,13 @@ const char *dmu_last_error(void);
  *    (lane, register) against the product.
  *  LDS_READ_*: the image is copied to LDS; lane l reads at in1[l] (masked to
  *    an aligned in-bounds address) with ds_read_b128 / ds_read_b64_tr_b16.
- *  LDS_FRAG: the tile is stored with the GEMM kernels' swizzled LDS writes and
- *    read back with their fragment reads for K-steps 0..3.
+ *  LDS_FRAG: the tile is stored with the tiled kernel's staging writes of a
+ *    K-contiguous operand and read back with its fragment reads (rows 16 b +
+ *    l % 16, bytes 64 ks + 16 (l / 16) .. +15).
+ *  LDS_FRAG_T: the tile (K-rows x values) is stored with the tiled kernel's
+ *    staging writes of an M/N-contiguous operand and read back with its
+ *    transposing fragment reads (column 16 b + l % 16, k = 32 ks + 8 (l / 16)
+ *    + 0..7).
  *  CVT_*: the GEMM epilogue's fp32 -> bf16 / fp16 conversion.
  * dmu_probe_info() reports m, n, k, the input type and the number of 32-bit
  * output words per lane.  `stream` as for dmu_gemm.
@@ -179,6 +186,7 @@ enum {
     DMU_PROBE_LDS_READ_B128 = 10,
     DMU_PROBE_LDS_READ_TR16 = 11,
     DMU_PROBE_LDS_FRAG = 12,
+    DMU_PROBE_LDS_FRAG_T = 13,
     DMU_PROBE_CVT_BF16 = 30,
     DMU_PROBE_CVT_F16 = 31
 };

@@ -27,7 +27,7 @@ REDUCED = {
     "c4o": dict(M=300, N=128, K=520, batch=2),
     "c5": dict(M=300, N=260, K=384),
 }
-KERNELS = [None, "256x256", "256x256w4", "128x128", "256x128", "generic"]
+KERNELS = [None, "256x256", "128x128", "256x128", "generic"]
 
 
 @pytest.mark.parametrize("cfg", list(REDUCED))

@@ -156,19 +156,41 @@ def test_lds_read_tr16_mapping():
 
 
 def test_lds_fragment_format():
-    """The kernels' swizzled LDS tile writes + fragment reads return, for lane l and
-    K-step ks, bytes 32*ks + 16*(l/32) .. +15 of logical row l % 32."""
+    """The tiled kernel's staging writes + fragment reads of a K-contiguous tile return,
+    for lane l, row block rb and K-step ks, bytes 64*ks + 16*(l/16) .. +15 of logical
+    row 16*rb + l % 16."""
     import torch
 
     words = np.arange(32 * 64, dtype=np.uint16)  # 32 rows x 64 16-bit words = 128 bytes/row
     out = torch.zeros(64 * 16, dtype=torch.int32, device="cuda:0")
     dmu.dmu_probe(dmu.DMU_PROBE_LDS_FRAG, gu.to_dev(words), None, out)
     torch.cuda.synchronize()
-    got = out.cpu().numpy().view(np.uint16).reshape(64, 4, 8)
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 2, 2, 8)
     for lane in range(64):
-        for ks in range(4):
-            w0 = (lane % 32) * 64 + (32 * ks + 16 * (lane // 32)) // 2
-            assert np.array_equal(got[lane, ks], words[w0: w0 + 8]), (lane, ks)
+        for rb in range(2):
+            for ks in range(2):
+                w0 = (16 * rb + lane % 16) * 64 + (64 * ks + 16 * (lane // 16)) // 2
+                assert np.array_equal(got[lane, rb, ks], words[w0: w0 + 8]), (lane, rb, ks)
+
+
+def test_lds_fragment_format_transposed():
+    """The tiled kernel's staging writes + transposing fragment reads of an M/N-contiguous
+    tile (64 K-rows x 128 values) return, for lane l, column block cb and K-step ks, the
+    values X[32*ks + 8*(l/16) + 0..7][16*cb + l % 16]: the operand layout of the 16 x 16
+    instruction."""
+    import torch
+
+    X = np.arange(64 * 128, dtype=np.uint16).reshape(64, 128)
+    out = torch.zeros(64 * 64, dtype=torch.int32, device="cuda:0")
+    dmu.dmu_probe(dmu.DMU_PROBE_LDS_FRAG_T, gu.to_dev(X.reshape(-1)), None, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 8, 2, 8)
+    for lane in range(64):
+        for cb in range(8):
+            for ks in range(2):
+                k0 = 32 * ks + 8 * (lane // 16)
+                want = X[k0: k0 + 8, 16 * cb + lane % 16]
+                assert np.array_equal(got[lane, cb, ks], want), (lane, cb, ks, got[lane, cb, ks], want)
 
 
 @pytest.mark.parametrize("t,variant", [("bf16", dmu.DMU_PROBE_CVT_BF16), ("f16", dmu.DMU_PROBE_CVT_F16)])
