@@ -100,9 +100,9 @@ __global__ void __launch_bounds__(64) probe_lds_tr16(const char *img, const int3
 }
 
 // The tiled kernel's K-contiguous LDS format: a 32-row x 128-byte tile is
-// written with the kernel's staging writes (transfer q, lane l -> LDS bytes
-// 1024 q + 16 l, carrying row 8q + l/8, logical chunk (l%8) ^ (l/8)) and read
-// back with its fragment reads for row blocks 0 and 16, K-steps 0 and 1.
+// written with the kernel's staging writes (transfer q, lane l carrying row
+// 8q + l/8, chunk l%8) and read back with its fragment reads for row blocks 0
+// and 16, K-steps 0 and 1.
 // Output per lane: [row block][K-step][16 bytes].
 __global__ void __launch_bounds__(64) probe_lds_frag(const char *tile, uint32_t *out)
 {
@@ -110,11 +110,11 @@ __global__ void __launch_bounds__(64) probe_lds_frag(const char *tile, uint32_t 
     __shared__ __attribute__((aligned(1024))) char lds[Tile::BYTES];
     const uint32_t l = threadIdx.x;
     for (int q = 0; q < Tile::NL; ++q) {
-        const uint32_t row = 8 * q + l / 8, chunk = (l % 8) ^ (l / 8);
+        const uint32_t row = 8 * q + l / 8, chunk = l % 8;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + row * 128u + chunk * 16u);
         Tile t;
         t.init(128, 0, l);
-        t.store(q, lds, 0, l, v);
+        t.store(q, lds, 0, l, v, 0, 128);
     }
     __syncthreads();
     for (int rb = 0; rb < 2; ++rb)
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(64) probe_lds_frag_t(const char *tile, uint32_
         t.init(256, 128, w, l);
         for (int i = 0; i < Tile::NL; ++i) {
             const uint32_t k = (w * Tile::NL + i) * Tile::RPI + l / Tile::CPR, chunk = l % Tile::CPR;
-            t.store(i, lds, w, l, *reinterpret_cast<const u32x4 *>(tile + k * 256u + chunk * 16u));
+            t.store(i, lds, w, l, *reinterpret_cast<const u32x4 *>(tile + k * 256u + chunk * 16u), 0, 0);
         }
     }
     __syncthreads();

@@ -69,42 +69,47 @@ template <int R, int NW, bool MASK> struct KcTile {
     static constexpr int NL = R / (8 * NW); // 1 KiB transfers per wavefront
     static_assert(NL * 8 * NW == R, "whole 1 KiB transfers per wavefront");
     static constexpr uint32_t BYTES = R * 128;
-    uint32_t voff;  // lane offset within a transfer: row l / 8, logical chunk (l % 8) ^ (l / 8)
+    uint32_t voff;  // lane offset within a transfer: row l / 8, chunk l % 8
     uint32_t cb;    // byte of that chunk within a K-tile row
+    uint32_t wlane; // LDS offset of this lane's 16 bytes within a transfer
     uint32_t first; // byte offset of the wavefront's first row
     uint32_t xstep; // bytes between the first rows of consecutive transfers
 
     // Transfer i of wavefront w moves rows 8q .. 8q+7 (q = w NL + i) into LDS
-    // bytes 1024 q .. +1023: lane l carries row 8q + l / 8, logical chunk
-    // (l % 8) ^ (l / 8), to physical chunk l % 8.
+    // bytes 1024 q .. +1023: lane l carries row 8q + l / 8, chunk l % 8 (eight
+    // consecutive lanes read one 128-byte row segment in order), to physical
+    // chunk (l % 8) ^ (l / 8).
     __device__ __forceinline__ void init(int64_t ld_bytes, uint32_t wave, uint32_t lane)
     {
-        cb = ((lane & 7u) ^ (lane >> 3)) * 16;
+        cb = (lane & 7u) * 16;
         voff = (lane >> 3) * (uint32_t)ld_bytes + cb;
+        wlane = (lane >> 3) * 128 + (((lane & 7u) ^ (lane >> 3)) << 4);
         first = 8 * wave * NL * (uint32_t)ld_bytes;
         xstep = 8 * (uint32_t)ld_bytes;
     }
     // K-tile kt: bytes kt*128 .. +127 of each row (k_bytes = K * element size).
-    // MASK: rows are only 4-byte aligned and K * element size need not be a
-    // multiple of 16, so the vector that straddles the end of a row also holds
-    // bytes of the next row; they are cleared here.
     __device__ __forceinline__ u32x4 load(int i, __amdgpu_buffer_rsrc_t r, int kt, uint32_t k_bytes) const
     {
         const uint32_t kb0 = (uint32_t)kt * 128u;
-        u32x4 x = load16s(r, kb0 + cb < k_bytes ? voff : OOB, first + (uint32_t)i * xstep + kb0);
+        return load16s(r, kb0 + cb < k_bytes ? voff : OOB, first + (uint32_t)i * xstep + kb0);
+    }
+    // The data of K-tile kt to LDS.  MASK: rows are only 4-byte aligned and
+    // K * element size need not be a multiple of 16, so the vector that
+    // straddles the end of a row also holds bytes of the next row; they are
+    // cleared here, where the load has long completed (clearing them right
+    // after the load would make the wavefront wait for it there).
+    __device__ __forceinline__ void store(int i, char *tile, uint32_t wave, uint32_t, u32x4 v, int kt,
+                                          uint32_t k_bytes) const
+    {
         if constexpr (MASK) {
-            const int32_t rem = (int32_t)k_bytes - (int32_t)(kb0 + cb);
+            const int32_t rem = (int32_t)k_bytes - (int32_t)((uint32_t)kt * 128u + cb);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const int32_t vb = rem - 4 * d;
-                x[d] &= vb >= 4 ? 0xffffffffu : (vb <= 0 ? 0u : ((1u << (8 * vb)) - 1u));
+                v[d] &= vb >= 4 ? 0xffffffffu : (vb <= 0 ? 0u : ((1u << (8 * vb)) - 1u));
             }
         }
-        return x;
-    }
-    __device__ __forceinline__ void store(int i, char *tile, uint32_t wave, uint32_t lane, u32x4 v) const
-    {
-        *reinterpret_cast<u32x4 *>(tile + (wave * NL + i) * 1024 + lane * 16) = v;
+        *reinterpret_cast<u32x4 *>(tile + (wave * NL + i) * 1024 + wlane) = v;
     }
     // Rows [r0, r0 + 16) (r0 a multiple of 16), K-step ks (0, 1): lane l reads
     // row r0 + l % 16, logical bytes 64 ks + 16 (l / 16) .. +15 of the K-tile.
@@ -163,7 +168,7 @@ template <int R, int NW> struct McTile {
     {
         return load16s(r, voff, first + (uint32_t)i * xstep + (uint32_t)kt * kstep);
     }
-    __device__ __forceinline__ void store(int i, char *tile, uint32_t, uint32_t, u32x4 v) const
+    __device__ __forceinline__ void store(int i, char *tile, uint32_t, uint32_t, u32x4 v, int, uint32_t) const
     {
         *reinterpret_cast<u32x4 *>(tile + wofs[i]) = v;
     }
@@ -318,11 +323,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         else
             sb[c - NA] = tb.load(c - NA, rb, kt, k_bytes);
     };
-    auto store_one = [&](int c, char *stage) {
+    auto store_one = [&](int c, char *stage, int kt) { // staging register c holds K-tile kt
         if (c < NA)
-            ta.store(c, stage, wave, lane, sa[c]);
+            ta.store(c, stage, wave, lane, sa[c], kt, k_bytes);
         else
-            tb.store(c - NA, stage + ABYTES, wave, lane, sb[c - NA]);
+            tb.store(c - NA, stage + ABYTES, wave, lane, sb[c - NA], kt, k_bytes);
     };
 
     acc_t acc[MT][NT];
@@ -347,7 +352,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
             load_one(c, 0);
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
-            store_one(c, smem);
+            store_one(c, smem, 0);
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
             load_one(c, 1);
@@ -390,7 +395,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
                 read_a(i, cur, 1);
 #pragma unroll
             for (int ci = q * NLD / SLOTS; ci < (q + 1) * NLD / SLOTS; ++ci) {
-                store_one(ci, nxt);
+                store_one(ci, nxt, kt + 1);
                 load_one(ci, kt + 2);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -404,7 +409,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
             const int slot = MN + q;
 #pragma unroll
             for (int ci = slot * NLD / SLOTS; ci < (slot + 1) * NLD / SLOTS; ++ci) {
-                store_one(ci, nxt);
+                store_one(ci, nxt, kt + 1);
                 load_one(ci, kt + 2);
             }
             __builtin_amdgcn_sched_barrier(0);
