@@ -140,7 +140,8 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
         open(os.path.join(profiles, f"traffic_{workload_name}.md"), "w").write("\n".join(md) + "\n")
 
     # matrix-core and LDS counters
-    sq = _counter_means(_rows(os.path.join(d, "sq", "**", "*counter_collection.csv")), counted)
+    sq_rows = _rows(os.path.join(d, "sq", "**", "*counter_collection.csv"))
+    sq = _counter_means(sq_rows, counted)
     if sq:
         get = lambda c: _pick(sq, c, is_gemm)
         busy = get("SQ_VALU_MFMA_BUSY_CYCLES")
@@ -159,6 +160,13 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
             util = busy / (grbm / 8 * 1024)
             md += ["", f"MFMA busy fraction = MFMA_BUSY / (GUI_ACTIVE / 8 XCDs x 1024 SIMDs) = {util:.3f}."]
             result["mfma_busy_fraction"] = util
+            dur, _ = _timed_average_us([r for r in sq_rows if r["Counter_Name"] == "GRBM_GUI_ACTIVE"], counted)
+            if dur:
+                clk = grbm / 8 / (dur * 1e-6) / 1e9
+                md += [f"Dispatch duration under counter collection {dur:.2f} us; GUI_ACTIVE / 8 / duration = "
+                       f"{clk:.2f} GHz (GUI_ACTIVE cycles per second of dispatch; the busy fraction above uses "
+                       f"the same cycles)."]
+                result["gui_active_ghz"] = clk
         if conflict is not None and active:
             md += [f"LDS bank-conflict cycles / LDS active cycles = {conflict / active:.3f}."]
             result["lds_conflict_fraction"] = conflict / active
