@@ -11,7 +11,7 @@ measures that ramp instead of the kernel.  Prints one JSON
 line with the throughput, the MFMA roofline of the kernel and the CPU oracle's
 rate on a bounded row slice of the same product.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq]
                   [--no-cpu-baseline] [--copy-calibration MiB]
   python bench.py --summarize DIR [--workload W]   (rocprofv3 output -> profiles/)
 """
@@ -39,7 +39,11 @@ WORKLOAD_NAMES = {
     "c4s": "batched32_gemm_4096x4096x128_f16_tn_f32out",
     "c4o": "batched32_gemm_4096x128x4096_f16_nn_f32out",
     "c5": "gemm_8192x8192x8192_i8_tn_i32out",
+    "c5dq": "gemm_8192x8192x8192_i8_tn_dequant_rowcol_scale_bias_gelu_bf16out",
 }
+
+# Workloads that run with the fused epilogue (dmu_gemm_ex): base problem, output type, activation.
+EPILOGUE_WORKLOADS = {"c5dq": ("c5", "bf16", "gelu_tanh")}
 
 
 def source_digest() -> str:
@@ -81,7 +85,9 @@ def kernel_for(workload: str) -> str:
     import dense_matrix_unit_tiled_amd as dmu
     import workloads
 
-    M, N, K, batch, in_t, out_t, acc_t, la, lb = workloads.FULL[workload]
+    base, out_override = (EPILOGUE_WORKLOADS[workload][:2] if workload in EPILOGUE_WORKLOADS else (workload, None))
+    M, N, K, batch, in_t, out_t, acc_t, la, lb = workloads.FULL[base]
+    out_t = out_override or out_t
     lda, ldb, sa, sb = workloads._layout_params(M, N, K, la, lb)
     base = 1 << 40  # aligned stand-in addresses: only validation and selection run
     a = dmu.gemm_args(M, N, K, base, lda, base + (1 << 36), ldb, base + (2 << 36), N, in_type=in_t,
@@ -155,7 +161,17 @@ def main() -> int:
         x = np.ascontiguousarray(x)
         return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to("cuda:0")
 
-    p = workloads.make(args.workload, "random", 0)
+    ep = None
+    if args.workload in EPILOGUE_WORKLOADS:
+        base, out_t, act = EPILOGUE_WORKLOADS[args.workload]
+        p = workloads.with_output(workloads.make(base, "random", 0), out_t)
+        e = workloads.make_epilogue(p, 0, act=act)
+        ep_vecs = [to_dev(v) for v in (e.row_scale, e.col_scale, e.bias)]  # kept alive for the launches
+        ep = dmu.epilogue_args(row_scale=ep_vecs[0], stride_row_scale=e.stride_rs, col_scale=ep_vecs[1],
+                               stride_col_scale=e.stride_cs, bias=ep_vecs[2], stride_bias=e.stride_bias,
+                               act=e.act)
+    else:
+        p = workloads.make(args.workload, "random", 0)
     dA, dB = to_dev(p.A), to_dev(p.B)
     dC = to_dev(p.C) if p.C is not None else None
     out_dt = {"f32": torch.float32, "f16": torch.int16, "bf16": torch.int16, "i32": torch.int32}
@@ -168,15 +184,16 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     print(f"# workload {WORKLOAD_NAMES[args.workload]} kernel {kernel}", file=sys.stderr, flush=True)
 
+    launch = (lambda: dmu.dmu_gemm(a, stream)) if ep is None else (lambda: dmu.dmu_gemm_ex(a, ep, stream))
     for _ in range(args.warmup):
-        dmu.dmu_gemm(a, stream)
+        launch()
     torch.cuda.synchronize()
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
-        dmu.dmu_gemm(a, stream)
+        launch()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps

@@ -2,9 +2,10 @@
 
 Argument marshalling only: every step of the product runs in the library's HIP
 kernels.  The functions keep the C names (``dmu_gemm``, ``dmu_gemm_check``,
-``dmu_gemm_kernel_name``, ``dmu_status_string``, ``dmu_last_error``,
-``dmu_probe``, ``dmu_probe_info``); ``gemm_args`` fills the argument struct from
-torch tensors (or raw integer device addresses).  PyTorch supplies device
+``dmu_gemm_ex``, ``dmu_gemm_ex_check``, ``dmu_gemm_kernel_name``,
+``dmu_status_string``, ``dmu_last_error``, ``dmu_probe``, ``dmu_probe_info``);
+``gemm_args`` and ``epilogue_args`` fill the argument structs from torch tensors
+(or raw integer device addresses).  PyTorch supplies device
 memory and streams only.
 
 If ``libdmu.so`` has not been built, the first call raises ``RuntimeError``:
@@ -53,6 +54,21 @@ class dmu_gemm_args(ctypes.Structure):
     ]
 
 
+DMU_ACT_NONE, DMU_ACT_RELU, DMU_ACT_GELU_TANH = 0, 1, 2
+ACTS = {"none": DMU_ACT_NONE, "relu": DMU_ACT_RELU, "gelu_tanh": DMU_ACT_GELU_TANH}
+
+
+class dmu_epilogue(ctypes.Structure):
+    """Mirror of ``struct dmu_epilogue`` (include/dmu.h)."""
+
+    _fields_ = [
+        ("row_scale", ctypes.c_void_p), ("stride_row_scale", ctypes.c_int64),
+        ("col_scale", ctypes.c_void_p), ("stride_col_scale", ctypes.c_int64),
+        ("bias", ctypes.c_void_p), ("stride_bias", ctypes.c_int64),
+        ("act", ctypes.c_int32),
+    ]
+
+
 class DmuError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{dmu_status_string(status)}: {detail}")
@@ -78,6 +94,9 @@ def _load():
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.dmu_gemm.argtypes, lib.dmu_gemm.restype = [P, vp], i32
     lib.dmu_gemm_check.argtypes, lib.dmu_gemm_check.restype = [P], i32
+    PE = ctypes.POINTER(dmu_epilogue)
+    lib.dmu_gemm_ex.argtypes, lib.dmu_gemm_ex.restype = [P, PE, vp], i32
+    lib.dmu_gemm_ex_check.argtypes, lib.dmu_gemm_ex_check.restype = [P, PE], i32
     lib.dmu_gemm_kernel_name.argtypes, lib.dmu_gemm_kernel_name.restype = [P], ctypes.c_char_p
     lib.dmu_status_string.argtypes, lib.dmu_status_string.restype = [i32], ctypes.c_char_p
     lib.dmu_last_error.argtypes, lib.dmu_last_error.restype = [], ctypes.c_char_p
@@ -134,6 +153,29 @@ def dmu_gemm(args: dmu_gemm_args, stream=None, check: bool = True) -> int:
     if check and st != DMU_OK:
         raise DmuError(st, dmu_last_error())
     return st
+
+
+def epilogue_args(row_scale=None, stride_row_scale=0, col_scale=None, stride_col_scale=0, bias=None,
+                  stride_bias=0, act="none") -> dmu_epilogue:
+    """Fill a dmu_epilogue from float32 tensors/addresses and an activation name."""
+    e = dmu_epilogue()
+    e.row_scale, e.stride_row_scale = _addr(row_scale), stride_row_scale
+    e.col_scale, e.stride_col_scale = _addr(col_scale), stride_col_scale
+    e.bias, e.stride_bias = _addr(bias), stride_bias
+    e.act = ACTS[act] if isinstance(act, str) else act
+    return e
+
+
+def dmu_gemm_ex(args: dmu_gemm_args, ep: dmu_epilogue | None, stream=None, check: bool = True) -> int:
+    """Launch D = epilogue(A*B + C) on ``stream`` (default: torch's current stream)."""
+    st = _load().dmu_gemm_ex(ctypes.byref(args), None if ep is None else ctypes.byref(ep), _stream(stream))
+    if check and st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return st
+
+
+def dmu_gemm_ex_check(args: dmu_gemm_args, ep: dmu_epilogue | None) -> int:
+    return _load().dmu_gemm_ex_check(ctypes.byref(args), None if ep is None else ctypes.byref(ep))
 
 
 def dmu_gemm_check(args: dmu_gemm_args) -> int:

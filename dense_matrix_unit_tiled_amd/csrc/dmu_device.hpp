@@ -143,6 +143,58 @@ template <> struct Out<I32> {
     static __device__ __forceinline__ int to_acc(int v) { return v; }
 };
 
+// ---------------------------------------------------------------------------
+// Fused epilogue on one output element, in fp32 ("Tensor Cores, CUTLASS and
+// CuTe" sections 5 and 7): D = round_out(act(rs * cs * P + bias + C)), with
+// P the fp32 accumulator or the int32 one converted to fp32, absent scales
+// 1 and absent bias 0.  int32 output takes only + C (two's-complement
+// wrap-around).  One routine for every kernel, with contraction off, so the
+// kernels round identically.
+// ---------------------------------------------------------------------------
+struct EpiPtrs {
+    const float *rs, *cs, *bias; // this batch slice's vectors (NULL: absent)
+};
+
+// The tanh form of GELU, 0.5 x (1 + tanh u), written as the equal x / (1 + e^(-2u))
+// (the sum 1 + tanh u cancels for strongly negative u, the quotient does not),
+// with e^(-2u) = 2^(-2u log2 e) on the hardware base-2 exponential and the
+// quotient through the hardware reciprocal (each about 1 ulp; together a
+// relative error near 1e-6, against some 35 instructions for the library
+// exp and an IEEE division).  Strongly negative x: 2^(...) overflows to
+// +inf, its reciprocal is 0 and the result -0, which is also the rounded
+// value of the exact x / (1 + e^(-2u)) there.
+__device__ __forceinline__ float gelu_tanh(float x)
+{
+#pragma clang fp contract(off)
+    const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x); // sqrt(2/pi) (x + 0.044715 x^3)
+    const float t = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // -2 log2(e) u
+    return x * __builtin_amdgcn_rcpf(1.0f + t);
+}
+
+template <int O, class ST>
+__device__ __forceinline__ typename Out<O>::t epi_one(int epi, int act, ST v, float rsv, float csv, float bv,
+                                                      bool has_c, typename Out<O>::t c)
+{
+    if constexpr (O == I32) {
+        return has_c ? (int)((uint32_t)v + (uint32_t)c) : (int)v;
+    } else {
+#pragma clang fp contract(off)
+        float a = (float)v;
+        if (epi) {
+            a = a * rsv;
+            a = a * csv;
+            a = a + bv;
+        }
+        if (has_c)
+            a = a + Out<O>::to_acc(c);
+        if (act == 1)
+            a = a > 0.0f ? a : 0.0f;
+        else if (act == 2)
+            a = gelu_tanh(a);
+        return Out<O>::from_acc(a);
+    }
+}
+
 // Parameters shared by every GEMM kernel (per-launch, passed by value).
 struct GemmParams {
     const char *A;
@@ -158,6 +210,11 @@ struct GemmParams {
     int32_t a_kc, b_kc;                         // 1: operand is K-contiguous in memory
     int32_t d_vec4;                             // 1: 4-element vector access to C/D is legal
     int64_t a_bytes, b_bytes;                   // bytes spanned by one batch slice of A / B
+    // fused epilogue: D = act(rs(i) * cs(j) * P + bias(j) + C(i,j)); NULL vectors are absent
+    const float *rs, *cs, *bias;
+    int64_t stride_rs, stride_cs, stride_bias;  // floats between batch slices
+    int32_t act;                                // 0 none, 1 ReLU, 2 tanh-GELU
+    int32_t epi;                                // 1 if any of rs, cs, bias is present
 };
 
 // ---------------------------------------------------------------------------

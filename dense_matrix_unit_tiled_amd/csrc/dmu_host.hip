@@ -61,14 +61,19 @@ int combo_of(int in, int acc, int out)
     if (in == DMU_BF16 && acc == DMU_F32 && out == DMU_BF16) return 2;
     if (in == DMU_BF16 && acc == DMU_F32 && out == DMU_F32) return 3;
     if (in == DMU_I8 && acc == DMU_I32 && out == DMU_I32) return 4;
+    if (in == DMU_I8 && acc == DMU_I32 && out == DMU_F32) return 5;  // dequantising outputs
+    if (in == DMU_I8 && acc == DMU_I32 && out == DMU_F16) return 6;
+    if (in == DMU_I8 && acc == DMU_I32 && out == DMU_BF16) return 7;
     return -1;
 }
 
-const char *const COMBO_NAMES[] = {"f16_f32", "f16_f16", "bf16_bf16", "bf16_f32", "i8_i32"};
+constexpr int NUM_COMBOS = 8;
+const char *const COMBO_NAMES[NUM_COMBOS] = {"f16_f32", "f16_f16", "bf16_bf16", "bf16_f32",
+                                             "i8_i32",  "i8_f32",  "i8_f16",    "i8_bf16"};
 
 // Names of every kernel variant, built once (thread-safe static init).
 struct NameTable {
-    char at[NUM_TILE_CFGS][3][3][5][48];
+    char at[NUM_TILE_CFGS][3][3][NUM_COMBOS][48];
 };
 
 const NameTable &kernel_names()
@@ -80,7 +85,7 @@ const NameTable &kernel_names()
         for (int a = 0; a < NUM_TILE_CFGS; ++a)
             for (int x = 0; x < 3; ++x)
                 for (int y = 0; y < 3; ++y)
-                    for (int c = 0; c < 5; ++c)
+                    for (int c = 0; c < NUM_COMBOS; ++c)
                         snprintf(t.at[a][x][y][c], sizeof(t.at[a][x][y][c]), "mfma_%s_%s_%s_%s", TILE_NAMES[a],
                                  a == TILE_GENERIC ? "any" : MODE_NAMES[x], a == TILE_GENERIC ? "any" : MODE_NAMES[y],
                                  COMBO_NAMES[c]);
@@ -126,6 +131,8 @@ int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, in
         return MC16;
     return -1;
 }
+
+int validate_epilogue(const dmu_gemm_args *a, const dmu_epilogue *ep, Plan *plan);
 
 int validate(const dmu_gemm_args *a, Plan *plan)
 {
@@ -280,6 +287,60 @@ int validate(const dmu_gemm_args *a, Plan *plan)
     return DMU_OK;
 }
 
+// The fused epilogue's operands, checked after the product's (plan filled by validate).
+int validate_epilogue(const dmu_gemm_args *a, const dmu_epilogue *ep, Plan *plan)
+{
+    if (!ep)
+        return DMU_OK;
+    if (ep->act < DMU_ACT_NONE || ep->act > DMU_ACT_GELU_TANH) {
+        set_error("epilogue activation %d is not DMU_ACT_NONE, DMU_ACT_RELU or DMU_ACT_GELU_TANH", ep->act);
+        return DMU_ERR_INVALID_ARG;
+    }
+    const bool any = ep->row_scale || ep->col_scale || ep->bias || ep->act != DMU_ACT_NONE;
+    if (any && a->out_type == DMU_I32) {
+        set_error("int32 output takes no epilogue");
+        return DMU_ERR_UNSUPPORTED;
+    }
+    if (ep->stride_row_scale < 0 || ep->stride_col_scale < 0 || ep->stride_bias < 0) {
+        set_error("negative epilogue vector stride");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (((uintptr_t)ep->row_scale % 4) || ((uintptr_t)ep->col_scale % 4) || ((uintptr_t)ep->bias % 4)) {
+        set_error("epilogue vector not aligned to 4 bytes");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (plan->launch) { // vectors are inputs: they may not overlap the output
+        const int64_t batch = a->batch;
+        uintptr_t d0, d1;
+        span(a->D, batch > 1 ? a->stride_d : 0, batch, extent(DMU_ROW_MAJOR, a->M, a->N, a->ldd),
+             elem_bytes(a->out_type), &d0, &d1);
+        const struct { const float *v; int64_t stride, n; const char *what; } vecs[3] = {
+            {ep->row_scale, ep->stride_row_scale, a->M, "row_scale"},
+            {ep->col_scale, ep->stride_col_scale, a->N, "col_scale"},
+            {ep->bias, ep->stride_bias, a->N, "bias"}};
+        for (const auto &v : vecs) {
+            if (!v.v)
+                continue;
+            uintptr_t x0, x1;
+            span(v.v, batch > 1 ? v.stride : 0, batch, v.n, 4, &x0, &x1);
+            if (overlap(d0, d1, x0, x1)) {
+                set_error("epilogue %s overlaps D", v.what);
+                return DMU_ERR_INVALID_ARG;
+            }
+        }
+    }
+    GemmParams &p = plan->p;
+    p.rs = ep->row_scale;
+    p.cs = ep->col_scale;
+    p.bias = ep->bias;
+    p.stride_rs = a->batch > 1 ? ep->stride_row_scale : 0;
+    p.stride_cs = a->batch > 1 ? ep->stride_col_scale : 0;
+    p.stride_bias = a->batch > 1 ? ep->stride_bias : 0;
+    p.act = ep->act;
+    p.epi = (ep->row_scale || ep->col_scale || ep->bias) ? 1 : 0;
+    return DMU_OK;
+}
+
 } // namespace
 } // namespace dmu
 
@@ -301,11 +362,23 @@ extern "C" const char *dmu_gemm_kernel_name(const dmu_gemm_args *args)
     return plan.name;
 }
 
-extern "C" int dmu_gemm(const dmu_gemm_args *args, void *stream)
+extern "C" int dmu_gemm_ex_check(const dmu_gemm_args *args, const dmu_epilogue *ep)
 {
     clear_error();
     Plan plan;
     int rc = validate(args, &plan);
+    if (rc == DMU_OK)
+        rc = validate_epilogue(args, ep, &plan);
+    return rc;
+}
+
+extern "C" int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, void *stream)
+{
+    clear_error();
+    Plan plan;
+    int rc = validate(args, &plan);
+    if (rc == DMU_OK)
+        rc = validate_epilogue(args, ep, &plan);
     if (rc != DMU_OK || !plan.launch)
         return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -315,7 +388,10 @@ extern "C" int dmu_gemm(const dmu_gemm_args *args, void *stream)
     case 1: e = launch_f16_f16(plan.cfg, plan.p, s); break;
     case 2: e = launch_bf16_bf16(plan.cfg, plan.p, s); break;
     case 3: e = launch_bf16_f32(plan.cfg, plan.p, s); break;
-    default: e = launch_i8_i32(plan.cfg, plan.p, s); break;
+    case 4: e = launch_i8_i32(plan.cfg, plan.p, s); break;
+    case 5: e = launch_i8_f32(plan.cfg, plan.p, s); break;
+    case 6: e = launch_i8_f16(plan.cfg, plan.p, s); break;
+    default: e = launch_i8_bf16(plan.cfg, plan.p, s); break;
     }
     if (e != hipSuccess) {
         set_error("dmu_gemm: launch of %s failed: %s", plan.name, hipGetErrorString(e));
@@ -323,6 +399,8 @@ extern "C" int dmu_gemm(const dmu_gemm_args *args, void *stream)
     }
     return DMU_OK;
 }
+
+extern "C" int dmu_gemm(const dmu_gemm_args *args, void *stream) { return dmu_gemm_ex(args, nullptr, stream); }
 
 extern "C" const char *dmu_status_string(int status)
 {

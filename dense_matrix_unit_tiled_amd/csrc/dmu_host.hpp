@@ -40,5 +40,8 @@ hipError_t launch_f16_f16(const LaunchCfg &c, const GemmParams &p, hipStream_t s
 hipError_t launch_bf16_bf16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 hipError_t launch_bf16_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 hipError_t launch_i8_i32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_i8_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_i8_f16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_i8_bf16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 
 } // namespace dmu

@@ -51,7 +51,8 @@ __device__ __forceinline__ void generic_fill(char *tile, const char *base, int64
 
 // 64 x 64 tile, wavefront w owns the 32 x 32 block (w / 2, w % 2): 2 x 2 tiles
 // of 16 x 16, stored straight from the accumulators (lane l: row l % 16,
-// columns 4 (l / 16) .. +3 of each tile), masked at the M/N edges.
+// columns 4 (l / 16) .. +3 of each tile) through the same fused epilogue,
+// masked at the M/N edges.
 template <int T, int O>
 __global__ void __launch_bounds__(256) gemm_generic(GemmParams p)
 {
@@ -97,6 +98,7 @@ __global__ void __launch_bounds__(256) gemm_generic(GemmParams p)
     }
     const char *Cb = p.C ? p.C + (int64_t)tc.b * p.stride_c * dt_bytes(O) : nullptr;
     char *Db = p.D + (int64_t)tc.b * p.stride_d * dt_bytes(O);
+    const EpiPtrs ep = epi_ptrs(p, tc.b);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t m = m0 + wm * 32 + 16 * i + (lane & 15u);
@@ -108,14 +110,11 @@ __global__ void __launch_bounds__(256) gemm_generic(GemmParams p)
         for (int j = 0; j < 2; ++j) {
             const int64_t n = n0 + wn * 32 + 16 * j + 4 * (lane >> 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (n + e < p.N) {
-                    auto a = acc[i][j][e];
-                    if (Crow)
-                        a += Out<O>::to_acc(Crow[n + e]);
-                    Drow[n + e] = Out<O>::from_acc(a);
-                }
-            }
+            for (int e = 0; e < 4; ++e)
+                if (n + e < p.N)
+                    Drow[n + e] = epi_one<O>(p.epi, p.act, acc[i][j][e], ep.rs ? ep.rs[m] : 1.0f,
+                                             ep.cs ? ep.cs[n + e] : 1.0f, ep.bias ? ep.bias[n + e] : 0.0f,
+                                             Crow != nullptr, Crow ? Crow[n + e] : ot{});
         }
     }
 }

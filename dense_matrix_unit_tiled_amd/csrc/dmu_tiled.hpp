@@ -200,12 +200,13 @@ template <int R, int NW> struct TileOf<MC16, R, NW> { typedef McTile<R, NW> type
 // Epilogue through LDS for 16 x 16 tiles: each 16-row stripe of the
 // wavefront's results is parked in its own LDS area and read back
 // row-contiguous, so that every store instruction writes whole rows of 16 NT
-// values (C added, RNE conversion, M/N masking on the way out).
+// values, with the fused epilogue (scales, bias, C, activation), RNE
+// conversion and M/N masking on the way out.
 // ---------------------------------------------------------------------------
 template <int O, int MT, int NT, class AccT>
 __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&acc)[MT][NT], char *lds,
-                                               int64_t m_base, int64_t n_base, uint32_t lane, const char *Cb,
-                                               char *Db)
+                                             int64_t m_base, int64_t n_base, uint32_t lane, const char *Cb,
+                                             char *Db, const EpiPtrs &ep)
 {
     typedef typename Out<O>::t ot;
     typedef decltype(acc[0][0][0]) sref;
@@ -215,6 +216,29 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
     constexpr int COLS = 16 * NT;
     constexpr int PITCH = COLS * 4 + 16; // bytes per parked row (+16 spreads rows over the banks)
     constexpr int LPR = COLS / 4;        // lanes per row on the way out
+    constexpr int RPI = 64 / LPR;        // rows per store instruction
+    constexpr int ITS = 16 / RPI;        // store instructions per 16-row stripe
+    // On the way out lane l always handles the same four columns (n_base +
+    // 4 (l % LPR) ..) and, in stripe mi and store it, row 16 mi + RPI it + l / LPR:
+    // its epilogue operands are fetched once, up front, instead of in the
+    // store loop (where every fetch would stall the loop).
+    float rsv[MT][ITS], csv[4], bv[4];
+    {
+        const int64_t n0 = n_base + 4 * (lane % LPR);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool in = n0 + e < p.N;
+            csv[e] = ep.cs && in ? ep.cs[n0 + e] : 1.0f;
+            bv[e] = ep.bias && in ? ep.bias[n0 + e] : 0.0f;
+        }
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int it = 0; it < ITS; ++it) {
+                const int64_t m = m_base + mi * 16 + RPI * it + lane / LPR;
+                rsv[mi][it] = ep.rs && m < p.M ? ep.rs[m] : 1.0f;
+            }
+    }
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
@@ -226,9 +250,8 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
             *reinterpret_cast<st4 *>(lds + (lane & 15u) * PITCH + (ni * 16 + 4 * (lane >> 4)) * 4) = v;
         }
 #pragma unroll
-        for (int it = 0; it < 16 * LPR / 64; ++it) {
-            const uint32_t idx = it * 64 + lane;
-            const uint32_t row = idx / LPR, col = (idx % LPR) * 4;
+        for (int it = 0; it < ITS; ++it) {
+            const uint32_t row = RPI * it + lane / LPR, col = (lane % LPR) * 4;
             const st4 v = *reinterpret_cast<const st4 *>(lds + row * PITCH + col * 4);
             const int64_t m = m_base + mi * 16 + row, n = n_base + col;
             if (m >= p.M)
@@ -236,36 +259,32 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
             const ot *Crow = Cb ? reinterpret_cast<const ot *>(Cb) + m * p.ldc : nullptr;
             ot *Drow = reinterpret_cast<ot *>(Db) + m * p.ldd;
             if (p.d_vec4 && n + 3 < p.N) {
-                ov4 o;
-                if (Crow) {
-                    const ov4 c = *reinterpret_cast<const ov4 *>(Crow + n);
+                ov4 c = {}, o;
+                if (Crow)
+                    c = *reinterpret_cast<const ov4 *>(Crow + n);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        st a = v[e];
-                        a += Out<O>::to_acc(c[e]);
-                        o[e] = Out<O>::from_acc(a);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        st a = v[e];
-                        o[e] = Out<O>::from_acc(a);
-                    }
-                }
+                for (int e = 0; e < 4; ++e)
+                    o[e] = epi_one<O>(p.epi, p.act, v[e], rsv[mi][it], csv[e], bv[e], Crow != nullptr, c[e]);
                 *reinterpret_cast<ov4 *>(Drow + n) = o;
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (n + e < p.N) {
-                        st a = v[e];
-                        if (Crow)
-                            a += Out<O>::to_acc(Crow[n + e]);
-                        Drow[n + e] = Out<O>::from_acc(a);
-                    }
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < p.N)
+                        Drow[n + e] = epi_one<O>(p.epi, p.act, v[e], rsv[mi][it], csv[e], bv[e], Crow != nullptr,
+                                                 Crow ? Crow[n + e] : ot{});
             }
         }
     }
+}
+
+// This batch slice's epilogue vectors.
+__device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams &p, int64_t b)
+{
+    EpiPtrs e;
+    e.rs = p.rs ? p.rs + b * p.stride_rs : nullptr;
+    e.cs = p.cs ? p.cs + b * p.stride_cs : nullptr;
+    e.bias = p.bias ? p.bias + b * p.stride_bias : nullptr;
+    return e;
 }
 
 template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
@@ -448,7 +467,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     constexpr int PARK = 16 * (16 * NT * 4 + 16);
     static_assert(NW * PARK <= 2 * STAGE, "parking area fits in the stages");
     store_staged<O, MT, NT>(p, acc, smem + wave2 * PARK, (int64_t)te.tm * BM + (wave2 / WGN) * WTM,
-                              (int64_t)te.tn * BN + (wave2 % WGN) * WTN, lane2, Cb, Db);
+                            (int64_t)te.tn * BN + (wave2 % WGN) * WTN, lane2, Cb, Db, epi_ptrs(p, te.b));
 }
 
 } // namespace dmu

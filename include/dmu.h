@@ -70,6 +70,11 @@ typedef enum {
  *  out_type         type of C and D.  Supported (in, acc, out) triples:
  *                     (F16,F32,F32) (F16,F32,F16) (F16,F16,F16)
  *                     (BF16,F32,BF16) (BF16,F32,F32) (I8,I32,I32)
+ *                     (I8,I32,F32) (I8,I32,F16) (I8,I32,BF16)
+ *                   The last three dequantise: the int32 sum is converted
+ *                   to fp32 (round to nearest even), goes through the
+ *                   optional epilogue of dmu_gemm_ex in fp32, and is rounded
+ *                   to the output type.
  *                   For acc_type == DMU_F16 the matrix cores still sum the
  *                   exact products in fp32 and the result is rounded once to
  *                   fp16 (gfx950 has no fp16-accumulating matrix
@@ -118,6 +123,50 @@ typedef struct dmu_gemm_args {
  * is written to D when an error is returned before the launch.
  */
 int dmu_gemm(const dmu_gemm_args *args, void *stream);
+
+/*
+ * Fused epilogue ("Tensor Cores, CUTLASS and CuTe", section 5: the scaled-mm
+ * epilogue multiplies the accumulator by a per-column and a per-row scale
+ * before the output conversion, as for int8 dequantisation; section 7: the
+ * bias + activation epilogue of a fused linear layer).  With P the product sum
+ * (the fp32 accumulator, or the int32 one converted to fp32):
+ *
+ *     D[b](i,j) = round_out( act( rs[b](i) * cs[b](j) * P + bias[b](j) + C[b](i,j) ) )
+ *
+ * evaluated in fp32 in that order and rounded once to the output type.
+ *
+ *  row_scale        M floats per batch slice (NULL: 1); slice b starts at
+ *                   row_scale + b * stride_row_scale (stride >= 0, 0 shares
+ *                   one vector across batches).
+ *  col_scale        N floats per batch slice (NULL: 1), likewise.
+ *  bias             N floats per batch slice (NULL: 0), likewise.
+ *  act              DMU_ACT_NONE, DMU_ACT_RELU (x > 0 ? x : +0) or
+ *                   DMU_ACT_GELU_TANH (0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3)))).
+ *
+ * Vectors are device pointers aligned to 4 bytes, read only, and may not
+ * overlap D.  int32 output takes no epilogue (DMU_ERR_UNSUPPORTED).
+ */
+enum { DMU_ACT_NONE = 0, DMU_ACT_RELU = 1, DMU_ACT_GELU_TANH = 2 };
+
+typedef struct dmu_epilogue {
+    const float *row_scale;
+    int64_t stride_row_scale;
+    const float *col_scale;
+    int64_t stride_col_scale;
+    const float *bias;
+    int64_t stride_bias;
+    int32_t act;
+} dmu_epilogue;
+
+/*
+ * D = epilogue(A*B + C) as described above, on `stream`; `ep` may be NULL (then
+ * exactly dmu_gemm).  Errors as for dmu_gemm, plus DMU_ERR_INVALID_ARG for a bad
+ * activation, a negative stride, a misaligned vector or one that overlaps D.
+ */
+int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, void *stream);
+
+/* Validate `args` and `ep` exactly as dmu_gemm_ex does, without touching the GPU. */
+int dmu_gemm_ex_check(const dmu_gemm_args *args, const dmu_epilogue *ep);
 
 /*
  * Validate `args` exactly as dmu_gemm does, without touching the GPU.

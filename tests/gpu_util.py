@@ -77,10 +77,12 @@ class force_kernel:
             os.environ["DMU_FORCE_KERNEL"] = self.old
 
 
-def run_dmu(p, force=None, fill=None, return_name=False):
-    """Run one workload on the GPU through dmu_gemm; D as raw bits (oracle format).
+def run_dmu(p, force=None, fill=None, return_name=False, ep=None, in_place=False):
+    """Run one workload on the GPU through dmu_gemm (dmu_gemm_ex when an epilogue
+    ``ep`` is given); D as raw bits (oracle format).
 
     fill: optional bit pattern written to D before the call (to see untouched cells).
+    in_place: D starts as a copy of C and the call passes C == D.
     """
     torch = _torch()
     dA, dB = to_dev(p.A), to_dev(p.B)
@@ -89,28 +91,83 @@ def run_dmu(p, force=None, fill=None, return_name=False):
     dD = torch.zeros(n, dtype=out_dtype(p.out_type), device="cuda:0")
     if fill is not None:
         dD.fill_(fill)
+    if in_place:
+        assert p.C is not None and p.ldc == p.ldd and p.stride_c == p.stride_d
+        dD[: dC.numel()].copy_(dC)
+        dC = dD
     args = make_args(p, dA, dB, dD, dC)
+    keep = []
     with force_kernel(force):
         name = dmu.dmu_gemm_kernel_name(args)
-        dmu.dmu_gemm(args)
+        if ep is None:
+            dmu.dmu_gemm(args)
+        else:
+            vec = lambda x: None if x is None else keep.append(to_dev(x)) or keep[-1]
+            e = dmu.epilogue_args(row_scale=vec(ep.row_scale), stride_row_scale=ep.stride_rs,
+                                  col_scale=vec(ep.col_scale), stride_col_scale=ep.stride_cs,
+                                  bias=vec(ep.bias), stride_bias=ep.stride_bias, act=ep.act)
+            dmu.dmu_gemm_ex(args, e)
     torch.cuda.synchronize()
     out = from_dev(dD, p.out_type)[: p.batch * p.stride_d]
     return (out, name) if return_name else out
 
 
-def run_oracle(p, nthreads=None):
+def run_oracle(p, nthreads=None, ep=None):
     return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, in_type=p.in_type,
                        out_type=p.out_type, layout_a=p.layout_a, layout_b=p.layout_b,
                        batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, C=p.C,
                        ldc=p.ldc, stride_c=p.stride_c, ldd=p.ldd, stride_d=p.stride_d,
-                       nthreads=nthreads)
+                       nthreads=nthreads, **(ep.kwargs() if ep is not None else {}))
 
 
-def oracle_at(p, bij):
+def oracle_at(p, bij, ep=None):
     return oracle.gemm_at(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, bij, in_type=p.in_type,
                           out_type=p.out_type, layout_a=p.layout_a, layout_b=p.layout_b,
                           batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, C=p.C,
-                          ldc=p.ldc, stride_c=p.stride_c)
+                          ldc=p.ldc, stride_c=p.stride_c, **(ep.kwargs() if ep is not None else {}))
+
+
+def product_at(p, bij):
+    """|P| (the plain product, no C, no epilogue) at (b, i, j), from the oracle in fp64 terms."""
+    q_out = "f32"
+    return np.abs(oracle.gemm_at(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, bij, in_type=p.in_type,
+                                 out_type=q_out, layout_a=p.layout_a, layout_b=p.layout_b,
+                                 batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b).astype(np.float64))
+
+
+def assert_close_epilogue(got: np.ndarray, want: np.ndarray, p, ep, bij: np.ndarray):
+    """The parity bar with a fused epilogue, at the elements (b, i, j) of ``bij`` (got/want
+    hold those elements).  The product's bound moves through the scales, the epilogue's
+    fp32 steps add a relative 1e-5 of the magnitudes summed, the activation is at most
+    1.2-Lipschitz, and a 16-bit output adds its 2e-2 relative allowance:
+      |D - ref| <= 1.2 (e_P |rs_i cs_j| + 1e-5 (|rs_i cs_j P_ij| + |bias_j| + |C_ij|)) [+ 2e-2 |ref|]
+    with e_P = 1e-3 sqrt(K) max|A| max|B| for fp16/bf16 inputs and 0 for int8 (exact sums)."""
+    b, i, j = bij[:, 0], bij[:, 1], bij[:, 2]
+    rs = ep.row_scale[b * ep.stride_rs + i].astype(np.float64) if ep.row_scale is not None else 1.0
+    cs = ep.col_scale[b * ep.stride_cs + j].astype(np.float64) if ep.col_scale is not None else 1.0
+    bias = np.abs(ep.bias[b * ep.stride_bias + j].astype(np.float64)) if ep.bias is not None else 0.0
+    cmag = np.abs(values(p.C[b * p.stride_c + i * p.ldc + j], p.out_type)) if p.C is not None else 0.0
+    P = product_at(p, bij)
+    if p.in_type == "i8":
+        e_p = 0.0
+    else:
+        amax, bmax = input_absmax(p)
+        e_p = 1e-3 * math.sqrt(max(p.K, 1)) * amax * bmax
+    s = np.abs(rs * cs)
+    tol = 1.2 * (e_p * s + 1e-5 * (s * P + bias + cmag)) + 1e-30
+    g, w = values(got, p.out_type), values(want, p.out_type)
+    if p.out_type != "f32":
+        tol = tol + 2e-2 * np.abs(w)
+    err = np.abs(g - w)
+    bad = np.nonzero(~(err <= tol))[0]
+    assert bad.size == 0, (f"{bad.size}/{g.size} outside tolerance; first {bad[:5]} at {bij[bad[:5]].tolist()}: "
+                           f"got {g[bad[:5]]} want {w[bad[:5]]} tol {np.broadcast_to(tol, g.shape)[bad[:5]]}")
+
+
+def all_bij(p) -> np.ndarray:
+    """Every (b, i, j) of the product, in the order of the flat D buffer's valid cells."""
+    b, i, j = np.meshgrid(np.arange(p.batch), np.arange(p.M), np.arange(p.N), indexing="ij")
+    return np.stack([b.ravel(), i.ravel(), j.ravel()], axis=1).astype(np.int64)
 
 
 def values(bits: np.ndarray, t: str) -> np.ndarray:

@@ -31,6 +31,9 @@ def test_struct_layout_matches_header():
     # 4 int64 + 5 int32 (+4 pad) + 4 x (pointer + 2 int64)
     assert ctypes.sizeof(dmu.dmu_gemm_args) == 32 + 24 + 4 * 24
     assert dmu.dmu_gemm_args.A.offset == 56
+    # 3 x (pointer + int64) + int32 (+4 pad)
+    assert ctypes.sizeof(dmu.dmu_epilogue) == 3 * 16 + 8
+    assert dmu.dmu_epilogue.act.offset == 48
 
 
 FAKE = 1 << 40  # device-looking addresses; never dereferenced by validation
@@ -57,7 +60,8 @@ def test_valid_arguments_pass():
     (dict(A=None), dmu.DMU_ERR_INVALID_ARG),
     (dict(D=None), dmu.DMU_ERR_INVALID_ARG),
     (dict(out_type="i32"), dmu.DMU_ERR_UNSUPPORTED),
-    (dict(in_type="i8", out_type="f32"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(in_type="i8", out_type="f32", acc_type="f32"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(in_type="i8", out_type="i32", acc_type="f32"), dmu.DMU_ERR_UNSUPPORTED),
     (dict(in_type="f32", out_type="f32"), dmu.DMU_ERR_UNSUPPORTED),
     (dict(in_type="bf16", out_type="f16"), dmu.DMU_ERR_UNSUPPORTED),
     (dict(D=FAKE + 100), dmu.DMU_ERR_INVALID_ARG),                 # D overlaps A
@@ -132,3 +136,53 @@ def test_probe_info():
         dmu.dmu_probe_info(999)
     with pytest.raises(dmu.DmuError):
         dmu.dmu_probe(dmu.DMU_PROBE_MFMA_32x32x16_BF16, None, None, None, stream=0)
+
+
+def ep(**kw):
+    base = dict(row_scale=FAKE + (3 << 30), col_scale=FAKE + (3 << 30) + 4096, bias=FAKE + (3 << 30) + 8192,
+                act="gelu_tanh")
+    base.update(kw)
+    return dmu.epilogue_args(**base)
+
+
+@pytest.mark.parametrize("in_t,out_t", [("f16", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "f32"),
+                                        ("i8", "f32"), ("i8", "f16"), ("i8", "bf16")])
+def test_epilogue_valid(in_t, out_t):
+    a = args(in_type=in_t, out_type=out_t)
+    assert dmu.dmu_gemm_ex_check(a, ep()) == dmu.DMU_OK
+    assert dmu.dmu_gemm_ex_check(a, None) == dmu.DMU_OK
+    assert dmu.dmu_gemm_ex_check(a, ep(row_scale=None, col_scale=None, bias=None, act="relu")) == dmu.DMU_OK
+    # batched, broadcast (stride 0) and strided vectors
+    b = args(in_type=in_t, out_type=out_t, batch=3, stride_d=256 * 256, stride_a=0, stride_b=0)
+    assert dmu.dmu_gemm_ex_check(b, ep(stride_row_scale=300, stride_col_scale=0, stride_bias=260)) == dmu.DMU_OK
+
+
+@pytest.mark.parametrize("kw,akw,status", [
+    (dict(act=3), {}, dmu.DMU_ERR_INVALID_ARG),
+    (dict(act=-1), {}, dmu.DMU_ERR_INVALID_ARG),
+    (dict(stride_bias=-1), {}, dmu.DMU_ERR_INVALID_ARG),
+    (dict(col_scale=FAKE + (3 << 30) + 2), {}, dmu.DMU_ERR_INVALID_ARG),          # misaligned
+    (dict(bias=FAKE + (2 << 30) + 64), {}, dmu.DMU_ERR_INVALID_ARG),               # bias inside D
+    (dict(), dict(in_type="i8", out_type="i32"), dmu.DMU_ERR_UNSUPPORTED),        # int32 takes no epilogue
+    (dict(row_scale=None, col_scale=None, bias=None, act="relu"), dict(in_type="i8", out_type="i32"),
+     dmu.DMU_ERR_UNSUPPORTED),
+])
+def test_epilogue_rejections(kw, akw, status):
+    a = args(**akw)
+    e = ep(**kw)
+    assert dmu.dmu_gemm_ex_check(a, e) == status
+    assert dmu.dmu_last_error() != ""
+    with pytest.raises(dmu.DmuError) as err:
+        dmu.dmu_gemm_ex(a, e, stream=0)  # rejected before any HIP call
+    assert err.value.status == status
+
+
+def test_int32_output_takes_empty_epilogue():
+    a = args(in_type="i8", out_type="i32")
+    assert dmu.dmu_gemm_ex_check(a, dmu.epilogue_args()) == dmu.DMU_OK
+
+
+@pytest.mark.parametrize("out_t", ["f32", "f16", "bf16"])
+def test_dequantising_kernel_names(out_t):
+    a = args(in_type="i8", out_type=out_t, K=512, lda=512, ldb=512, layout_b="col")
+    assert dmu.dmu_gemm_kernel_name(a).endswith(f"i8_{out_t}")
