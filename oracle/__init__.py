@@ -1,4 +1,5 @@
-"""CPU oracle for D = A*B + C (ctypes binding of ``oracle/oracle.c``).
+"""CPU oracle for D = A*B + C and for attention, O = softmax(scale Q K^T) V
+(ctypes binding of ``oracle/oracle.c``).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` import this package.  The GPU library and its
@@ -44,6 +45,11 @@ def _load():
     lib.oracle_gemm_ex.restype = i32
     lib.oracle_gemm_at_ex.argtypes = common + ep + [i64, vp, vp]
     lib.oracle_gemm_at_ex.restype = i32
+    att = [i64, i64, i64, i64, i64, i32, i32, ctypes.c_double, vp, i64, i64, vp, i64, i64, vp, i64, i64]
+    lib.oracle_attention.argtypes = att + [vp, i64, i64, i32]
+    lib.oracle_attention.restype = i32
+    lib.oracle_attention_rows.argtypes = att + [i64, vp, vp, i32]
+    lib.oracle_attention_rows.restype = i32
     lib.oracle_decode_array.argtypes = [i32, vp, vp, i64]
     lib.oracle_decode_array.restype = None
     lib.oracle_encode_array.argtypes = [i32, vp, vp, i64]
@@ -164,3 +170,44 @@ def encode(t: str, values) -> np.ndarray:
     out = np.empty(values.size, dtype=np.uint32 if t == "f32" else np.uint16)
     _load().oracle_encode_array(TYPES[t], _ptr(values), _ptr(out), values.size)
     return out.view(np.float32) if t == "f32" else out
+
+
+def _att_common(batch, sq, sk, d, dv, Q, ldq, stride_q, K, ldk, stride_k, V, ldv, stride_v, in_type, out_type,
+                scale):
+    span = lambda s_, rows, ld, cols: 0 if batch == 0 or rows == 0 else (batch - 1) * s_ + (rows - 1) * ld + cols
+    Q = _prep(Q, in_type, span(stride_q, sq, ldq, d), "Q")
+    K = _prep(K, in_type, span(stride_k, sk, ldk, d), "K")
+    V = _prep(V, in_type, span(stride_v, sk, ldv, dv), "V")
+    # the softmax scale is an fp32 number on the GPU side; the oracle takes that same value
+    args = (batch, sq, sk, d, dv, TYPES[in_type], TYPES[out_type], float(np.float32(scale)), _ptr(Q), ldq, stride_q,
+            _ptr(K), ldk, stride_k, _ptr(V), ldv, stride_v)
+    return args, (Q, K, V)
+
+
+def attention(batch, sq, sk, d, dv, Q, ldq, stride_q, K, ldk, stride_k, V, ldv, stride_v, *, in_type, out_type,
+              scale, ldo=None, stride_o=None, nthreads=None):
+    """O = softmax(scale * Q K^T) V for every row (flat, batch*stride_o elements of out_type bits)."""
+    ldo = dv if ldo is None else ldo
+    stride_o = sq * ldo if stride_o is None else stride_o
+    args, keep = _att_common(batch, sq, sk, d, dv, Q, ldq, stride_q, K, ldk, stride_k, V, ldv, stride_v,
+                             in_type, out_type, scale)
+    O = np.zeros(max(batch * stride_o, 1), dtype=_NP_IN[out_type])
+    st = _load().oracle_attention(*args, _ptr(O), ldo, stride_o, nthreads or default_threads())
+    if st:
+        raise ValueError(f"oracle_attention rejected its arguments (code {st})")
+    del keep
+    return O[: batch * stride_o]
+
+
+def attention_rows(batch, sq, sk, d, dv, Q, ldq, stride_q, K, ldk, stride_k, V, ldv, stride_v, rows, *,
+                   in_type, out_type, scale, nthreads=None):
+    """Rows (b, i) of O (``rows`` shape [n, 2]) as an [n, dv] array of out_type bits."""
+    args, keep = _att_common(batch, sq, sk, d, dv, Q, ldq, stride_q, K, ldk, stride_k, V, ldv, stride_v,
+                             in_type, out_type, scale)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+    out = np.zeros(max(len(rows) * dv, 1), dtype=_NP_IN[out_type])
+    st = _load().oracle_attention_rows(*args, len(rows), _ptr(rows), _ptr(out), nthreads or default_threads())
+    if st:
+        raise ValueError(f"oracle_attention_rows rejected its arguments (code {st})")
+    del keep
+    return out[: len(rows) * dv].reshape(len(rows), dv)

@@ -54,6 +54,10 @@
  *   A is logical M x K, B is logical K x N; C and D are row-major M x N.
  *   Batch b adds b*stride_* to each base.
  *
+ * The file also holds the attention forward O = softmax(scale Q K^T) V (see
+ * oracle_attention below), evaluated the same way: exact fp64 inputs, fp64
+ * sums in index order, one rounding of each output.
+ *
  * Parity pins for this file live in tests/test_oracle_*.py.
  */
 #include <math.h>
@@ -461,4 +465,180 @@ int oracle_gemm_at(ORACLE_ARGS, int64_t nsample, const int64_t *bij, void *out)
     return oracle_gemm_at_ex(M, N, K, batch, in_type, out_type, layout_a, layout_b, A, lda, stride_a, B,
                              ldb, stride_b, C, ldc, stride_c, NULL, 0, NULL, 0, NULL, 0, OR_ACT_NONE,
                              nsample, bij, out);
+}
+
+/* ------------------------------------------------------------------ */
+/* Attention forward                                                   */
+/* ------------------------------------------------------------------ */
+
+/*
+ * O = softmax(scale * Q K^T) V, one batch slice at a time: the computation
+ * whose two products the pages move onto the matrix units (layout-experiment
+ * post, sections 1-2: S = QK^T and O = PV of a FlashAttention kernel, with the
+ * elementwise exp taking S to P in between; "Tensor Cores, CUTLASS and CuTe",
+ * part 3 section 2: the softmax of each row of S = QK^T needs that row's max
+ * and sum, and P = softmax(S) feeds O = P V).
+ *
+ * Q is seq_q x d, K is seq_k x d, V is seq_k x dv, O is seq_q x dv, all
+ * row-major with the given leading dimensions and batch strides (elements).
+ * For query row i, in fp64 over the exact input values:
+ *
+ *     s_j = scale * sum_{t<d} Q(i,t) K(j,t)          (t in increasing order)
+ *     m   = max_j s_j
+ *     w_j = exp(s_j - m)                              (the largest weight is 1)
+ *     O(i,c) = (sum_{j<seq_k} w_j V(j,c)) / (sum_{j<seq_k} w_j)
+ *
+ * rounded once to out_type.  Subtracting the row maximum does not change the
+ * quotient; it keeps every exp at most 1.  seq_k == 0 leaves O undefined and is
+ * rejected.
+ */
+typedef struct {
+    int64_t batch, sq, sk, d, dv;
+    int in_type, out_type;
+    double scale;
+    const void *Q; int64_t ldq, stride_q;
+    const void *K; int64_t ldk, stride_k;
+    const void *V; int64_t ldv, stride_v;
+    void *O; int64_t ldo, stride_o;
+    const int64_t *rows; /* selected (b, i) pairs, or NULL for all rows */
+    int64_t begin, end;  /* work split over the row list */
+    int status;
+} att_t;
+
+static void attention_row(const att_t *a, int64_t b, int64_t i, double *s, double *acc, int64_t out_row)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < a->sk; ++j) {
+        double dot = 0.0;
+        for (int64_t t = 0; t < a->d; ++t)
+            dot += load_fp(a->Q, a->in_type, b * a->stride_q + i * a->ldq + t) *
+                   load_fp(a->K, a->in_type, b * a->stride_k + j * a->ldk + t);
+        s[j] = a->scale * dot;
+        if (s[j] > m)
+            m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t c = 0; c < a->dv; ++c)
+        acc[c] = 0.0;
+    for (int64_t j = 0; j < a->sk; ++j) {
+        const double w = exp(s[j] - m);
+        l += w;
+        for (int64_t c = 0; c < a->dv; ++c)
+            acc[c] += w * load_fp(a->V, a->in_type, b * a->stride_v + j * a->ldv + c);
+    }
+    for (int64_t c = 0; c < a->dv; ++c)
+        store_out(a->O, a->out_type, out_row + c, acc[c] / l);
+}
+
+static void *attention_rows(void *arg)
+{
+    att_t *a = (att_t *)arg;
+    double *s = (double *)malloc((size_t)a->sk * sizeof(double));
+    double *acc = (double *)malloc((size_t)(a->dv ? a->dv : 1) * sizeof(double));
+    if (!s || !acc) {
+        a->status = 4;
+        free(s);
+        free(acc);
+        return NULL;
+    }
+    for (int64_t r = a->begin; r < a->end; ++r) {
+        int64_t b, i, out_row;
+        if (a->rows) { /* selected rows: output row r of a dense [n][dv] array */
+            b = a->rows[2 * r];
+            i = a->rows[2 * r + 1];
+            out_row = r * a->dv;
+        } else {
+            b = r / a->sq;
+            i = r % a->sq;
+            out_row = b * a->stride_o + i * a->ldo;
+        }
+        attention_row(a, b, i, s, acc, out_row);
+    }
+    free(s);
+    free(acc);
+    return NULL;
+}
+
+static int attention_run(att_t *base, int64_t nrows, int nthreads)
+{
+    if (base->batch < 0 || base->sq < 0 || base->sk <= 0 || base->d < 0 || base->dv < 0)
+        return 1;
+    if ((base->in_type != OR_F16 && base->in_type != OR_BF16 && base->in_type != OR_F32) ||
+        (base->out_type != OR_F16 && base->out_type != OR_BF16 && base->out_type != OR_F32))
+        return 2;
+    if (nrows == 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nrows)
+        nthreads = (int)nrows;
+    att_t *jobs = (att_t *)calloc((size_t)nthreads, sizeof(att_t));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return 4;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *base;
+        jobs[t].begin = nrows * t / nthreads;
+        jobs[t].end = nrows * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&tids[t], NULL, attention_rows, &jobs[t]) != 0)
+            jobs[t].status = -1;
+    attention_rows(&jobs[0]);
+    int st = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (jobs[t].status == -1) {
+            jobs[t].status = 0;
+            attention_rows(&jobs[t]);
+        } else {
+            pthread_join(tids[t], NULL);
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (jobs[t].status)
+            st = jobs[t].status;
+    free(jobs);
+    free(tids);
+    return st;
+}
+
+#define ATTENTION_ARGS                                                                              \
+    int64_t batch, int64_t sq, int64_t sk, int64_t d, int64_t dv, int in_type, int out_type,          \
+        double scale, const void *Q, int64_t ldq, int64_t stride_q, const void *K, int64_t ldk,       \
+        int64_t stride_k, const void *V, int64_t ldv, int64_t stride_v
+
+static att_t make_att(ATTENTION_ARGS)
+{
+    att_t a;
+    memset(&a, 0, sizeof(a));
+    a.batch = batch; a.sq = sq; a.sk = sk; a.d = d; a.dv = dv;
+    a.in_type = in_type; a.out_type = out_type; a.scale = scale;
+    a.Q = Q; a.ldq = ldq; a.stride_q = stride_q;
+    a.K = K; a.ldk = ldk; a.stride_k = stride_k;
+    a.V = V; a.ldv = ldv; a.stride_v = stride_v;
+    return a;
+}
+
+/* Every row of O. */
+int oracle_attention(ATTENTION_ARGS, void *O, int64_t ldo, int64_t stride_o, int nthreads)
+{
+    att_t a = make_att(batch, sq, sk, d, dv, in_type, out_type, scale, Q, ldq, stride_q, K, ldk, stride_k, V,
+                       ldv, stride_v);
+    a.O = O; a.ldo = ldo; a.stride_o = stride_o;
+    return attention_run(&a, batch * sq, nthreads);
+}
+
+/* Selected rows: out[r][0..dv) = O[b](i, .) for (b, i) = rows[2r], rows[2r+1]. */
+int oracle_attention_rows(ATTENTION_ARGS, int64_t nrows, const int64_t *rows, void *out, int nthreads)
+{
+    att_t a = make_att(batch, sq, sk, d, dv, in_type, out_type, scale, Q, ldq, stride_q, K, ldk, stride_k, V,
+                       ldv, stride_v);
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[2 * r] < 0 || rows[2 * r] >= batch || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= sq)
+            return 5;
+    a.O = out; a.rows = rows;
+    return attention_run(&a, nrows, nthreads);
 }

@@ -4,7 +4,7 @@ Each case below plants one mistake in a copy of ``oracle/oracle.c`` (a dropped
 term, a wrong sign, index or stride, a transposed operand, a wrong rounding
 rule, a wrong codec constant), builds that copy into a temporary library, and
 runs the oracle pin suite (tests/test_oracle_gemm.py, tests/test_oracle_codecs.py,
-tests/test_oracle_epilogue.py)
+tests/test_oracle_epilogue.py, tests/test_oracle_attention.py)
 against it in a child process.  The suite must fail for every mutant; a mutant
 that survives is a mistake the pins would not see.
 """
@@ -77,6 +77,18 @@ MUTANTS = [
     ("int32 saturates", "static int32_t wrap_i32(int64_t v) { return (int32_t)(uint32_t)(uint64_t)v; }",
      "static int32_t wrap_i32(int64_t v) { return v > INT32_MAX ? INT32_MAX : "
      "(v < INT32_MIN ? INT32_MIN : (int32_t)v); }"),
+    ("attention: K indexed (d, key)", "b * a->stride_k + j * a->ldk + t", "b * a->stride_k + t * a->ldk + j"),
+    ("attention: batch stride of V ignored", "b * a->stride_v + j * a->ldv + c", "0 * a->stride_v + j * a->ldv + c"),
+    ("attention: last key dropped", "for (int64_t j = 0; j < a->sk; ++j) {\n        const double w",
+     "for (int64_t j = 0; j + 1 < a->sk; ++j) {\n        const double w"),
+    ("attention: last score term dropped", "for (int64_t t = 0; t < a->d; ++t)", "for (int64_t t = 0; t + 1 < a->d; ++t)"),
+    ("attention: not normalised", "acc[c] / l);", "acc[c]);"),
+    ("attention: scale applied twice", "s[j] = a->scale * dot;", "s[j] = a->scale * a->scale * dot;"),
+    ("attention: row maximum not subtracted", "const double w = exp(s[j] - m);", "const double w = exp(s[j]);"),
+    ("attention: first score as the maximum", "if (s[j] > m)\n            m = s[j];",
+     "if (j == 0)\n            m = s[j];"),
+    ("attention: ldo taken as dv", "out_row = b * a->stride_o + i * a->ldo;", "out_row = b * a->stride_o + i * a->dv;"),
+    ("attention: selected rows map to the wrong query", "i = a->rows[2 * r + 1];", "i = a->rows[2 * r];"),
 ]
 
 RUNNER = (
@@ -84,7 +96,7 @@ RUNNER = (
     "oracle.LIB_PATH = sys.argv[1]\n"
     "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '--no-header',\n"
     "                      'tests/test_oracle_gemm.py', 'tests/test_oracle_codecs.py',\n"
-    "                      'tests/test_oracle_epilogue.py']))\n"
+    "                      'tests/test_oracle_epilogue.py', 'tests/test_oracle_attention.py']))\n"
 )
 
 
