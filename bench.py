@@ -11,7 +11,7 @@ measures that ramp instead of the kernel.  Prints one JSON
 line with the throughput, the MFMA roofline of the kernel and the CPU oracle's
 rate on a bounded row slice of the same product.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c4fa]
                   [--no-cpu-baseline] [--copy-calibration MiB]
   python bench.py --summarize DIR [--workload W]   (rocprofv3 output -> profiles/)
 """
@@ -41,6 +41,10 @@ WORKLOAD_NAMES = {
     "c5": "gemm_8192x8192x8192_i8_tn_i32out",
     "c5dq": "gemm_8192x8192x8192_i8_tn_dequant_rowcol_scale_bias_gelu_bf16out",
 }
+
+# Fused attention (dmu_attention): batch, seq_q, seq_k, head_dim, in type, out type.
+ATTENTION_WORKLOADS = {"c4fa": (32, 4096, 4096, 128, "f16", "f32")}
+WORKLOAD_NAMES["c4fa"] = "batched32_attention_4096x4096x128_f16_f32out_fused"
 
 # Workloads that run with the fused epilogue (dmu_gemm_ex): base problem, output type, activation.
 EPILOGUE_WORKLOADS = {"c5dq": ("c5", "bf16", "gelu_tanh")}
@@ -85,6 +89,10 @@ def kernel_for(workload: str) -> str:
     import dense_matrix_unit_tiled_amd as dmu
     import workloads
 
+    if workload in ATTENTION_WORKLOADS:
+        *_, in_t, out_t = ATTENTION_WORKLOADS[workload]
+        return f"attn_fwd_{in_t}_{out_t}"
+
     base, out_override = (EPILOGUE_WORKLOADS[workload][:2] if workload in EPILOGUE_WORKLOADS else (workload, None))
     M, N, K, batch, in_t, out_t, acc_t, la, lb = workloads.FULL[base]
     out_t = out_override or out_t
@@ -124,6 +132,49 @@ def cpu_baseline(p, budget_s: float = 15.0):
                       f"({rows2}x{p.N}x{p.K} MACs, {t2:.1f} s, fp64 sums, {threads} threads)"}
 
 
+def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
+    """Time the fused attention forward over inputs resident in HBM (same protocol as the GEMM)."""
+    batch, sq, sk, hd, in_t, out_t = ATTENTION_WORKLOADS[args.workload]
+    rng = np.random.default_rng([41, 0])
+    # Q, K, V uniform in [-1, 1] (the recipe of the batched attention-shaped pair), scale 1/sqrt(d)
+    dQ = to_dev(workloads.to_bits(rng.uniform(-1, 1, batch * sq * hd), in_t))
+    dK = to_dev(workloads.to_bits(rng.uniform(-1, 1, batch * sk * hd), in_t))
+    dV = to_dev(workloads.to_bits(rng.uniform(-1, 1, batch * sk * hd), in_t))
+    dO = torch.zeros(batch * sq * hd, dtype=torch.float32 if out_t == "f32" else torch.int16, device="cuda:0")
+    a = dmu.attention_args(batch, sq, sk, hd, dQ, hd, dK, hd, dV, hd, dO, hd, in_type=in_t, out_type=out_t,
+                           scale=1.0 / hd ** 0.5, stride_q=sq * hd, stride_k=sk * hd, stride_v=sk * hd,
+                           stride_o=sq * hd)
+    stream = torch.cuda.current_stream()
+    kernel = kernel_for(args.workload)
+    print(f"# workload {WORKLOAD_NAMES[args.workload]} kernel {kernel}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        dmu.dmu_attention(a, stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        dmu.dmu_attention(a, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = 4.0 * batch * sq * sk * hd  # the two products, 2 flops per multiply-add
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[in_t]
+    result = {
+        "metric": "achieved TFLOPS (fused attention forward, both products)", "value": round(tflops, 3),
+        "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": in_t, "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": batch, "seq_q": sq, "seq_k": sk,
+                   "head_dim": hd, "in_type": in_t, "out_type": out_t, "kernel": kernel,
+                   "pct_of_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": stored_traffic(args.workload, kernel)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +211,9 @@ def main() -> int:
     def to_dev(x):  # raw element bits on the GPU (uint16 patterns travel as int16)
         x = np.ascontiguousarray(x)
         return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to("cuda:0")
+
+    if args.workload in ATTENTION_WORKLOADS:
+        return run_attention(args, dmu, workloads, torch, np, to_dev)
 
     ep = None
     if args.workload in EPILOGUE_WORKLOADS:

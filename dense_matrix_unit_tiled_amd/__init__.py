@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the product runs in the library's HIP
 kernels.  The functions keep the C names (``dmu_gemm``, ``dmu_gemm_check``,
-``dmu_gemm_ex``, ``dmu_gemm_ex_check``, ``dmu_gemm_kernel_name``,
+``dmu_gemm_ex``, ``dmu_gemm_ex_check``, ``dmu_attention``, ``dmu_attention_check``,
+``dmu_gemm_kernel_name``,
 ``dmu_status_string``, ``dmu_last_error``, ``dmu_probe``, ``dmu_probe_info``);
 ``gemm_args`` and ``epilogue_args`` fill the argument structs from torch tensors
 (or raw integer device addresses).  PyTorch supplies device
@@ -69,6 +70,20 @@ class dmu_epilogue(ctypes.Structure):
     ]
 
 
+class dmu_attention_args(ctypes.Structure):
+    """Mirror of ``struct dmu_attention_args`` (include/dmu.h)."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seq_q", ctypes.c_int64), ("seq_k", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64), ("in_type", ctypes.c_int32), ("out_type", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("Q", ctypes.c_void_p), ("ldq", ctypes.c_int64), ("stride_q", ctypes.c_int64),
+        ("K", ctypes.c_void_p), ("ldk", ctypes.c_int64), ("stride_k", ctypes.c_int64),
+        ("V", ctypes.c_void_p), ("ldv", ctypes.c_int64), ("stride_v", ctypes.c_int64),
+        ("O", ctypes.c_void_p), ("ldo", ctypes.c_int64), ("stride_o", ctypes.c_int64),
+    ]
+
+
 class DmuError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{dmu_status_string(status)}: {detail}")
@@ -94,6 +109,9 @@ def _load():
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.dmu_gemm.argtypes, lib.dmu_gemm.restype = [P, vp], i32
     lib.dmu_gemm_check.argtypes, lib.dmu_gemm_check.restype = [P], i32
+    PA = ctypes.POINTER(dmu_attention_args)
+    lib.dmu_attention.argtypes, lib.dmu_attention.restype = [PA, vp], i32
+    lib.dmu_attention_check.argtypes, lib.dmu_attention_check.restype = [PA], i32
     PE = ctypes.POINTER(dmu_epilogue)
     lib.dmu_gemm_ex.argtypes, lib.dmu_gemm_ex.restype = [P, PE, vp], i32
     lib.dmu_gemm_ex_check.argtypes, lib.dmu_gemm_ex_check.restype = [P, PE], i32
@@ -176,6 +194,31 @@ def dmu_gemm_ex(args: dmu_gemm_args, ep: dmu_epilogue | None, stream=None, check
 
 def dmu_gemm_ex_check(args: dmu_gemm_args, ep: dmu_epilogue | None) -> int:
     return _load().dmu_gemm_ex_check(ctypes.byref(args), None if ep is None else ctypes.byref(ep))
+
+
+def attention_args(batch, seq_q, seq_k, head_dim, Q, ldq, K, ldk, V, ldv, O, ldo, *, in_type, out_type, scale,
+                   stride_q=0, stride_k=0, stride_v=0, stride_o=0) -> dmu_attention_args:
+    """Fill a dmu_attention_args from tensors/addresses and type names."""
+    a = dmu_attention_args()
+    a.batch, a.seq_q, a.seq_k, a.head_dim = batch, seq_q, seq_k, head_dim
+    a.in_type, a.out_type, a.scale = DTYPES[in_type], DTYPES[out_type], scale
+    a.Q, a.ldq, a.stride_q = _addr(Q), ldq, stride_q
+    a.K, a.ldk, a.stride_k = _addr(K), ldk, stride_k
+    a.V, a.ldv, a.stride_v = _addr(V), ldv, stride_v
+    a.O, a.ldo, a.stride_o = _addr(O), ldo, stride_o
+    return a
+
+
+def dmu_attention(args: dmu_attention_args, stream=None, check: bool = True) -> int:
+    """Launch O = softmax(scale Q K^T) V on ``stream`` (default: torch's current stream)."""
+    st = _load().dmu_attention(ctypes.byref(args), _stream(stream))
+    if check and st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return st
+
+
+def dmu_attention_check(args: dmu_attention_args) -> int:
+    return _load().dmu_attention_check(ctypes.byref(args))
 
 
 def dmu_gemm_check(args: dmu_gemm_args) -> int:

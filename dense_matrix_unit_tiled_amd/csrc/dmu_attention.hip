@@ -1,0 +1,401 @@
+// Fused attention forward on the matrix cores: O = softmax(scale Q K^T) V.
+//
+// The pages move the two products of a FlashAttention kernel onto the matrix
+// units and keep P = softmax(S) in registers between them (layout-experiment
+// post, sections 1-2; "Tensor Cores, CUTLASS and CuTe", part 3 section 2: the
+// accumulator of S = Q K^T is reused as an operand of O = P V, and each row's
+// max and sum are taken across the lanes that share the row).  This is that
+// computation for gfx950, one pass over the keys with the online softmax:
+//
+//   workgroup   8 wavefronts, 256 query rows of one batch slice (32 per
+//               wavefront: two 16-row tiles), walking the keys in blocks of 64.
+//   K, V        64-key blocks double-buffered in LDS through the GEMM kernel's
+//               staging path: K in the K-contiguous layout (two 64 x 64 halves
+//               of the head dimension), V in the transposed layout.
+//   S = Q K^T   MFMA(srcA = K fragment, srcB = Q fragment) on 16 x 16 tiles: lane
+//               l owns S[q = l % 16][key = 16 t + 4 (l / 16) + r] of key tile t.
+//               Q's fragments stay in registers for the whole pass.
+//   softmax     in base 2: s' = S scale log2(e); per row the running maximum m
+//               (across the four lanes that share the row), p = 2^(s' - m), the
+//               running sum l (kept per lane, added up at the end) and a
+//               correction 2^(m_old - m_new) of O and l when m grows.  Keys past
+//               seq_k get s' = -inf, so p = 0.
+//   O += P V    MFMA(srcA = V^T fragment, srcB = P fragment): P's fragment for 32
+//               keys is the two 16-key accumulator tiles of S, rounded to the
+//               input type and packed -- the V^T fragment is read in the same
+//               key order (McTile::frag_split), so P never leaves the registers.
+//               Lane l owns O[q = l % 16][d = 16 dt + 4 (l / 16) + r].
+//   epilogue    O / l, rounded once to the output type.
+#include <hip/hip_runtime.h>
+
+#include "../../include/dmu.h"
+#include "dmu_host.hpp"
+#include "dmu_tiled.hpp"
+
+namespace dmu {
+
+struct AttnParams {
+    const char *Q, *K, *V;
+    char *O;
+    int64_t ldq, ldk, ldv, ldo;                 // elements
+    int64_t stride_q, stride_k, stride_v, stride_o;
+    int32_t sq, sk, nqb;                        // query blocks per batch slice
+    float scale_log2;                           // scale * log2(e)
+    int64_t q_bytes, k_bytes, v_bytes;          // bytes spanned by one batch slice
+};
+
+namespace {
+
+constexpr int HD = 128;   // head dimension
+constexpr int BQ = 256;   // query rows per workgroup
+constexpr int BKEYS = 64; // keys per block
+
+template <int T> struct Pack16;
+template <> struct Pack16<F16> {
+    static __device__ __forceinline__ uint32_t two(float a, float b)
+    {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    }
+};
+template <> struct Pack16<BF16> {
+    static __device__ __forceinline__ uint32_t two(float a, float b)
+    {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+    }
+};
+
+__device__ __forceinline__ float row_max4(float v) // over the lanes l, l^16, l^32, l^48
+{
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+}
+
+template <int T, int O>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_fwd(AttnParams p)
+{
+    typedef KcTile<BKEYS, 8, false> KT; // one 64-key x 64-value half of a K block
+    typedef McTile<HD, 8> VT;           // 64 keys x 128 values of a V block
+    typedef typename Out<O>::t ot;
+    constexpr uint32_t KBYTES = 2 * KT::BYTES;
+    constexpr uint32_t STAGE = KBYTES + ((VT::BYTES + 255) & ~255u);
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t wg = blockIdx.x;
+    const int64_t b = wg / (uint32_t)p.nqb, q0 = (int64_t)(wg % (uint32_t)p.nqb) * BQ + wave * 32;
+    const char *Qb = p.Q + b * p.stride_q * 2, *Kb = p.K + b * p.stride_k * 2, *Vb = p.V + b * p.stride_v * 2;
+
+    // Q fragments of this wavefront's two row tiles, straight from memory
+    // (rows past seq_q lie past the slice end and read as zeros).
+    u32x4 qf[2][4];
+    {
+        const int64_t start = q0 * p.ldq * 2;
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(Qb + start, start < p.q_bytes ? (uint32_t)(p.q_bytes - start) : 0u);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qf[rt][ks] = load16s(rq, (uint32_t)((16 * rt + (lane & 15u)) * p.ldq * 2) + 64 * ks + 16 * (lane >> 4),
+                                     0);
+    }
+
+    KT tk;
+    VT tv;
+    tk.init(p.ldk * 2, wave, lane);
+    tv.init(p.ldv * 2, HD, wave, lane);
+    const int nblk = (p.sk + BKEYS - 1) / BKEYS;
+    u32x4 sk_[2], sv_[VT::NL]; // the next block between its global loads and its LDS writes
+    auto load_blk = [&](int blk) {
+        const int64_t ks0 = (int64_t)blk * BKEYS * p.ldk * 2, vs0 = (int64_t)blk * BKEYS * p.ldv * 2;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + ks0, ks0 < p.k_bytes ? (uint32_t)(p.k_bytes - ks0) : 0u);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + vs0, vs0 < p.v_bytes ? (uint32_t)(p.v_bytes - vs0) : 0u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            sk_[h] = tk.load(0, rk, h, HD * 2);
+#pragma unroll
+        for (int i = 0; i < VT::NL; ++i)
+            sv_[i] = tv.load(i, rv, 0, 0);
+    };
+    auto store_blk = [&](char *stage) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            tk.store(0, stage + h * KT::BYTES, wave, lane, sk_[h], h, HD * 2);
+#pragma unroll
+        for (int i = 0; i < VT::NL; ++i)
+            tv.store(i, stage + KBYTES, wave, lane, sv_[i], 0, 0);
+    };
+
+    f32x4 o[2][HD / 16];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt)
+            o[rt][dt] = f32x4{};
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+
+    load_blk(0);
+    store_blk(smem);
+    load_blk(1);
+    stage_barrier();
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const char *cur = smem + (blk & 1) * STAGE;
+        char *nxt = smem + ((blk + 1) & 1) * STAGE;
+
+        // S = Q K^T for the 64 keys of this block
+        f32x4 s[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                s[rt][t] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 kf[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                kf[t] = KT::frag(cur + (ks >> 1) * KT::BYTES, 16 * t, ks & 1, lane);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    s[rt][t] = Mfma<T>::step(kf[t], qf[rt][ks], s[rt][t]);
+        }
+
+        // the next block to the free stage, the one after it into the staging registers
+        store_blk(nxt);
+        load_blk(blk + 2);
+
+        // online softmax; P packed as the operand of O += P V
+        u32x4 pf[2][2];
+        const int key0 = blk * BKEYS + 4 * (int)(lane >> 4);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = s[rt][t][r] * p.scale_log2;
+                    v = key0 + 16 * t + r < p.sk ? v : -INFINITY;
+                    s[rt][t][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            const float m_new = fmaxf(m[rt], row_max4(mx));
+            const float corr = __builtin_amdgcn_exp2f(m[rt] - m_new);
+            m[rt] = m_new;
+            float sum = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(s[rt][t][r] - m_new);
+                    s[rt][t][r] = e;
+                    sum += e;
+                }
+            l[rt] = l[rt] * corr + sum;
+#pragma unroll
+            for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[rt][dt][r] *= corr;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                pf[rt][kk] = u32x4{Pack16<T>::two(s[rt][2 * kk][0], s[rt][2 * kk][1]),
+                                   Pack16<T>::two(s[rt][2 * kk][2], s[rt][2 * kk][3]),
+                                   Pack16<T>::two(s[rt][2 * kk + 1][0], s[rt][2 * kk + 1][1]),
+                                   Pack16<T>::two(s[rt][2 * kk + 1][2], s[rt][2 * kk + 1][3])};
+        }
+
+        // O += P V
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < HD / 16; ++dt) {
+                const u32x4 vf = VT::frag_split(cur + KBYTES, 16 * dt, kk, lane);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    o[rt][dt] = Mfma<T>::step(vf, pf[rt][kk], o[rt][dt]);
+            }
+        stage_barrier();
+    }
+
+    // O / l, each row's sum added up over the four lanes that hold its parts
+    char *Ob = p.O + b * p.stride_o * (int64_t)sizeof(ot);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        float tot = l[rt];
+        tot += __shfl_xor(tot, 16);
+        tot += __shfl_xor(tot, 32);
+        const float inv = 1.0f / tot;
+        const int64_t q = q0 + 16 * rt + (lane & 15u);
+        if (q >= p.sq)
+            continue;
+        ot *row = reinterpret_cast<ot *>(Ob) + q * p.ldo;
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt) {
+            typedef ot ov4 __attribute__((ext_vector_type(4)));
+            ov4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[r] = Out<O>::from_acc(o[rt][dt][r] * inv);
+            *reinterpret_cast<ov4 *>(row + 16 * dt + 4 * (lane >> 4)) = v;
+        }
+    }
+}
+
+int elem_size(int t) { return t == DMU_F32 ? 4 : 2; }
+
+int attn_validate(const dmu_attention_args *a, AttnParams *p, bool *launch)
+{
+    *launch = false;
+    if (!a) {
+        set_error("args is NULL");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->batch < 0 || a->seq_q < 0 || a->seq_k < 0 || a->head_dim < 0) {
+        set_error("negative size");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->batch >= ((int64_t)1 << 31) || a->seq_q >= ((int64_t)1 << 31) || a->seq_k >= ((int64_t)1 << 31)) {
+        set_error("size of 2^31 or more is not supported");
+        return DMU_ERR_UNSUPPORTED;
+    }
+    if (a->head_dim != HD) {
+        set_error("head_dim %lld is not supported (128 is)", (long long)a->head_dim);
+        return DMU_ERR_UNSUPPORTED;
+    }
+    if ((a->in_type != DMU_F16 && a->in_type != DMU_BF16) ||
+        (a->out_type != DMU_F32 && a->out_type != DMU_F16 && a->out_type != DMU_BF16)) {
+        set_error("unsupported types (in %d, out %d)", a->in_type, a->out_type);
+        return DMU_ERR_UNSUPPORTED;
+    }
+    if (a->batch == 0 || a->seq_q == 0)
+        return DMU_OK;
+    if (a->seq_k == 0) {
+        set_error("seq_k == 0: the softmax of an empty row is undefined");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (!a->Q || !a->K || !a->V || !a->O) {
+        set_error("NULL operand pointer");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->ldq < HD || a->ldk < HD || a->ldv < HD || a->ldo < HD) {
+        set_error("leading dimension below head_dim");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (a->stride_q < 0 || a->stride_k < 0 || a->stride_v < 0 || a->stride_o < 0) {
+        set_error("negative batch stride");
+        return DMU_ERR_INVALID_ARG;
+    }
+    const int osz = elem_size(a->out_type);
+    const int64_t ext_q = (a->seq_q - 1) * a->ldq + HD, ext_k = (a->seq_k - 1) * a->ldk + HD;
+    const int64_t ext_o = (a->seq_q - 1) * a->ldo + HD;
+    if (a->batch > 1 && a->stride_o < ext_o) {
+        set_error("stride_o lets batch slices of O overlap");
+        return DMU_ERR_INVALID_ARG;
+    }
+    auto aligned = [](const void *ptr, int64_t ld, int64_t stride, int esz) {
+        return ((uintptr_t)ptr % 16) == 0 && (ld * esz) % 16 == 0 && (stride * esz) % 16 == 0;
+    };
+    const bool b1 = a->batch > 1;
+    if (!aligned(a->Q, a->ldq, b1 ? a->stride_q : 0, 2) || !aligned(a->K, a->ldk, b1 ? a->stride_k : 0, 2) ||
+        !aligned(a->V, a->ldv, b1 ? a->stride_v : 0, 2) || !aligned(a->O, a->ldo, b1 ? a->stride_o : 0, osz)) {
+        set_error("operands must have 16-byte aligned pointers, rows and batch strides");
+        return DMU_ERR_UNSUPPORTED;
+    }
+    const int64_t slice_max = ((int64_t)1 << 31);
+    if (ext_q * 2 >= slice_max || ext_k * 2 >= slice_max || ((a->seq_k - 1) * a->ldv + HD) * 2 >= slice_max) {
+        set_error("a batch slice of 2 GiB or more is not supported");
+        return DMU_ERR_UNSUPPORTED;
+    }
+    // O may not overlap the inputs
+    auto span = [&](const void *ptr, int64_t stride, int64_t ext, int esz, uintptr_t *lo, uintptr_t *hi) {
+        *lo = (uintptr_t)ptr;
+        *hi = *lo + (uintptr_t)(((a->batch - 1) * (b1 ? stride : 0) + ext) * esz);
+    };
+    uintptr_t o0, o1, x0, x1;
+    span(a->O, a->stride_o, ext_o, osz, &o0, &o1);
+    const struct { const void *p; int64_t stride, ext; } ins[3] = {
+        {a->Q, a->stride_q, ext_q}, {a->K, a->stride_k, ext_k}, {a->V, a->stride_v, (a->seq_k - 1) * a->ldv + HD}};
+    for (const auto &x : ins) {
+        span(x.p, x.stride, x.ext, 2, &x0, &x1);
+        if (o0 < x1 && x0 < o1) {
+            set_error("O overlaps an input");
+            return DMU_ERR_INVALID_ARG;
+        }
+    }
+    const int64_t nqb = (a->seq_q + BQ - 1) / BQ;
+    if (nqb * a->batch >= ((int64_t)1 << 31)) {
+        set_error("too many workgroups for one launch");
+        return DMU_ERR_UNSUPPORTED;
+    }
+    p->Q = static_cast<const char *>(a->Q);
+    p->K = static_cast<const char *>(a->K);
+    p->V = static_cast<const char *>(a->V);
+    p->O = static_cast<char *>(a->O);
+    p->ldq = a->ldq;
+    p->ldk = a->ldk;
+    p->ldv = a->ldv;
+    p->ldo = a->ldo;
+    p->stride_q = b1 ? a->stride_q : 0;
+    p->stride_k = b1 ? a->stride_k : 0;
+    p->stride_v = b1 ? a->stride_v : 0;
+    p->stride_o = b1 ? a->stride_o : 0;
+    p->sq = (int32_t)a->seq_q;
+    p->sk = (int32_t)a->seq_k;
+    p->nqb = (int32_t)nqb;
+    p->scale_log2 = a->scale * 1.4426950408889634f;
+    p->q_bytes = ext_q * 2;
+    p->k_bytes = ext_k * 2;
+    p->v_bytes = ((a->seq_k - 1) * a->ldv + HD) * 2;
+    *launch = true;
+    return DMU_OK;
+}
+
+template <int T, int O> hipError_t go(const AttnParams &p, int64_t grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((attn_fwd<T, O>), dim3((uint32_t)grid), dim3(512), 0, s, p);
+    return hipGetLastError();
+}
+
+} // namespace
+} // namespace dmu
+
+using namespace dmu;
+
+extern "C" int dmu_attention_check(const dmu_attention_args *args)
+{
+    clear_error();
+    AttnParams p;
+    bool launch;
+    return attn_validate(args, &p, &launch);
+}
+
+extern "C" int dmu_attention(const dmu_attention_args *args, void *stream)
+{
+    clear_error();
+    AttnParams p;
+    bool launch;
+    int rc = attn_validate(args, &p, &launch);
+    if (rc != DMU_OK || !launch)
+        return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t grid = (int64_t)p.nqb * args->batch;
+    hipError_t e;
+    const bool bf = args->in_type == DMU_BF16;
+    switch (args->out_type) {
+    case DMU_F32: e = bf ? go<BF16, F32>(p, grid, s) : go<F16, F32>(p, grid, s); break;
+    case DMU_F16: e = bf ? go<BF16, F16>(p, grid, s) : go<F16, F16>(p, grid, s); break;
+    default: e = bf ? go<BF16, BF16>(p, grid, s) : go<F16, BF16>(p, grid, s); break;
+    }
+    if (e != hipSuccess) {
+        set_error("dmu_attention: launch failed: %s", hipGetErrorString(e));
+        return DMU_ERR_HIP;
+    }
+    return DMU_OK;
+}

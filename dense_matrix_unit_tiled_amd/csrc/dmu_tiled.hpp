@@ -189,6 +189,24 @@ template <int R, int NW> struct McTile {
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         return u32x4{l2[0], l2[1], h2[0], h2[1]};
     }
+    // Columns [c0, c0 + 16), keys of K-step kk (32 keys) in the order that the
+    // 16 x 16 accumulator of a preceding product leaves them in (lane l owns
+    // rows 4 (l / 16) + 0..3 of each 16-row tile): lane l gets column c0 + l % 16
+    // at k = 32 kk + 4 (l / 16) + 0..3 and 32 kk + 16 + 4 (l / 16) + 0..3.  So the
+    // accumulators of two adjacent 16-key tiles, packed, are the other operand
+    // of the same instruction, with no data movement.
+    static __device__ __forceinline__ u32x4 frag_split(const char *tile, uint32_t c0, uint32_t kk, uint32_t lane)
+    {
+        constexpr uint32_t P = 2 * R + 32;
+        const uint32_t g = lane >> 4, j = lane & 15u;
+        const uint32_t k = 32 * kk + 4 * g + (j >> 2);
+        const uint32_t a0 = mc_row_off<R>(k) + (c0 + 4 * (j & 3u)) * 2;
+        const uint32_t a1 = a0 + 8 * P; // k + 16: same region, eight region rows on
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(tile + a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(tile + a1));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
 };
 
 template <int MODE, int R, int NW> struct TileOf;

@@ -175,6 +175,54 @@ int dmu_gemm_ex_check(const dmu_gemm_args *args, const dmu_epilogue *ep);
 int dmu_gemm_check(const dmu_gemm_args *args);
 
 /*
+ * Attention forward, fused on the matrix cores: for every batch slice b,
+ *
+ *     O[b] = softmax(scale * Q[b] K[b]^T) V[b]      (softmax over each row)
+ *
+ * The pages move the two products of this computation onto the matrix units
+ * and keep P = softmax(S) in registers between them (layout-experiment post,
+ * sections 1-2; "Tensor Cores, CUTLASS and CuTe", part 3 section 2: the
+ * accumulator of S = Q K^T feeds O = P V, with each row's max and sum taken
+ * across the lanes that share the row).  Here S never leaves the chip: each
+ * workgroup walks the keys in blocks with a running row maximum and sum (the
+ * online softmax), P is rounded to the input type for the P V product.
+ *
+ *  batch, seq_q, seq_k  sizes; batch and seq_q >= 0 (0: nothing is done),
+ *                   seq_k >= 1.  Each below 2^31.
+ *  head_dim         d of Q, K and V; 128 is supported.
+ *  in_type          DMU_F16 or DMU_BF16 (Q, K, V).
+ *  out_type         DMU_F32, DMU_F16 or DMU_BF16 (O); rounded once (RNE).
+ *  scale            softmax scale (e.g. 1/sqrt(head_dim)), fp32.
+ *  Q, ldq, stride_q row-major seq_q x head_dim, leading dimension and batch
+ *  K, ldk, stride_k stride in elements (seq_k x head_dim for K and V);
+ *  V, ldv, stride_v pointers and leading dimensions 16-byte aligned (ld a
+ *                   multiple of 8 elements), strides >= 0.
+ *  O, ldo, stride_o row-major seq_q x head_dim of out_type; rows 16-byte
+ *                   aligned; may not overlap Q, K or V, nor its own batches.
+ *
+ * Errors as for dmu_gemm: DMU_ERR_INVALID_ARG / DMU_ERR_UNSUPPORTED before any
+ * HIP call, DMU_ERR_HIP for a failed launch.  Asynchronous on `stream`.
+ */
+typedef struct dmu_attention_args {
+    int64_t batch, seq_q, seq_k, head_dim;
+    int32_t in_type, out_type; /* dmu_dtype */
+    float scale;
+    const void *Q;
+    int64_t ldq, stride_q;
+    const void *K;
+    int64_t ldk, stride_k;
+    const void *V;
+    int64_t ldv, stride_v;
+    void *O;
+    int64_t ldo, stride_o;
+} dmu_attention_args;
+
+int dmu_attention(const dmu_attention_args *args, void *stream);
+
+/* Validate `args` exactly as dmu_attention does, without touching the GPU. */
+int dmu_attention_check(const dmu_attention_args *args);
+
+/*
  * Name of the kernel variant dmu_gemm would launch for `args` (a static
  * string, e.g. "mfma_256x256_nn_bf16"), or NULL if the arguments are invalid
  * or the call would launch nothing.  Host-only; no GPU access.

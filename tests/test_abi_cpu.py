@@ -186,3 +186,46 @@ def test_int32_output_takes_empty_epilogue():
 def test_dequantising_kernel_names(out_t):
     a = args(in_type="i8", out_type=out_t, K=512, lda=512, ldb=512, layout_b="col")
     assert dmu.dmu_gemm_kernel_name(a).endswith(f"i8_{out_t}")
+
+
+def att(**kw):
+    base = dict(batch=2, seq_q=300, seq_k=200, head_dim=128, Q=FAKE, ldq=128, K=FAKE + (1 << 30), ldk=128,
+                V=FAKE + (2 << 30), ldv=128, O=FAKE + (3 << 30), ldo=128, in_type="f16", out_type="f32",
+                scale=0.088, stride_q=300 * 128, stride_k=200 * 128, stride_v=200 * 128, stride_o=300 * 128)
+    base.update(kw)
+    return dmu.attention_args(**base)
+
+
+def test_attention_struct_layout():
+    # 4 int64 + 2 int32 + float (+4 pad) + 4 x (pointer + 2 int64)
+    assert ctypes.sizeof(dmu.dmu_attention_args) == 32 + 16 + 4 * 24
+    assert dmu.dmu_attention_args.Q.offset == 48
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(in_type="bf16", out_type="bf16"), dict(out_type="f16"),
+                                dict(batch=0), dict(seq_q=0), dict(seq_q=1, seq_k=1, batch=1)])
+def test_attention_valid(kw):
+    assert dmu.dmu_attention_check(att(**kw)) == dmu.DMU_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(in_type="f32"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(out_type="i32"), dmu.DMU_ERR_UNSUPPORTED),
+    (dict(seq_k=0), dmu.DMU_ERR_INVALID_ARG),
+    (dict(seq_q=-1), dmu.DMU_ERR_INVALID_ARG),
+    (dict(ldk=100), dmu.DMU_ERR_INVALID_ARG),
+    (dict(ldq=130), dmu.DMU_ERR_UNSUPPORTED),                    # rows not 16-byte aligned
+    (dict(V=FAKE + (2 << 30) + 2), dmu.DMU_ERR_UNSUPPORTED),      # misaligned pointer
+    (dict(stride_o=100), dmu.DMU_ERR_INVALID_ARG),               # batches of O overlap
+    (dict(O=FAKE + 4096), dmu.DMU_ERR_INVALID_ARG),              # O overlaps Q
+    (dict(K=None), dmu.DMU_ERR_INVALID_ARG),
+    (dict(stride_k=-1), dmu.DMU_ERR_INVALID_ARG),
+])
+def test_attention_rejections(kw, status):
+    a = att(**kw)
+    assert dmu.dmu_attention_check(a) == status
+    assert dmu.dmu_last_error() != ""
+    with pytest.raises(dmu.DmuError) as e:
+        dmu.dmu_attention(a, stream=0)  # rejected before any HIP call
+    assert e.value.status == status
