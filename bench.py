@@ -132,17 +132,45 @@ def cpu_baseline(p, budget_s: float = 15.0):
                       f"({rows2}x{p.N}x{p.K} MACs, {t2:.1f} s, fp64 sums, {threads} threads)"}
 
 
+def attention_cpu_baseline(batch, sq, sk, hd, Q, K, V, in_t, out_t, scale, budget_s: float = 15.0):
+    """The oracle, as it stands, on the host cores over a bounded sample of query rows."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+
+    def run(n):
+        rows = np.stack([np.arange(n) % batch, (np.arange(n) * 997) % sq], axis=1)
+        t0 = time.perf_counter()
+        oracle.attention_rows(batch, sq, sk, hd, hd, Q, hd, sq * hd, K, hd, sk * hd, V, hd, sk * hd, rows,
+                              in_type=in_t, out_type=out_t, scale=scale, nthreads=threads)
+        return time.perf_counter() - t0
+
+    n = threads
+    t = run(n)
+    n2 = int(min(batch * sq, max(n, n * budget_s / max(t, 1e-3))))
+    n2 = max(threads, (n2 // threads) * threads)
+    t2 = run(n2)
+    flops = 4.0 * n2 * sk * hd
+    return {"value": round(flops / t2 / 1e12, 6), "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{n2} query rows spread over the {batch} slices of the {batch}x{sq}x{sk}x{hd} "
+                      f"attention ({t2:.1f} s, fp64, {threads} threads)"}
+
+
 def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
     """Time the fused attention forward over inputs resident in HBM (same protocol as the GEMM)."""
     batch, sq, sk, hd, in_t, out_t = ATTENTION_WORKLOADS[args.workload]
     rng = np.random.default_rng([41, 0])
     # Q, K, V uniform in [-1, 1] (the recipe of the batched attention-shaped pair), scale 1/sqrt(d)
-    dQ = to_dev(workloads.to_bits(rng.uniform(-1, 1, batch * sq * hd), in_t))
-    dK = to_dev(workloads.to_bits(rng.uniform(-1, 1, batch * sk * hd), in_t))
-    dV = to_dev(workloads.to_bits(rng.uniform(-1, 1, batch * sk * hd), in_t))
+    Q = workloads.to_bits(rng.uniform(-1, 1, batch * sq * hd), in_t)
+    K = workloads.to_bits(rng.uniform(-1, 1, batch * sk * hd), in_t)
+    V = workloads.to_bits(rng.uniform(-1, 1, batch * sk * hd), in_t)
+    dQ, dK, dV = to_dev(Q), to_dev(K), to_dev(V)
     dO = torch.zeros(batch * sq * hd, dtype=torch.float32 if out_t == "f32" else torch.int16, device="cuda:0")
+    scale = 1.0 / hd ** 0.5
     a = dmu.attention_args(batch, sq, sk, hd, dQ, hd, dK, hd, dV, hd, dO, hd, in_type=in_t, out_type=out_t,
-                           scale=1.0 / hd ** 0.5, stride_q=sq * hd, stride_k=sk * hd, stride_v=sk * hd,
+                           scale=scale, stride_q=sq * hd, stride_k=sk * hd, stride_v=sk * hd,
                            stride_o=sq * hd)
     stream = torch.cuda.current_stream()
     kernel = kernel_for(args.workload)
@@ -157,6 +185,8 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    print(f"# timed {args.steps} launches: {ms * 1e3:.2f} us each", file=sys.stderr, flush=True)
+    copy_calibration(args, torch)
     flops = 4.0 * batch * sq * sk * hd  # the two products, 2 flops per multiply-add
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[in_t]
@@ -169,10 +199,22 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
                    "pct_of_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": stored_traffic(args.workload, kernel)},
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else
+        attention_cpu_baseline(batch, sq, sk, hd, Q, K, V, in_t, out_t, scale),
     }
     print(json.dumps(result), flush=True)
     return 0
+
+
+def copy_calibration(args, torch):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def main() -> int:
@@ -253,13 +295,7 @@ def main() -> int:
     ms = start.elapsed_time(end) / args.steps
     print(f"# timed {args.steps} launches: {ms * 1e3:.2f} us each", file=sys.stderr, flush=True)
 
-    if args.copy_calibration:
-        n = args.copy_calibration * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    copy_calibration(args, torch)
 
     flops = float(p.flops)
     tflops = flops / (ms * 1e-3) / 1e12

@@ -8,18 +8,25 @@
 // computation for gfx950, one pass over the keys with the online softmax:
 //
 //   workgroup   8 wavefronts, 256 query rows of one batch slice (32 per
-//               wavefront: two 16-row tiles), walking the keys in blocks of 64.
-//   K, V        64-key blocks double-buffered in LDS through the GEMM kernel's
-//               staging path: K in the K-contiguous layout (two 64 x 64 halves
-//               of the head dimension), V in the transposed layout.
+//               wavefront: two 16-row tiles), walking the keys in blocks of 64;
+//               workgroups renumbered so that one batch slice's query blocks
+//               share an XCD (and its L2 copy of K and V).
+//   K, V        64-key blocks through the GEMM kernel's register-staged LDS
+//               path, in two rings of two buffers: K (K-contiguous layout, two
+//               64 x 64 halves of the head dimension) one block ahead of V
+//               (transposed layout).  One barrier per block.
 //   S = Q K^T   MFMA(srcA = K fragment, srcB = Q fragment) on 16 x 16 tiles: lane
 //               l owns S[q = l % 16][key = 16 t + 4 (l / 16) + r] of key tile t.
 //               Q's fragments stay in registers for the whole pass.
-//   softmax     in base 2: s' = S scale log2(e); per row the running maximum m
-//               (across the four lanes that share the row), p = 2^(s' - m), the
-//               running sum l (kept per lane, added up at the end) and a
-//               correction 2^(m_old - m_new) of O and l when m grows.  Keys past
-//               seq_k get s' = -inf, so p = 0.
+//   pipeline    step j computes the scores of block j+1 while block j's
+//               softmax runs (independent work for the matrix core and the
+//               VALU in one region), then O += P V for block j.
+//   softmax     in base 2 with c = scale log2(e) >= 0 (a negative scale negates
+//               Q instead): per row the running maximum m of c s (across the
+//               four lanes that share the row), p = 2^(c s - m) (one FMA and the
+//               hardware exp2), the running sum l (kept per lane, added up at
+//               the end) and the correction 2^(m_old - m_new) of O and l.  Only
+//               the last block can hold keys past seq_k; they get p = 0.
 //   O += P V    MFMA(srcA = V^T fragment, srcB = P fragment): P's fragment for 32
 //               keys is the two 16-key accumulator tiles of S, rounded to the
 //               input type and packed -- the V^T fragment is read in the same
@@ -27,6 +34,8 @@
 //               Lane l owns O[q = l % 16][d = 16 dt + 4 (l / 16) + r].
 //   epilogue    O / l, rounded once to the output type.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "../../include/dmu.h"
 #include "dmu_host.hpp"
@@ -51,18 +60,19 @@ constexpr int BQ = 256;   // query rows per workgroup
 constexpr int BKEYS = 64; // keys per block
 
 template <int T> struct Pack16;
-template <> struct Pack16<F16> {
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <> struct Pack16<F16> { // two values rounded to fp16 (RNE), the first in the low half
     static __device__ __forceinline__ uint32_t two(float a, float b)
     {
-        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
     }
 };
 template <> struct Pack16<BF16> {
     static __device__ __forceinline__ uint32_t two(float a, float b)
     {
-        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
     }
 };
 
@@ -72,6 +82,8 @@ __device__ __forceinline__ float row_max4(float v) // over the lanes l, l^16, l^
     return fmaxf(v, __shfl_xor(v, 32));
 }
 
+template <bool B> using Bool = std::integral_constant<bool, B>;
+
 template <int T, int O>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_fwd(AttnParams p)
 {
@@ -79,12 +91,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     typedef McTile<HD, 8> VT;           // 64 keys x 128 values of a V block
     typedef typename Out<O>::t ot;
     constexpr uint32_t KBYTES = 2 * KT::BYTES;
-    constexpr uint32_t STAGE = KBYTES + ((VT::BYTES + 255) & ~255u);
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    constexpr uint32_t VBYTES = (VT::BYTES + 255) & ~255u;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * (KBYTES + VBYTES)];
+    char *const kbuf = smem, *const vbuf = smem + 2 * KBYTES; // two K blocks, two V blocks
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t wg = blockIdx.x;
+    // Workgroup i runs on XCD i mod 8: renumber so that each XCD receives a
+    // contiguous range, i.e. the query blocks of one batch slice share that
+    // XCD's L2 for K and V.
+    const uint32_t n_wg = gridDim.x, xcd = blockIdx.x % 8u, per = n_wg / 8u, extra = n_wg % 8u;
+    const uint32_t wg = xcd * per + min(xcd, extra) + blockIdx.x / 8u;
     const int64_t b = wg / (uint32_t)p.nqb, q0 = (int64_t)(wg % (uint32_t)p.nqb) * BQ + wave * 32;
     const char *Qb = p.Q + b * p.stride_q * 2, *Kb = p.K + b * p.stride_k * 2, *Vb = p.V + b * p.stride_v * 2;
 
@@ -102,31 +119,48 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
                 qf[rt][ks] = load16s(rq, (uint32_t)((16 * rt + (lane & 15u)) * p.ldq * 2) + 64 * ks + 16 * (lane >> 4),
                                      0);
     }
+    // scale * log2(e); a negative scale negates Q instead (exactly), so c >= 0
+    float c = p.scale_log2;
+    if (c < 0.0f) {
+        c = -c;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    qf[rt][ks][e] ^= 0x80008000u;
+    }
 
     KT tk;
     VT tv;
     tk.init(p.ldk * 2, wave, lane);
     tv.init(p.ldv * 2, HD, wave, lane);
     const int nblk = (p.sk + BKEYS - 1) / BKEYS;
-    u32x4 sk_[2], sv_[VT::NL]; // the next block between its global loads and its LDS writes
-    auto load_blk = [&](int blk) {
-        const int64_t ks0 = (int64_t)blk * BKEYS * p.ldk * 2, vs0 = (int64_t)blk * BKEYS * p.ldv * 2;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + ks0, ks0 < p.k_bytes ? (uint32_t)(p.k_bytes - ks0) : 0u);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + vs0, vs0 < p.v_bytes ? (uint32_t)(p.v_bytes - vs0) : 0u);
+    u32x4 sk_[2], sv_[VT::NL]; // a K and a V block between their global loads and their LDS writes
+    auto load_k = [&](int blk) {
+        const int64_t s0 = (int64_t)blk * BKEYS * p.ldk * 2;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + s0, s0 < p.k_bytes ? (uint32_t)(p.k_bytes - s0) : 0u);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            sk_[h] = tk.load(0, rk, h, HD * 2);
-#pragma unroll
-        for (int i = 0; i < VT::NL; ++i)
-            sv_[i] = tv.load(i, rv, 0, 0);
+            sk_[h] = tk.load(0, r, h, HD * 2);
     };
-    auto store_blk = [&](char *stage) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            tk.store(0, stage + h * KT::BYTES, wave, lane, sk_[h], h, HD * 2);
+    auto load_v = [&](int blk) {
+        const int64_t s0 = (int64_t)blk * BKEYS * p.ldv * 2;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + s0, s0 < p.v_bytes ? (uint32_t)(p.v_bytes - s0) : 0u);
 #pragma unroll
         for (int i = 0; i < VT::NL; ++i)
-            tv.store(i, stage + KBYTES, wave, lane, sv_[i], 0, 0);
+            sv_[i] = tv.load(i, r, 0, 0);
+    };
+    auto store_k = [&](char *dst) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            tk.store(0, dst + h * KT::BYTES, wave, lane, sk_[h], h, HD * 2);
+    };
+    auto store_v = [&](char *dst) {
+#pragma unroll
+        for (int i = 0; i < VT::NL; ++i)
+            tv.store(i, dst, wave, lane, sv_[i], 0, 0);
     };
 
     f32x4 o[2][HD / 16];
@@ -136,18 +170,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int dt = 0; dt < HD / 16; ++dt)
             o[rt][dt] = f32x4{};
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+    f32x4 sa[2][4], sb[2][4]; // the scores of two consecutive key blocks
 
-    load_blk(0);
-    store_blk(smem);
-    load_blk(1);
-    stage_barrier();
-
-    for (int blk = 0; blk < nblk; ++blk) {
-        const char *cur = smem + (blk & 1) * STAGE;
-        char *nxt = smem + ((blk + 1) & 1) * STAGE;
-
-        // S = Q K^T for the 64 keys of this block
-        f32x4 s[2][4];
+    // S = Q K^T for the 64 keys of the K block at kt
+    auto scores = [&](f32x4 (&s)[2][4], const char *kt) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -158,20 +184,21 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
             u32x4 kf[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                kf[t] = KT::frag(cur + (ks >> 1) * KT::BYTES, 16 * t, ks & 1, lane);
+                kf[t] = KT::frag(kt + (ks >> 1) * KT::BYTES, 16 * t, ks & 1, lane);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
                     s[rt][t] = Mfma<T>::step(kf[t], qf[rt][ks], s[rt][t]);
         }
-
-        // the next block to the free stage, the one after it into the staging registers
-        store_blk(nxt);
-        load_blk(blk + 2);
-
-        // online softmax; P packed as the operand of O += P V
-        u32x4 pf[2][2];
+    };
+    // Online softmax of block blk's scores: the running max m and sum l,
+    // O rescaled by 2^(m_old - m_new), P = 2^(c s - m) packed as the operand
+    // of O += P V (tiles 2kk and 2kk+1 of S make P's fragment kk).  Only the
+    // last block can hold keys past seq_k: they get no weight.
+    float corr_[2];           // the last softmax's O correction per row tile
+    auto softmax = [&](f32x4 (&s)[2][4], u32x4 (&pf)[2][2], int blk, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         const int key0 = blk * BKEYS + 4 * (int)(lane >> 4);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -179,13 +206,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = s[rt][t][r] * p.scale_log2;
-                    v = key0 + 16 * t + r < p.sk ? v : -INFINITY;
-                    s[rt][t][r] = v;
-                    mx = fmaxf(mx, v);
-                }
-            const float m_new = fmaxf(m[rt], row_max4(mx));
+                for (int r = 0; r < 4; ++r)
+                    mx = fmaxf(mx, MASKED && key0 + 16 * t + r >= p.sk ? -INFINITY : s[rt][t][r]);
+            const float m_new = fmaxf(m[rt], row_max4(mx) * c);
             const float corr = __builtin_amdgcn_exp2f(m[rt] - m_new);
             m[rt] = m_new;
             float sum = 0.0f;
@@ -193,16 +216,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(s[rt][t][r] - m_new);
+                    float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][t][r], c, -m_new));
+                    if (MASKED)
+                        e = key0 + 16 * t + r < p.sk ? e : 0.0f;
                     s[rt][t][r] = e;
                     sum += e;
                 }
             l[rt] = l[rt] * corr + sum;
-#pragma unroll
-            for (int dt = 0; dt < HD / 16; ++dt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[rt][dt][r] *= corr;
+            corr_[rt] = corr;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 pf[rt][kk] = u32x4{Pack16<T>::two(s[rt][2 * kk][0], s[rt][2 * kk][1]),
@@ -210,19 +231,84 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
                                    Pack16<T>::two(s[rt][2 * kk + 1][0], s[rt][2 * kk + 1][1]),
                                    Pack16<T>::two(s[rt][2 * kk + 1][2], s[rt][2 * kk + 1][3])};
         }
-
-        // O += P V
+    };
+    // O = corr O + P V for the V block at vt (each O tile rescaled right before its first product)
+    auto pv = [&](const u32x4 (&pf)[2][2], const char *vt) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int dt = 0; dt < HD / 16; ++dt) {
-                const u32x4 vf = VT::frag_split(cur + KBYTES, 16 * dt, kk, lane);
+                const u32x4 vf = VT::frag_split(vt, 16 * dt, kk, lane);
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < 2; ++rt) {
+                    if (kk == 0)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            o[rt][dt][r] *= corr_[rt];
                     o[rt][dt] = Mfma<T>::step(vf, pf[rt][kk], o[rt][dt]);
+                }
             }
+    };
+    // One pipelined step j (j + 1 < nblk; PAR = (j + shift) mod 2).  LDS holds
+    // K block j+1 (K buffer 1-PAR) and V block j (V buffer PAR); the staging registers
+    // hold K block j+2 and V block j+1.  The scores of block j+1 are computed
+    // while block j's softmax runs, then O += P V for block j; K block j+2
+    // goes to K buffer PAR (block j's, last read in step j-1) and V block j+1
+    // to V buffer 1-PAR (block j-1's), and the next two blocks are fetched.
+    auto step = [&](int j, auto par) {
+        constexpr int PAR = decltype(par)::value ? 1 : 0;
+        f32x4 (&s_cur)[2][4] = PAR ? sb : sa;
+        f32x4 (&s_nxt)[2][4] = PAR ? sa : sb;
+        scores(s_nxt, kbuf + (1 - PAR) * KBYTES);
+        u32x4 pf[2][2];
+        softmax(s_cur, pf, j, Bool<false>());
+        pv(pf, vbuf + PAR * VBYTES);
+        store_k(kbuf + PAR * KBYTES);
+        store_v(vbuf + (1 - PAR) * VBYTES);
+        load_k(j + 3);
+        load_v(j + 2);
         stage_barrier();
+    };
+    // the last block (scores already in s_cur, V in buffer PAR)
+    auto last = [&](int j, auto par) {
+        constexpr int PAR = decltype(par)::value ? 1 : 0;
+        f32x4 (&s_cur)[2][4] = PAR ? sb : sa;
+        u32x4 pf[2][2];
+        softmax(s_cur, pf, j, Bool<true>());
+        pv(pf, vbuf + PAR * VBYTES);
+    };
+
+    // Block j's K and V live in buffers (j + shift) mod 2 and its scores in sa
+    // or sb by the same parity; shift = nblk mod 2 makes the last block odd,
+    // so that the loop body is a fixed pair of steps (one step is peeled off
+    // the front when the number of steps, nblk - 1, is odd).
+    const int shift = nblk & 1;
+    // prologue: K0 and V0, the scores of block 0, K1; K2 and V1 wait in the staging registers
+    load_k(0);
+    load_v(0);
+    store_k(kbuf + shift * KBYTES);
+    store_v(vbuf + shift * VBYTES);
+    load_k(1);
+    load_v(1);
+    stage_barrier();
+    if (shift)
+        scores(sb, kbuf + KBYTES);
+    else
+        scores(sa, kbuf);
+    store_k(kbuf + (1 - shift) * KBYTES);
+    load_k(2);
+    stage_barrier();
+
+    int j = 0;
+    if (!shift) { // nblk even (>= 2): an odd number of steps
+        step(0, Bool<false>());
+        j = 1;
     }
+    for (; j + 1 < nblk; j += 2) {
+        step(j, Bool<true>());
+        step(j + 1, Bool<false>());
+    }
+    last(nblk - 1, Bool<true>());
 
     // O / l, each row's sum added up over the four lanes that hold its parts
     char *Ob = p.O + b * p.stride_o * (int64_t)sizeof(ot);

@@ -69,7 +69,8 @@ def _pick(means, counter, pred):
 
 
 def is_gemm(name: str) -> bool:
-    return "dmu::gemm_" in name
+    """A kernel of this library (GEMM kernels and the fused attention kernel)."""
+    return "dmu::gemm_" in name or "attn_fwd" in name
 
 
 def is_copy(name: str) -> bool:
@@ -102,7 +103,7 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
         avg, n = _timed_average_us(_rows(os.path.join(d, "trace", "**", "*kernel_trace.csv")), timed)
         if avg is not None:
             result["avg_us"] = avg
-            lines += ["", f"GEMM dispatches timed by the benchmark (the last {n}, after the warm-up that "
+            lines += ["", f"Library-kernel dispatches timed by the benchmark (the last {n}, after the warm-up that "
                           f"raises the clock): average {avg:.2f} us."]
         open(os.path.join(profiles, f"{kernel_label}_{workload_name}_kernel_trace.md"), "w").write(
             "\n".join(lines) + "\n")
@@ -132,7 +133,7 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
               f"Calibration: a plain device copy of {COPY_MIB} MiB reads FETCH_SIZE = {f_copy:.0f} KiB "
               f"and WRITE_SIZE = {w_copy:.0f} KiB, so the factors are {f_factor:.3f} (fetch) and "
               f"{w_factor:.3f} (write).", "",
-              "| per GEMM launch | counter (KiB) | calibrated bytes |", "|---|---|---|",
+              "| per kernel launch | counter (KiB) | calibrated bytes |", "|---|---|---|",
               f"| FETCH_SIZE | {f_gemm:.0f} | {fetch_b / 1e6:.1f} MB |",
               f"| WRITE_SIZE | {w_gemm:.0f} | {write_b / 1e6:.1f} MB |",
               f"| total | | {(fetch_b + write_b) / 1e6:.1f} MB |", "",
@@ -149,7 +150,7 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
         conflict, active = get("SQ_LDS_BANK_CONFLICT"), get("SQ_LDS_IDX_ACTIVE")
         md = [f"# Matrix-core and LDS counters: {workload_name}", "",
               "Command (from the repository root on the GPU host):", "", "```", commands["sq"], "```", "",
-              "| counter (per GEMM dispatch, summed over the chip) | value |", "|---|---|"]
+              "| counter (per kernel dispatch, summed over the chip) | value |", "|---|---|"]
         for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
                   "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"):
             v = get(c)

@@ -148,3 +148,26 @@ def test_full_size_sampled_rows():
                            {(int(rng.integers(32)), int(rng.integers(4096))) for _ in range(120)}))
     want = att.want_rows(rows)
     check(att, np.stack([got[b, i] for b, i in rows]), want)
+
+
+@pytest.mark.parametrize("scale", [-0.25, -1.0 / math.sqrt(HD)])
+def test_negative_scale(scale):
+    """A negative scale: the kernel negates Q (exactly) and uses |scale|."""
+    att = Att(2, 100, 150, "bf16", "f32", 8, scale=scale)
+    check(att, att.run(), att.want())
+
+
+def test_zero_scale_is_mean_of_v():
+    """scale = 0: every key gets the same weight, so O(i) is the mean of V's rows for every query."""
+    att = Att(1, 40, 130, "f16", "f32", 9, scale=0.0)
+    got = att.run()
+    check(att, got, att.want())
+    mean = gu.values(att.V, "f16").reshape(130, HD).mean(axis=0)
+    assert np.max(np.abs(got[0] - mean)) <= 2 * UNIT["f16"] + 1e-6
+
+
+@pytest.mark.parametrize("batch,sq", [(13, 20), (5, 600)])
+def test_grid_not_a_multiple_of_eight(batch, sq):
+    """Workgroup counts of 13 and 15 cover every query row once after the XCD renumbering."""
+    att = Att(batch, sq, 70, "f16", "f16", 10)
+    check(att, att.run(), att.want())
