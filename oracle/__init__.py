@@ -19,10 +19,11 @@ import numpy as np
 
 from .build import LIB_PATH, build
 
-TYPES = {"f16": 1, "bf16": 2, "f32": 3, "i8": 4, "i32": 5}
+TYPES = {"f16": 1, "bf16": 2, "f32": 3, "i8": 4, "i32": 5, "e4m3": 6}
 LAYOUTS = {"row": 0, "col": 1}
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2}
-_NP_IN = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32, "i8": np.int8, "i32": np.int32}
+_NP_IN = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32, "i8": np.int8, "i32": np.int32,
+          "e4m3": np.uint8}
 
 _lib = None
 
@@ -52,6 +53,8 @@ def _load():
     lib.oracle_attention_rows.restype = i32
     lib.oracle_decode_array.argtypes = [i32, vp, vp, i64]
     lib.oracle_decode_array.restype = None
+    lib.oracle_decode_array8.argtypes = [i32, vp, vp, i64]
+    lib.oracle_decode_array8.restype = None
     lib.oracle_encode_array.argtypes = [i32, vp, vp, i64]
     lib.oracle_encode_array.restype = None
     _lib = lib
@@ -88,7 +91,7 @@ def _prep(x, t, need, name):
 
 def _common(M, N, K, A, lda, B, ldb, in_type, out_type, layout_a, layout_b, batch,
             stride_a, stride_b, C, ldc, stride_c):
-    if in_type not in ("f16", "bf16", "f32", "i8"):
+    if in_type not in ("f16", "bf16", "f32", "i8", "e4m3"):
         raise ValueError(f"unsupported input type {in_type}")
     acc_t = out_type  # C has the output type
     span = lambda s, e: 0 if batch == 0 or e == 0 else (batch - 1) * s + e
@@ -157,7 +160,12 @@ def gemm_at(M, N, K, A, lda, B, ldb, bij, *, in_type, out_type, layout_a="row",
 
 
 def decode(t: str, bits) -> np.ndarray:
-    """Exact fp64 values of fp16 or bf16 bit patterns."""
+    """Exact fp64 values of fp16, bf16 or e4m3 bit patterns."""
+    if t == "e4m3":
+        bits = np.ascontiguousarray(bits, dtype=np.uint8).reshape(-1)
+        out = np.empty(bits.size, dtype=np.float64)
+        _load().oracle_decode_array8(TYPES[t], _ptr(bits), _ptr(out), bits.size)
+        return out
     bits = np.ascontiguousarray(bits, dtype=np.uint16).reshape(-1)
     out = np.empty(bits.size, dtype=np.float64)
     _load().oracle_decode_array(TYPES[t], _ptr(bits), _ptr(out), bits.size)

@@ -21,7 +21,9 @@
  *   - Layout-experiment post (KingOfEgg, RTX 5080), section 3: D = A x B + C
  *     with an fp32 accumulator as the floor for long accumulations.
  *
- * Floating-point inputs (fp16, bf16, fp32) are decoded to exact fp64 values by
+ * Floating-point inputs (fp16, bf16, fp32, and FP8 e4m3 -- "Tensor Cores,
+ * CUTLASS and CuTe", section 2.1 lists e4m3 inputs with an fp32 accumulator,
+ * section 6.5 the FP8 scaled GEMM) are decoded to exact fp64 values by
  * this file's own codecs; every product of two such values is exact in fp64,
  * and the products are summed in fp64 in increasing k.  C is added in fp64,
  * and the result is rounded ONCE, with IEEE round-to-nearest-even, directly
@@ -66,7 +68,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 1, OR_BF16 = 2, OR_F32 = 3, OR_I8 = 4, OR_I32 = 5 };
+enum { OR_F16 = 1, OR_BF16 = 2, OR_F32 = 3, OR_I8 = 4, OR_I32 = 5, OR_E4M3 = 6 };
 enum { OR_ROW = 0, OR_COL = 1 };
 enum { OR_ACT_NONE = 0, OR_ACT_RELU = 1, OR_ACT_GELU_TANH = 2 };
 
@@ -99,6 +101,23 @@ double oracle_decode_bf16(uint16_t h)
         v = m ? NAN : INFINITY;
     else
         v = ldexp((double)(m | 0x80), e - 134); /* (128+m) * 2^(e-127-7) */
+    return s ? -v : v;
+}
+
+/* FP8 e4m3 (the pages' 8-bit input type; the "FN" form of the OCP 8-bit
+ * formats): 1 sign, 4 exponent (bias 7), 3 stored mantissa bits, no
+ * infinities; exponent and mantissa all ones is NaN, so the largest finite
+ * value is 1.75 * 2^8 = 448. */
+double oracle_decode_e4m3(uint8_t h)
+{
+    int s = (h >> 7) & 1, e = (h >> 3) & 0xf, m = h & 0x7;
+    double v;
+    if (e == 0xf && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9); /* subnormal: m * 2^(1-7-3) */
+    else
+        v = ldexp((double)(m | 0x8), e - 10); /* (8+m) * 2^(e-7-3) */
     return s ? -v : v;
 }
 
@@ -155,6 +174,12 @@ void oracle_decode_array(int type, const uint16_t *in, double *out, int64_t n)
         out[i] = type == OR_F16 ? oracle_decode_f16(in[i]) : oracle_decode_bf16(in[i]);
 }
 
+void oracle_decode_array8(int type, const uint8_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = type == OR_E4M3 ? oracle_decode_e4m3(in[i]) : NAN;
+}
+
 void oracle_encode_array(int type, const double *in, void *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) {
@@ -176,6 +201,7 @@ static double load_fp(const void *p, int type, int64_t idx)
     switch (type) {
     case OR_F16: return oracle_decode_f16(((const uint16_t *)p)[idx]);
     case OR_BF16: return oracle_decode_bf16(((const uint16_t *)p)[idx]);
+    case OR_E4M3: return oracle_decode_e4m3(((const uint8_t *)p)[idx]);
     default: return (double)((const float *)p)[idx]; /* fp32 -> fp64 is exact */
     }
 }
@@ -223,7 +249,7 @@ typedef struct {
     int status;
 } job_t;
 
-static int is_fp_in(int t) { return t == OR_F16 || t == OR_BF16 || t == OR_F32; }
+static int is_fp_in(int t) { return t == OR_F16 || t == OR_BF16 || t == OR_F32 || t == OR_E4M3; }
 
 static int check_args(const job_t *j)
 {

@@ -78,7 +78,22 @@ def round32(x: Fraction) -> np.float32:
     return best
 
 
+@lru_cache(maxsize=None)
+def _e4m3_table():
+    """The 256 e4m3 code values through torch's float8_e4m3fn conversion (a library routine)."""
+    import torch
+
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def e4m3_values(bits: np.ndarray) -> np.ndarray:
+    return _e4m3_table()[np.asarray(bits, dtype=np.uint8)]
+
+
 def exact_value(bits, t: str) -> Fraction:
+    if t == "e4m3":
+        return Fraction(float(_e4m3_table()[int(bits)]))
     if t == "f16":
         return Fraction(f16_value(int(bits)))
     if t == "bf16":

@@ -4,7 +4,7 @@ Each case below plants one mistake in a copy of ``oracle/oracle.c`` (a dropped
 term, a wrong sign, index or stride, a transposed operand, a wrong rounding
 rule, a wrong codec constant), builds that copy into a temporary library, and
 runs the oracle pin suite (tests/test_oracle_gemm.py, tests/test_oracle_codecs.py,
-tests/test_oracle_epilogue.py, tests/test_oracle_attention.py)
+tests/test_oracle_epilogue.py, tests/test_oracle_attention.py, tests/test_oracle_fp8.py)
 against it in a child process.  The suite must fail for every mutant; a mutant
 that survives is a mistake the pins would not see.
 """
@@ -77,6 +77,13 @@ MUTANTS = [
     ("int32 saturates", "static int32_t wrap_i32(int64_t v) { return (int32_t)(uint32_t)(uint64_t)v; }",
      "static int32_t wrap_i32(int64_t v) { return v > INT32_MAX ? INT32_MAX : "
      "(v < INT32_MIN ? INT32_MIN : (int32_t)v); }"),
+    ("e4m3 exponent bias", "ldexp((double)(m | 0x8), e - 10);", "ldexp((double)(m | 0x8), e - 11);"),
+    ("e4m3 subnormal scale", "ldexp((double)m, -9);", "ldexp((double)m, -10);"),
+    ("e4m3 all-ones exponent taken as infinity", "if (e == 0xf && m == 0x7)\n        return NAN;",
+     "if (e == 0xf)\n        return m ? NAN : INFINITY;"),
+    ("e4m3 sign ignored", "    return s ? -v : v;\n}\n\n/*\n * Round x", "    return v;\n}\n\n/*\n * Round x"),
+    ("e4m3 read as a 16-bit type", "case OR_E4M3: return oracle_decode_e4m3(((const uint8_t *)p)[idx]);",
+     "case OR_E4M3: return oracle_decode_e4m3((uint8_t)((const uint16_t *)p)[idx]);"),
     ("attention: K indexed (d, key)", "b * a->stride_k + j * a->ldk + t", "b * a->stride_k + t * a->ldk + j"),
     ("attention: batch stride of V ignored", "b * a->stride_v + j * a->ldv + c", "0 * a->stride_v + j * a->ldv + c"),
     ("attention: last key dropped", "for (int64_t j = 0; j < a->sk; ++j) {\n        const double w",
@@ -96,7 +103,8 @@ RUNNER = (
     "oracle.LIB_PATH = sys.argv[1]\n"
     "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '--no-header',\n"
     "                      'tests/test_oracle_gemm.py', 'tests/test_oracle_codecs.py',\n"
-    "                      'tests/test_oracle_epilogue.py', 'tests/test_oracle_attention.py']))\n"
+    "                      'tests/test_oracle_epilogue.py', 'tests/test_oracle_attention.py',\n"
+    "                      'tests/test_oracle_fp8.py']))\n"
 )
 
 

@@ -84,6 +84,11 @@ def to_bits(x: np.ndarray, t: str) -> np.ndarray:
 
         f = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
         return f.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if t == "e4m3":
+        import torch
+
+        f = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        return f.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     if t == "f32":
         return np.asarray(x, dtype=np.float32)
     if t == "i8":
