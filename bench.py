@@ -11,7 +11,7 @@ measures that ramp instead of the kernel.  Prints one JSON
 line with the throughput, the MFMA roofline of the kernel and the CPU oracle's
 rate on a bounded row slice of the same product.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c4fa]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c6|c4fa]
                   [--no-cpu-baseline] [--copy-calibration MiB]
   python bench.py --summarize DIR [--workload W]   (rocprofv3 output -> profiles/)
 """
@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X published dense peaks (matrix cores), TFLOP/s or TOP/s, and HBM3E bandwidth.
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "i8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "i8": 5000.0, "e4m3": 5000.0}
 PEAK_HBM_GBS = 8000.0
 
 WORKLOAD_NAMES = {
@@ -39,6 +39,7 @@ WORKLOAD_NAMES = {
     "c4s": "batched32_gemm_4096x4096x128_f16_tn_f32out",
     "c4o": "batched32_gemm_4096x128x4096_f16_nn_f32out",
     "c5": "gemm_8192x8192x8192_i8_tn_i32out",
+    "c6": "gemm_8192x8192x8192_e4m3_tn_f32acc_bf16out",
     "c5dq": "gemm_8192x8192x8192_i8_tn_dequant_rowcol_scale_bias_gelu_bf16out",
 }
 

@@ -20,7 +20,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdmu.so")
 
-DMU_F16, DMU_BF16, DMU_F32, DMU_I8, DMU_I32 = 1, 2, 3, 4, 5
+DMU_F16, DMU_BF16, DMU_F32, DMU_I8, DMU_I32, DMU_E4M3 = 1, 2, 3, 4, 5, 6
 DMU_ROW_MAJOR, DMU_COL_MAJOR = 0, 1
 DMU_OK, DMU_ERR_INVALID_ARG, DMU_ERR_UNSUPPORTED, DMU_ERR_HIP = 0, -1, -2, -3
 
@@ -30,6 +30,7 @@ DMU_PROBE_MFMA_16x16x32_BF16 = 3
 DMU_PROBE_MFMA_16x16x32_F16 = 4
 DMU_PROBE_MFMA_32x32x32_I8 = 5
 DMU_PROBE_MFMA_16x16x64_I8 = 6
+DMU_PROBE_MFMA_16x16x128_E4M3 = 7
 DMU_PROBE_LDS_READ_B128 = 10
 DMU_PROBE_LDS_READ_TR16 = 11
 DMU_PROBE_LDS_FRAG = 12
@@ -37,7 +38,7 @@ DMU_PROBE_LDS_FRAG_T = 13
 DMU_PROBE_CVT_BF16 = 30
 DMU_PROBE_CVT_F16 = 31
 
-DTYPES = {"f16": DMU_F16, "bf16": DMU_BF16, "f32": DMU_F32, "i8": DMU_I8, "i32": DMU_I32}
+DTYPES = {"f16": DMU_F16, "bf16": DMU_BF16, "f32": DMU_F32, "i8": DMU_I8, "i32": DMU_I32, "e4m3": DMU_E4M3}
 LAYOUTS = {"row": DMU_ROW_MAJOR, "col": DMU_COL_MAJOR}
 
 

@@ -13,6 +13,12 @@
 //       X[row = l % 16][k = 8 (l / 16) + s], s = 0..7  (16 contiguous bytes)
 //     accumulator register r of lane l holds D[row = 4 (l / 16) + r][col = l % 16]
 //   v_mfma_i32_16x16x64_i8: the same with 16 int8 per lane, k = 16 (l / 16) + s.
+//   v_mfma_f32_16x16x128_f8f6f4 (e4m3 operands): 32 bytes per lane -- a whole
+//       128-byte K-tile row shared by 4 lanes; the kernels give lane l the two
+//       16-byte fragments of the 16-bit instructions' two K-steps, bytes
+//       16 (l / 16) .. +15 and 64 + 16 (l / 16) .. +15 of row l % 16, for A and
+//       B alike, so every k of the row meets its partner (probed); the
+//       accumulator layout is that of the 16-bit instructions.
 // Both operands are "row of X with contiguous k", so the kernels keep operand
 // tiles in LDS as rows of 128 bytes (one K-tile: 64 fp16/bf16 or 128 int8
 // values, two K-steps) and read one 16-byte fragment per lane.  The 32 x 32
@@ -37,10 +43,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Dt { F16 = 1, BF16 = 2, F32 = 3, I8 = 4, I32 = 5 };
+enum Dt { F16 = 1, BF16 = 2, F32 = 3, I8 = 4, I32 = 5, E4M3 = 6 };
 
 // Operand load modes of the tiled kernel.
 enum Mode {
@@ -50,7 +57,7 @@ enum Mode {
 };
 
 // Bytes of one element of a type code.
-__host__ __device__ constexpr int dt_bytes(int t) { return (t == F32 || t == I32) ? 4 : (t == I8 ? 1 : 2); }
+__host__ __device__ constexpr int dt_bytes(int t) { return (t == F32 || t == I32) ? 4 : (t == I8 || t == E4M3 ? 1 : 2); }
 
 // ---------------------------------------------------------------------------
 // MFMA wrappers: one 16 x 16 x (32 fp16/bf16 | 64 int8) step, 16-byte operands.
@@ -79,6 +86,24 @@ template <> struct Mfma<I8> {
     {
         return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, x), __builtin_bit_cast(i32x4, y), c, 0,
                                                      0, 0);
+    }
+};
+
+// One 16 x 16 x 128 e4m3 step over a whole 128-byte K-tile row: operands are
+// the two 16-byte fragments (K-steps 0 and 1 of the 16-bit layout) of each
+// side.  Format code 0 (e4m3) for both operands; the scale operands are zero,
+// which selects the unscaled instruction.
+template <> struct Mfma<E4M3> {
+    typedef f32x4 acc_t;
+    static __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi)
+    {
+        const uint32_t a0 = lo[0], a1 = lo[1], a2 = lo[2], a3 = lo[3];
+        const uint32_t b0 = hi[0], b1 = hi[1], b2 = hi[2], b3 = hi[3];
+        return i32x8{(int)a0, (int)a1, (int)a2, (int)a3, (int)b0, (int)b1, (int)b2, (int)b3};
+    }
+    static __device__ __forceinline__ acc_t step2(u32x4 x0, u32x4 x1, u32x4 y0, u32x4 y1, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(join(x0, x1), join(y0, y1), c, 0, 0, 0, 0, 0, 0);
     }
 };
 

@@ -50,7 +50,7 @@ struct Plan {
 
 constexpr int64_t LIM31 = (int64_t)1 << 31;
 
-int elem_bytes(int t) { return (t == DMU_F32 || t == DMU_I32) ? 4 : (t == DMU_I8 ? 1 : 2); }
+int elem_bytes(int t) { return (t == DMU_F32 || t == DMU_I32) ? 4 : (t == DMU_I8 || t == DMU_E4M3 ? 1 : 2); }
 
 // Supported (in, acc, out) triples -> launcher index.
 int combo_of(int in, int acc, int out)
@@ -64,12 +64,16 @@ int combo_of(int in, int acc, int out)
     if (in == DMU_I8 && acc == DMU_I32 && out == DMU_F32) return 5;  // dequantising outputs
     if (in == DMU_I8 && acc == DMU_I32 && out == DMU_F16) return 6;
     if (in == DMU_I8 && acc == DMU_I32 && out == DMU_BF16) return 7;
+    if (in == DMU_E4M3 && acc == DMU_F32 && out == DMU_F32) return 8;
+    if (in == DMU_E4M3 && acc == DMU_F32 && out == DMU_F16) return 9;
+    if (in == DMU_E4M3 && acc == DMU_F32 && out == DMU_BF16) return 10;
     return -1;
 }
 
-constexpr int NUM_COMBOS = 8;
+constexpr int NUM_COMBOS = 11;
 const char *const COMBO_NAMES[NUM_COMBOS] = {"f16_f32", "f16_f16", "bf16_bf16", "bf16_f32",
-                                             "i8_i32",  "i8_f32",  "i8_f16",    "i8_bf16"};
+                                             "i8_i32",  "i8_f32",  "i8_f16",    "i8_bf16",
+                                             "e4m3_f32", "e4m3_f16", "e4m3_bf16"};
 
 // Names of every kernel variant, built once (thread-safe static init).
 struct NameTable {
@@ -246,6 +250,8 @@ int validate(const dmu_gemm_args *a, Plan *plan)
         if (env && strcmp(env, "256x256") == 0) tile = TILE_256x256;
         if (env && strcmp(env, "256x128") == 0) tile = TILE_256x128;
         if (env && strcmp(env, "128x128") == 0) tile = TILE_128x128;
+        if (a->in_type == DMU_E4M3 && tile == TILE_256x256)
+            tile = TILE_256x128; // e4m3 fragments need the registers of a 64 x 64 wavefront tile
     }
     const int64_t bm = tile_bm(tile), bn = tile_bn(tile);
     const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
@@ -391,7 +397,10 @@ extern "C" int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, vo
     case 4: e = launch_i8_i32(plan.cfg, plan.p, s); break;
     case 5: e = launch_i8_f32(plan.cfg, plan.p, s); break;
     case 6: e = launch_i8_f16(plan.cfg, plan.p, s); break;
-    default: e = launch_i8_bf16(plan.cfg, plan.p, s); break;
+    case 7: e = launch_i8_bf16(plan.cfg, plan.p, s); break;
+    case 8: e = launch_e4m3_f32(plan.cfg, plan.p, s); break;
+    case 9: e = launch_e4m3_f16(plan.cfg, plan.p, s); break;
+    default: e = launch_e4m3_bf16(plan.cfg, plan.p, s); break;
     }
     if (e != hipSuccess) {
         set_error("dmu_gemm: launch of %s failed: %s", plan.name, hipGetErrorString(e));

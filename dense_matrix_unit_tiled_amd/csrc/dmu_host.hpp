@@ -43,5 +43,8 @@ hipError_t launch_i8_i32(const LaunchCfg &c, const GemmParams &p, hipStream_t s)
 hipError_t launch_i8_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 hipError_t launch_i8_f16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 hipError_t launch_i8_bf16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_e4m3_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_e4m3_f16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
+hipError_t launch_e4m3_bf16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 
 } // namespace dmu

@@ -5,9 +5,9 @@
 //              two barriers per K-tile (the simplest correct form, as in the
 //              "hgemm_mma_m16n8k16_mma2x4_warp4x4_kernel" walkthrough).  Every
 //              output element goes through the same sequence of 16 x 16 x 32
-//              (int8: x 64) matrix instructions over the same K-steps as in the
-//              tiled kernel, so the two give bit-identical results on the same
-//              inputs.
+//              (int8: x 64; e4m3: one x 128 per K-tile) matrix instructions
+//              over the same K-steps as in the tiled kernel, so the two give
+//              bit-identical results on the same inputs.
 #pragma once
 
 #include "dmu_tiled.hpp"
@@ -18,6 +18,7 @@ template <int T> struct In;
 template <> struct In<F16> { static constexpr int bytes = 2; };
 template <> struct In<BF16> { static constexpr int bytes = 2; };
 template <> struct In<I8> { static constexpr int bytes = 1; };
+template <> struct In<E4M3> { static constexpr int bytes = 1; };
 
 template <int T, int E> struct Elem;
 template <int T> struct Elem<T, 2> { typedef uint16_t t; };
@@ -80,19 +81,35 @@ __global__ void __launch_bounds__(256) gemm_generic(GemmParams p)
         generic_fill<T>(smem, Ab, p.lda, p.a_kc != 0, m0, p.M, k0, p.K, tid);
         generic_fill<T>(smem + 64 * 128, Bb, p.ldb, p.b_kc != 0, n0, p.N, k0, p.K, tid);
         __syncthreads();
+        if constexpr (T == E4M3) { // one MFMA over both K-step halves, as in the tiled kernel
+            u32x4 af[2][2], bf[2][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 af[2], bf[2];
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = Frag::frag(smem, wm * 32 + 16 * i, ks, lane);
-                bf[i] = Frag::frag(smem + 64 * 128, wn * 32 + 16 * i, ks, lane);
-            }
+                for (int h = 0; h < 2; ++h) {
+                    af[i][h] = Frag::frag(smem, wm * 32 + 16 * i, h, lane);
+                    bf[i][h] = Frag::frag(smem + 64 * 128, wn * 32 + 16 * i, h, lane);
+                }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = Mfma<T>::step(bf[j], af[i], acc[i][j]);
+                    acc[i][j] = Mfma<E4M3>::step2(bf[j][0], bf[j][1], af[i][0], af[i][1], acc[i][j]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u32x4 af[2], bf[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    af[i] = Frag::frag(smem, wm * 32 + 16 * i, ks, lane);
+                    bf[i] = Frag::frag(smem + 64 * 128, wn * 32 + 16 * i, ks, lane);
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = Mfma<T>::step(bf[j], af[i], acc[i][j]);
+            }
         }
         __syncthreads();
     }

@@ -55,6 +55,16 @@ __global__ void __launch_bounds__(64) probe_mfma(const char *a, const char *bt, 
                                                   0);
         for (int r = 0; r < 16; ++r)
             out[l * 16 + r] = (uint32_t)c[r];
+    } else if (V == DMU_PROBE_MFMA_16x16x128_E4M3) {
+        // the GEMM kernels' two 16-byte fragments of a 128-byte row: bytes
+        // 16 (l / 16) .. +15 and 64 + 16 (l / 16) .. +15 of row l % 16
+        const u32x4 x0 = probe_frag(a, 16, 128, l), x1 = probe_frag(a + 64, 16, 128, l);
+        const u32x4 y0 = probe_frag(bt, 16, 128, l), y1 = probe_frag(bt + 64, 16, 128, l);
+        const f32x4 c = Mfma<E4M3>::step2(x0, x1, y0, y1, f32x4{});
+        for (int r = 0; r < 4; ++r) {
+            const float v = c[r];
+            out[l * 4 + r] = __builtin_bit_cast(uint32_t, v);
+        }
     } else if (V == DMU_PROBE_MFMA_16x16x64_I8) {
         const u32x4 x = probe_frag(a, 16, 64, l), y = probe_frag(bt, 16, 64, l);
         i32x4 c = {};
@@ -176,6 +186,7 @@ extern "C" int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type,
     case DMU_PROBE_MFMA_16x16x32_F16: mm = 16, nn = 16, kk = 32, t = DMU_F16, r = 4; break;
     case DMU_PROBE_MFMA_32x32x32_I8: mm = 32, nn = 32, kk = 32, t = DMU_I8, r = 16; break;
     case DMU_PROBE_MFMA_16x16x64_I8: mm = 16, nn = 16, kk = 64, t = DMU_I8, r = 4; break;
+    case DMU_PROBE_MFMA_16x16x128_E4M3: mm = 16, nn = 16, kk = 128, t = DMU_E4M3, r = 4; break;
     case DMU_PROBE_LDS_READ_B128: r = 4; break;
     case DMU_PROBE_LDS_READ_TR16: r = 2; break;
     case DMU_PROBE_LDS_FRAG: r = 16; break;
@@ -217,6 +228,7 @@ extern "C" int dmu_probe(int variant, const void *in0, const void *in1, void *ou
         DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_16x16x32_F16)
         DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_32x32x32_I8)
         DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_16x16x64_I8)
+        DMU_PROBE_MFMA_CASE(DMU_PROBE_MFMA_16x16x128_E4M3)
 #undef DMU_PROBE_MFMA_CASE
     case DMU_PROBE_LDS_READ_B128:
         hipLaunchKernelGGL(probe_lds_b128, dim3(1), dim3(64), 0, s, a, reinterpret_cast<const int32_t *>(b), o);

@@ -3,7 +3,9 @@
 // A workgroup of 8 wavefronts (WGM x WGN) computes a BM x BN tile of D; each
 // wavefront owns an (BM/WGM) x (BN/WGN) block of 16 x 16 MFMA tiles.  K is
 // walked in K-tiles of 128 bytes per row (64 fp16/bf16 or 128 int8 values),
-// each two K-steps of the 16 x 16 instructions.  Three-level tiling
+// each two K-steps of the 16 x 16 instructions; 128 e4m3 values make one
+// 16 x 16 x 128 step ("Tensor Cores, CUTLASS and CuTe" section 6.5: FP8's
+// BK = 128 moves the bytes of BF16's BK = 64).  Three-level tiling
 // (workgroup, wavefront, instruction) as in the
 // "hgemm_mma_m16n8k16_mma2x4_warp4x4_kernel" walkthrough (sections 2-6) and
 // "Tensor Cores, CUTLASS and CuTe" section 4.2, re-sized for 64-lane
@@ -309,7 +311,9 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
 __global__ void __launch_bounds__(64 * WGM * WGN)
     __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tiled(GemmParams p)
 {
-    constexpr int E = T == I8 ? 1 : 2;
+    constexpr bool F8 = T == E4M3;           // one 16 x 16 x 128 MFMA per K-tile and tile
+    constexpr int E = (T == I8 || F8) ? 1 : 2;
+    constexpr int FH = F8 ? 2 : 1;           // 16-byte fragment halves an MFMA reads
     constexpr int NW = WGM * WGN;
     static_assert(NW == 8, "eight wavefronts, two per SIMD");
     constexpr int WTM = BM / WGM, WTN = BN / WGN; // wavefront tile
@@ -318,6 +322,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     static_assert(MT % 2 == 0, "a K-step runs in two halves of the tile rows");
     static_assert(AMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(BMODE != MC16 || E == 2, "transposed operands are 16-bit");
+    static_assert(!F8 || MN <= 16, "e4m3 fragments (8 registers per tile) fit beside the accumulators");
     typedef typename Mfma<T>::acc_t acc_t;
     typedef typename TileOf<AMODE, BM, NW>::type ATile;
     typedef typename TileOf<BMODE, BN, NW>::type BTile;
@@ -374,10 +379,24 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         for (int j = 0; j < NT; ++j)
             acc[i][j] = acc_t{};
 
-    u32x4 af[MT], bfr[NT];
-    auto read_a = [&](int i, const char *stage, int ks) { af[i] = ATile::frag(stage, wm * WTM + i * 16, ks, lane); };
+    // Operand fragments of one K-step (e4m3: both K-step halves of the K-tile,
+    // which one MFMA consumes together).
+    u32x4 af[MT][FH], bfr[NT][FH];
+    auto read_a = [&](int i, const char *stage, int ks) {
+#pragma unroll
+        for (int h = 0; h < FH; ++h)
+            af[i][h] = ATile::frag(stage, wm * WTM + i * 16, F8 ? h : ks, lane);
+    };
     auto read_b = [&](int j, const char *stage, int ks) {
-        bfr[j] = BTile::frag(stage + ABYTES, wn * WTN + j * 16, ks, lane);
+#pragma unroll
+        for (int h = 0; h < FH; ++h)
+            bfr[j][h] = BTile::frag(stage + ABYTES, wn * WTN + j * 16, F8 ? h : ks, lane);
+    };
+    auto mfma = [&](int i, int j) {
+        if constexpr (F8)
+            acc[i][j] = Mfma<E4M3>::step2(bfr[j][0], bfr[j][1], af[i][0], af[i][1], acc[i][j]);
+        else
+            acc[i][j] = Mfma<T>::step(bfr[j][0], af[i][0], acc[i][j]);
     };
 
     const int nk = (int)(((int64_t)p.K * E + 127) / 128);
@@ -417,6 +436,41 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     // first half of K-step 1, ahead of the stage hand-over.  K-tiles past K
     // read as zeros through the range check, so the body is branch-free.
     constexpr int SLOTS = MN + HALF;
+    if constexpr (F8) {
+        // e4m3: one K-step per K-tile.  First half: the staging copies; the
+        // barrier; second half: each fragment of K-tile kt+1 is read from the
+        // other stage right after its last use (the first half's A rows at
+        // once).  Every read of a stage happens before the barrier that
+        // precedes its overwrite.
+        for (int kt = 0; kt < nk; ++kt) {
+            char *nxt = smem + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+            for (int q = 0; q < HALF; ++q) {
+                mfma(row_of(q), col_of(q));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ci = q * NLD / HALF; ci < (q + 1) * NLD / HALF; ++ci) {
+                    store_one(ci, nxt, kt + 1);
+                    load_one(ci, kt + 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            stage_barrier();
+#pragma unroll
+            for (int q = HALF; q < MN; ++q) {
+                const int i = row_of(q), j = col_of(q), h = q - HALF;
+                mfma(i, j);
+                __builtin_amdgcn_sched_barrier(0);
+                if (h < HM)
+                    read_a(h, nxt, 0);
+                if (q == last_b(j))
+                    read_b(j, nxt, 0);
+                if (q == last_a(i))
+                    read_a(i, nxt, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else
     for (int kt = 0; kt < nk; ++kt) {
         const char *cur = smem + (kt & 1) * STAGE;
         char *nxt = smem + ((kt + 1) & 1) * STAGE;
@@ -424,7 +478,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
 #pragma unroll
         for (int q = 0; q < MN; ++q) {
             const int i = row_of(q), j = col_of(q);
-            acc[i][j] = Mfma<T>::step(bfr[j], af[i], acc[i][j]);
+            mfma(i, j);
             __builtin_amdgcn_sched_barrier(0); // reads below reuse the registers this MFMA reads
             if (q == last_b(j))
                 read_b(j, cur, 1);
@@ -441,7 +495,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
 #pragma unroll
         for (int q = 0; q < HALF; ++q) {
             const int i = row_of(q), j = col_of(q);
-            acc[i][j] = Mfma<T>::step(bfr[j], af[i], acc[i][j]);
+            mfma(i, j);
             __builtin_amdgcn_sched_barrier(0);
             const int slot = MN + q;
 #pragma unroll
@@ -458,7 +512,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
 #pragma unroll
         for (int q = HALF; q < MN; ++q) {
             const int i = row_of(q), j = col_of(q), h = q - HALF;
-            acc[i][j] = Mfma<T>::step(bfr[j], af[i], acc[i][j]);
+            mfma(i, j);
             __builtin_amdgcn_sched_barrier(0);
             if (h < HM)
                 read_a(h, nxt, 0);

@@ -6,18 +6,19 @@
  *     D[b] = A[b] * B[b] + C[b]        for b = 0 .. batch-1
  *
  * on the chip's matrix cores (MFMA), with fp16/bf16 inputs and fp32
- * accumulation, an fp16-output ("fp16 accumulate") variant and an
- * int8 -> int32 variant.
+ * accumulation, an fp16-output ("fp16 accumulate") variant, an int8 -> int32
+ * variant and FP8 e4m3 inputs with fp32 accumulation.
  *
  * Sources for the operation and its conventions:
  *   - "Tensor Cores, CUTLASS and CuTe", section 2.1 (one matrix instruction is
  *     D = A*B + C with low-precision inputs and an fp32/int32 accumulator; the
  *     table of input/accumulator type pairs, including fp16 accumulation and
- *     int8 -> int32), section 4.1 (the 4096^3 bf16 problem: bf16 in, fp32
+ *     int8 -> int32 and e4m3 -> fp32), section 4.1 (the 4096^3 bf16 problem: bf16 in, fp32
  *     accumulate, bf16 out; "TN" = A row-major M x K, B stored N x K row-major),
  *     section 4.4 (the host entry point checks device, type, rank and
  *     contiguity before it reinterprets untyped pointers) and section 7 (the
- *     strided-batched BLAS form alpha*A*B + beta*C).
+ *     strided-batched BLAS form alpha*A*B + beta*C); section 6.5 (FP8 GEMMs:
+ *     a K-tile of 128 one-byte values moves the bytes of 64 bf16 values).
  *   - "hgemm_mma_m16n8k16_mma2x4_warp4x4_kernel" walkthrough, section 1.1
  *     (C = A x B with A M x K and B K x N, both row-major: "NN").
  *   - Layout-experiment post (KingOfEgg, RTX 5080), section 3 (D = A x B + C;
@@ -43,7 +44,9 @@ typedef enum {
     DMU_BF16 = 2, /* bfloat16 (upper half of a binary32) */
     DMU_F32 = 3,  /* IEEE binary32                       */
     DMU_I8 = 4,   /* signed 8-bit integer                */
-    DMU_I32 = 5   /* signed 32-bit integer               */
+    DMU_I32 = 5,  /* signed 32-bit integer               */
+    DMU_E4M3 = 6  /* FP8 e4m3: 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+                     no infinities, S.1111.111 is NaN, largest finite 448   */
 } dmu_dtype;
 
 /* Storage order of a logical matrix X(r, c) with leading dimension ld (elements):
@@ -64,13 +67,14 @@ typedef enum {
  *
  *  M, N, K, batch   sizes, each >= 0.  M, N or batch == 0: nothing is done.
  *                   K == 0: D = C (or 0 when C is NULL).
- *  in_type          type of A and B: DMU_F16, DMU_BF16 or DMU_I8.
- *  acc_type         accumulator: DMU_F32 (fp16/bf16 in), DMU_F16 (fp16 in,
- *                   "fp16 accumulate") or DMU_I32 (int8 in).
+ *  in_type          type of A and B: DMU_F16, DMU_BF16, DMU_I8 or DMU_E4M3.
+ *  acc_type         accumulator: DMU_F32 (fp16/bf16/e4m3 in), DMU_F16 (fp16
+ *                   in, "fp16 accumulate") or DMU_I32 (int8 in).
  *  out_type         type of C and D.  Supported (in, acc, out) triples:
  *                     (F16,F32,F32) (F16,F32,F16) (F16,F16,F16)
  *                     (BF16,F32,BF16) (BF16,F32,F32) (I8,I32,I32)
  *                     (I8,I32,F32) (I8,I32,F16) (I8,I32,BF16)
+ *                     (E4M3,F32,F32) (E4M3,F32,F16) (E4M3,F32,BF16)
  *                   The last three dequantise: the int32 sum is converted
  *                   to fp32 (round to nearest even), goes through the
  *                   optional epilogue of dmu_gemm_ex in fp32, and is rounded
@@ -259,7 +263,9 @@ const char *dmu_last_error(void);
  *  MFMA_*: lane l loads its operand fragments straight from in0/in1 with the
  *    hypothesised mapping (X[row = l % m][k = (16 bytes / element) * (l / m) + s])
  *    and issues one MFMA with a zero accumulator; the caller checks every
- *    (lane, register) against the product.
+ *    (lane, register) against the product.  MFMA_16x16x128_E4M3 takes 32 bytes
+ *    per lane, the GEMM kernels' two 16-byte fragments of a 128-byte row: bytes
+ *    16 (l / 16) .. +15 and 64 + 16 (l / 16) .. +15 of row l % 16.
  *  LDS_READ_*: the image is copied to LDS; lane l reads at in1[l] (masked to
  *    an aligned in-bounds address) with ds_read_b128 / ds_read_b64_tr_b16.
  *  LDS_FRAG: the tile is stored with the tiled kernel's staging writes of a
@@ -280,6 +286,7 @@ enum {
     DMU_PROBE_MFMA_16x16x32_F16 = 4,
     DMU_PROBE_MFMA_32x32x32_I8 = 5,
     DMU_PROBE_MFMA_16x16x64_I8 = 6,
+    DMU_PROBE_MFMA_16x16x128_E4M3 = 7,
     DMU_PROBE_LDS_READ_B128 = 10,
     DMU_PROBE_LDS_READ_TR16 = 11,
     DMU_PROBE_LDS_FRAG = 12,

@@ -171,6 +171,8 @@ def all_bij(p) -> np.ndarray:
 
 
 def values(bits: np.ndarray, t: str) -> np.ndarray:
+    if t == "e4m3":
+        return exact.e4m3_values(bits)
     if t == "f16":
         return exact.f16_values(bits)
     if t == "bf16":

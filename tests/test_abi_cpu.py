@@ -229,3 +229,42 @@ def test_attention_rejections(kw, status):
     with pytest.raises(dmu.DmuError) as e:
         dmu.dmu_attention(a, stream=0)  # rejected before any HIP call
     assert e.value.status == status
+
+
+TN8 = dict(layout_b="col", in_type="e4m3")
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(M=8192, N=8192, K=8192, lda=8192, ldb=8192, ldd=8192, out_type="bf16", **TN8),
+     "mfma_256x128_k16_k16_e4m3_bf16"),
+    (dict(out_type="f32", **TN8), "mfma_128x128_k16_k16_e4m3_f32"),
+    (dict(K=200, lda=200, ldb=200, out_type="f16", **TN8), "mfma_128x128_kd_kd_e4m3_f16"),
+    (dict(K=130, lda=130, ldb=130, out_type="f32", **TN8), "mfma_generic64_any_any_e4m3_f32"),
+    (dict(in_type="e4m3", out_type="f32"), "mfma_generic64_any_any_e4m3_f32"),  # B row-major
+    (dict(M=4096, N=128, K=4096, lda=4096, ldb=4096, ldd=128, out_type="f32", **TN8),
+     "mfma_256x128_k16_k16_e4m3_f32"),
+])
+def test_e4m3_kernel_selection(kw, expect):
+    assert dmu.dmu_gemm_kernel_name(args(**kw)) == expect
+
+
+def test_e4m3_never_takes_the_256x256_tile(monkeypatch):
+    """e4m3 fragments need the registers of a 64 x 64 wavefront tile: a forced 256x256 runs 256x128."""
+    monkeypatch.setenv("DMU_FORCE_KERNEL", "256x256")
+    a = args(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096, out_type="bf16", **TN8)
+    assert dmu.dmu_gemm_kernel_name(a) == "mfma_256x128_k16_k16_e4m3_bf16"
+
+
+@pytest.mark.parametrize("kw", [dict(out_type="i32"), dict(out_type="f32", acc_type="i32"),
+                                dict(out_type="f16", acc_type="f16")])
+def test_e4m3_rejections(kw):
+    assert dmu.dmu_gemm_check(args(in_type="e4m3", **kw)) == dmu.DMU_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("out_t", ["f32", "f16", "bf16"])
+def test_e4m3_epilogue_valid(out_t):
+    assert dmu.dmu_gemm_ex_check(args(out_type=out_t, **TN8), ep()) == dmu.DMU_OK
+
+
+def test_e4m3_probe_info():
+    assert dmu.dmu_probe_info(dmu.DMU_PROBE_MFMA_16x16x128_E4M3) == (16, 16, 128, dmu.DMU_E4M3, 4)

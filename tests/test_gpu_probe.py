@@ -16,8 +16,9 @@ pytestmark = pytest.mark.gpu
 
 MFMA = [dmu.DMU_PROBE_MFMA_32x32x16_BF16, dmu.DMU_PROBE_MFMA_32x32x16_F16,
         dmu.DMU_PROBE_MFMA_16x16x32_BF16, dmu.DMU_PROBE_MFMA_16x16x32_F16,
-        dmu.DMU_PROBE_MFMA_32x32x32_I8, dmu.DMU_PROBE_MFMA_16x16x64_I8]
-TNAME = {dmu.DMU_BF16: "bf16", dmu.DMU_F16: "f16", dmu.DMU_I8: "i8"}
+        dmu.DMU_PROBE_MFMA_32x32x32_I8, dmu.DMU_PROBE_MFMA_16x16x64_I8,
+        dmu.DMU_PROBE_MFMA_16x16x128_E4M3]
+TNAME = {dmu.DMU_BF16: "bf16", dmu.DMU_F16: "f16", dmu.DMU_I8: "i8", dmu.DMU_E4M3: "e4m3"}
 
 
 def acc_owner(m: int, lane: int, r: int):
@@ -70,7 +71,9 @@ def test_mfma_k_pairing(variant):
     """A[i][k] = k, B[k][j] = k: any mismatch between how A and B pair their k
     slots lowers sum(k^2) (rearrangement inequality), which the i*j pattern cannot see."""
     m, n, k, t, regs = dmu.dmu_probe_info(variant)
-    kk = np.arange(k) % (64 if t == dmu.DMU_I8 else 256)
+    # values exact in the input type (e4m3 holds the integers up to 16; a mispairing
+    # by a multiple of 16 is left to the random-integer probe)
+    kk = np.arange(k) % {dmu.DMU_I8: 64, dmu.DMU_E4M3: 16}.get(t, 256)
     A = np.repeat(kk[None, :], m, axis=0)
     B = np.repeat(kk[:, None], n, axis=1)
     if t == dmu.DMU_I8:
