@@ -11,7 +11,7 @@ measures that ramp instead of the kernel.  Prints one JSON
 line with the throughput, the MFMA roofline of the kernel and the CPU oracle's
 rate on a bounded row slice of the same product.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c6|c4fa]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c6|lk|lksk|c4fa]
                   [--no-cpu-baseline] [--copy-calibration MiB]
   python bench.py --summarize DIR [--workload W]   (rocprofv3 output -> profiles/)
 """
@@ -40,12 +40,17 @@ WORKLOAD_NAMES = {
     "c4o": "batched32_gemm_4096x128x4096_f16_nn_f32out",
     "c5": "gemm_8192x8192x8192_i8_tn_i32out",
     "c6": "gemm_8192x8192x8192_e4m3_tn_f32acc_bf16out",
+    "lk": "gemm_1024x1024x16384_bf16_nn_f32acc_bf16out",
+    "lksk": "gemm_1024x1024x16384_bf16_nn_f32acc_bf16out_streamk",
     "c5dq": "gemm_8192x8192x8192_i8_tn_dequant_rowcol_scale_bias_gelu_bf16out",
 }
 
 # Fused attention (dmu_attention): batch, seq_q, seq_k, head_dim, in type, out type.
 ATTENTION_WORKLOADS = {"c4fa": (32, 4096, 4096, 128, "f16", "f32")}
 WORKLOAD_NAMES["c4fa"] = "batched32_attention_4096x4096x128_f16_f32out_fused"
+
+# Workloads that run the persistent stream-K schedule (dmu_gemm_streamk): base problem.
+STREAMK_WORKLOADS = {"lksk": "lk"}
 
 # Workloads that run with the fused epilogue (dmu_gemm_ex): base problem, output type, activation.
 EPILOGUE_WORKLOADS = {"c5dq": ("c5", "bf16", "gelu_tanh")}
@@ -94,7 +99,8 @@ def kernel_for(workload: str) -> str:
         *_, in_t, out_t = ATTENTION_WORKLOADS[workload]
         return f"attn_fwd_{in_t}_{out_t}"
 
-    base, out_override = (EPILOGUE_WORKLOADS[workload][:2] if workload in EPILOGUE_WORKLOADS else (workload, None))
+    base, out_override = (EPILOGUE_WORKLOADS[workload][:2] if workload in EPILOGUE_WORKLOADS else
+                          (STREAMK_WORKLOADS.get(workload, workload), None))
     M, N, K, batch, in_t, out_t, acc_t, la, lb = workloads.FULL[base]
     out_t = out_override or out_t
     lda, ldb, sa, sb = workloads._layout_params(M, N, K, la, lb)
@@ -104,7 +110,11 @@ def kernel_for(workload: str) -> str:
                       stride_a=sa if batch > 1 else 0, stride_b=sb if batch > 1 else 0,
                       stride_d=M * N if batch > 1 else 0,
                       C=(base + (3 << 36)) if workload == "c1" else None, ldc=N if workload == "c1" else 0)
-    return dmu.dmu_gemm_kernel_name(a)
+    name = dmu.dmu_gemm_kernel_name(a)
+    if workload in STREAMK_WORKLOADS and "generic" not in name:
+        # the stream-K kernel runs 256 x 128 tiles where the data-parallel plan has 256 x 256
+        name = "streamk_" + name.replace("mfma_256x256", "mfma_256x128")
+    return name
 
 
 def cpu_baseline(p, budget_s: float = 15.0):
@@ -268,7 +278,7 @@ def main() -> int:
                                stride_col_scale=e.stride_cs, bias=ep_vecs[2], stride_bias=e.stride_bias,
                                act=e.act)
     else:
-        p = workloads.make(args.workload, "random", 0)
+        p = workloads.make(STREAMK_WORKLOADS.get(args.workload, args.workload), "random", 0)
     dA, dB = to_dev(p.A), to_dev(p.B)
     dC = to_dev(p.C) if p.C is not None else None
     out_dt = {"f32": torch.float32, "f16": torch.int16, "bf16": torch.int16, "i32": torch.int32}
@@ -277,11 +287,15 @@ def main() -> int:
                       out_type=p.out_type, acc_type=p.acc_type, layout_a=p.layout_a,
                       layout_b=p.layout_b, batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b,
                       C=dC, ldc=p.ldc, stride_c=p.stride_c, stride_d=p.stride_d)
-    kernel = dmu.dmu_gemm_kernel_name(a)
+    kernel = kernel_for(args.workload)
     stream = torch.cuda.current_stream()
     print(f"# workload {WORKLOAD_NAMES[args.workload]} kernel {kernel}", file=sys.stderr, flush=True)
 
     launch = (lambda: dmu.dmu_gemm(a, stream)) if ep is None else (lambda: dmu.dmu_gemm_ex(a, ep, stream))
+    if args.workload in STREAMK_WORKLOADS:
+        ws_bytes = dmu.dmu_gemm_streamk_workspace_size(a)
+        ws = torch.zeros(max(ws_bytes, 4) // 4 + 1, dtype=torch.int32, device="cuda:0")  # zero-filled once
+        launch = lambda: dmu.dmu_gemm_streamk(a, None, ws, 4 * ws.numel(), stream)
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()

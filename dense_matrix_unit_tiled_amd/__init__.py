@@ -116,6 +116,9 @@ def _load():
     PE = ctypes.POINTER(dmu_epilogue)
     lib.dmu_gemm_ex.argtypes, lib.dmu_gemm_ex.restype = [P, PE, vp], i32
     lib.dmu_gemm_ex_check.argtypes, lib.dmu_gemm_ex_check.restype = [P, PE], i32
+    lib.dmu_gemm_streamk.argtypes, lib.dmu_gemm_streamk.restype = [P, PE, vp, ctypes.c_size_t, vp], i32
+    lib.dmu_gemm_streamk_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dmu_gemm_streamk_workspace_size.restype = i32
     lib.dmu_gemm_kernel_name.argtypes, lib.dmu_gemm_kernel_name.restype = [P], ctypes.c_char_p
     lib.dmu_status_string.argtypes, lib.dmu_status_string.restype = [i32], ctypes.c_char_p
     lib.dmu_last_error.argtypes, lib.dmu_last_error.restype = [], ctypes.c_char_p
@@ -195,6 +198,25 @@ def dmu_gemm_ex(args: dmu_gemm_args, ep: dmu_epilogue | None, stream=None, check
 
 def dmu_gemm_ex_check(args: dmu_gemm_args, ep: dmu_epilogue | None) -> int:
     return _load().dmu_gemm_ex_check(ctypes.byref(args), None if ep is None else ctypes.byref(ep))
+
+
+def dmu_gemm_streamk_workspace_size(args: dmu_gemm_args) -> int:
+    """Workspace bytes dmu_gemm_streamk needs on the current device (0: none)."""
+    n = ctypes.c_size_t(0)
+    st = _load().dmu_gemm_streamk_workspace_size(ctypes.byref(args), ctypes.byref(n))
+    if st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return n.value
+
+
+def dmu_gemm_streamk(args: dmu_gemm_args, ep: dmu_epilogue | None, workspace, workspace_bytes: int,
+                     stream=None, check: bool = True) -> int:
+    """Launch the stream-K schedule of D = epilogue(A*B + C) with a caller-owned, zero-filled workspace."""
+    st = _load().dmu_gemm_streamk(ctypes.byref(args), None if ep is None else ctypes.byref(ep), _addr(workspace),
+                                  workspace_bytes, _stream(stream))
+    if check and st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return st
 
 
 def attention_args(batch, seq_q, seq_k, head_dim, Q, ldq, K, ldk, V, ldv, O, ldo, *, in_type, out_type, scale,

@@ -242,6 +242,17 @@ struct GemmParams {
     int32_t epi;                                // 1 if any of rs, cs, bias is present
 };
 
+// Workspace of the stream-K kernel (dmu_streamk.hpp).
+struct StreamKParams {
+    uint32_t *flags;     // one per worker; zero outside a call
+    uint32_t *error;     // set nonzero when a wait ran past its limit
+    char *partials;      // one slot of BM x BN accumulators per worker
+    uint32_t workers;    // W, the grid size
+    uint32_t nk;         // K-tiles per tile
+    uint32_t q, r;       // I = q W + r iterations (I = tiles x nk < 2^31)
+    uint32_t spin_limit; // polls of a flag before a wait gives up
+};
+
 // ---------------------------------------------------------------------------
 // Workgroup -> (batch, tile_m, tile_n).
 //
@@ -257,13 +268,20 @@ struct TileCoord {
     int32_t b, tm, tn;
 };
 
-__device__ __forceinline__ TileCoord tile_of(const GemmParams &p, uint32_t wg)
+// Workgroup id -> a number in [0, n) such that XCD x (which receives ids
+// x, x + 8, ...) gets a contiguous range, in increasing id order.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t n, uint32_t wg)
 {
-    constexpr uint32_t XCDS = 8, GROUP_M = 4;
-    const uint32_t n = p.total_tiles;
+    constexpr uint32_t XCDS = 8;
     const uint32_t q = n / XCDS, r = n % XCDS;
     const uint32_t x = wg % XCDS, i = wg / XCDS;
-    const uint32_t t = x * q + (x < r ? x : r) + i; // bijection on [0, n)
+    return x * q + (x < r ? x : r) + i; // bijection on [0, n)
+}
+
+// Tile number -> (batch, tile_m, tile_n): column-major groups of GROUP_M tile rows.
+__device__ __forceinline__ TileCoord tile_coord(const GemmParams &p, uint32_t t)
+{
+    constexpr uint32_t GROUP_M = 4;
     const uint32_t per_batch = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n;
     TileCoord c;
     c.b = (int32_t)(t / per_batch);
@@ -275,6 +293,11 @@ __device__ __forceinline__ TileCoord tile_of(const GemmParams &p, uint32_t wg)
     c.tm = (int32_t)(first_m + u % rows);
     c.tn = (int32_t)(u / rows);
     return c;
+}
+
+__device__ __forceinline__ TileCoord tile_of(const GemmParams &p, uint32_t wg)
+{
+    return tile_coord(p, xcd_remap(p.total_tiles, wg));
 }
 
 } // namespace dmu

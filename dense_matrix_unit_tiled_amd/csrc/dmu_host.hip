@@ -347,6 +347,147 @@ int validate_epilogue(const dmu_gemm_args *a, const dmu_epilogue *ep, Plan *plan
     return DMU_OK;
 }
 
+// Stream-K workspace layout: flags (one 32-bit word per worker), the error
+// word, then one BM x BN slot of 32-bit accumulators per worker.
+struct SkLayout {
+    uint32_t workers; // 0: the call runs the data-parallel kernel
+    uint32_t nk, q, r; // K-tiles per tile; iterations = q workers + r
+    size_t error_off, partials_off, slot_bytes, bytes;
+};
+
+constexpr uint32_t SK_SPIN_LIMIT = 1u << 22; // polls (each after a short sleep), well over a second
+
+// Stream-K runs the 256 x 128 tile where the data-parallel plan has 256 x 256.
+void sk_retile(Plan *plan, const dmu_gemm_args *a)
+{
+    if (!plan->launch || plan->cfg.tile != TILE_256x256)
+        return;
+    const int64_t tm = (a->M + 255) / 256, tn = (a->N + 127) / 128;
+    if (tm * tn * a->batch >= ((int64_t)1 << 31))
+        return; // too many iterations for the 32-bit schedule anyway: stays data-parallel
+    plan->cfg.tile = TILE_256x128;
+    plan->p.tiles_m = (int32_t)tm;
+    plan->p.tiles_n = (int32_t)tn;
+    plan->p.total_tiles = (uint32_t)(tm * tn * a->batch);
+    plan->name = kernel_names().at[plan->cfg.tile][plan->cfg.amode][plan->cfg.bmode][plan->combo];
+}
+
+// Stream-K pays when the data-parallel tiles leave compute units idle: it is
+// chosen when those tiles fill less than 80 % of their waves (measured on the
+// 256-unit chip: 1024 x 1024 x 16384 bf16, 64 tiles, 123 -> 50 us; the
+// 5000 x 3000 x 2050 problem, 240 tiles = 94 %, stays data-parallel: stream-K
+// on its 480 smaller tiles took 97 us against 73 us).  DMU_STREAMK=always or
+// never overrides the choice (tests and sweeps).
+constexpr double SK_MIN_IDLE_FILL = 0.8;
+
+int sk_layout(Plan *plan, const dmu_gemm_args *a, SkLayout *sk)
+{
+    memset(sk, 0, sizeof(*sk));
+    if (!plan->launch || plan->cfg.tile == TILE_GENERIC)
+        return DMU_OK;
+    const char *mode = getenv("DMU_STREAMK");
+    if (mode && strcmp(mode, "never") == 0)
+        return DMU_OK;
+    const int64_t nk = (a->K * elem_bytes(a->in_type) + 127) / 128;
+    if (nk == 0)
+        return DMU_OK; // K == 0: D = C, data-parallel
+    static int cus[64] = {0}; // compute units per device, asked once
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        set_error("dmu_gemm_streamk: no current HIP device");
+        return DMU_ERR_HIP;
+    }
+    if (__atomic_load_n(&cus[dev], __ATOMIC_RELAXED) == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            set_error("dmu_gemm_streamk: cannot read the compute-unit count");
+            return DMU_ERR_HIP;
+        }
+        __atomic_store_n(&cus[dev], n, __ATOMIC_RELAXED);
+    }
+    const uint64_t n = (uint64_t)__atomic_load_n(&cus[dev], __ATOMIC_RELAXED);
+    if (!(mode && strcmp(mode, "always") == 0)) {
+        const uint64_t tiles = plan->p.total_tiles, waves = (tiles + n - 1) / n;
+        if ((double)tiles >= SK_MIN_IDLE_FILL * (double)(waves * n))
+            return DMU_OK; // the data-parallel waves are full enough
+    }
+    sk_retile(plan, a);
+    const Plan &pl = *plan;
+    if (pl.cfg.tile == TILE_256x256)
+        return DMU_OK; // too many tiles to retile: data-parallel
+    const uint64_t iters = (uint64_t)pl.p.total_tiles * (uint64_t)nk;
+    if (iters >= ((uint64_t)1 << 31))
+        return DMU_OK; // more iterations than the 32-bit schedule counts: data-parallel
+    sk->workers = (uint32_t)(iters < n ? iters : n);
+    sk->nk = (uint32_t)nk;
+    sk->q = (uint32_t)(iters / sk->workers);
+    sk->r = (uint32_t)(iters % sk->workers);
+    sk->slot_bytes = (size_t)tile_bm(pl.cfg.tile) * tile_bn(pl.cfg.tile) * 4;
+    sk->error_off = ((size_t)sk->workers * 4 + 255) & ~(size_t)255;
+    sk->partials_off = sk->error_off + 256;
+    sk->bytes = sk->partials_off + (size_t)sk->workers * sk->slot_bytes;
+    return DMU_OK;
+}
+
+hipError_t launch_plan(const Plan &plan, hipStream_t s)
+{
+    switch (plan.combo) {
+    case 0: return launch_f16_f32(plan.cfg, plan.p, s);
+    case 1: return launch_f16_f16(plan.cfg, plan.p, s);
+    case 2: return launch_bf16_bf16(plan.cfg, plan.p, s);
+    case 3: return launch_bf16_f32(plan.cfg, plan.p, s);
+    case 4: return launch_i8_i32(plan.cfg, plan.p, s);
+    case 5: return launch_i8_f32(plan.cfg, plan.p, s);
+    case 6: return launch_i8_f16(plan.cfg, plan.p, s);
+    case 7: return launch_i8_bf16(plan.cfg, plan.p, s);
+    case 8: return launch_e4m3_f32(plan.cfg, plan.p, s);
+    case 9: return launch_e4m3_f16(plan.cfg, plan.p, s);
+    default: return launch_e4m3_bf16(plan.cfg, plan.p, s);
+    }
+}
+
+hipError_t launch_plan_sk(const Plan &plan, const StreamKParams &k, hipStream_t s)
+{
+    switch (plan.combo) {
+    case 0: return launch_f16_f32_sk(plan.cfg, plan.p, k, s);
+    case 1: return launch_f16_f16_sk(plan.cfg, plan.p, k, s);
+    case 2: return launch_bf16_bf16_sk(plan.cfg, plan.p, k, s);
+    case 3: return launch_bf16_f32_sk(plan.cfg, plan.p, k, s);
+    case 4: return launch_i8_i32_sk(plan.cfg, plan.p, k, s);
+    case 5: return launch_i8_f32_sk(plan.cfg, plan.p, k, s);
+    case 6: return launch_i8_f16_sk(plan.cfg, plan.p, k, s);
+    case 7: return launch_i8_bf16_sk(plan.cfg, plan.p, k, s);
+    case 8: return launch_e4m3_f32_sk(plan.cfg, plan.p, k, s);
+    case 9: return launch_e4m3_f16_sk(plan.cfg, plan.p, k, s);
+    default: return launch_e4m3_bf16_sk(plan.cfg, plan.p, k, s);
+    }
+}
+
+// The workspace may not overlap any operand.
+bool workspace_overlaps(const dmu_gemm_args *a, const void *ws, size_t bytes)
+{
+    const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + bytes;
+    const int64_t batch = a->batch, esz = elem_bytes(a->in_type), osz = elem_bytes(a->out_type);
+    uintptr_t x0, x1;
+    span(a->D, batch > 1 ? a->stride_d : 0, batch, extent(DMU_ROW_MAJOR, a->M, a->N, a->ldd), (int)osz, &x0, &x1);
+    if (overlap(w0, w1, x0, x1))
+        return true;
+    if (a->C) {
+        span(a->C, batch > 1 ? a->stride_c : 0, batch, extent(DMU_ROW_MAJOR, a->M, a->N, a->ldc), (int)osz, &x0, &x1);
+        if (overlap(w0, w1, x0, x1))
+            return true;
+    }
+    if (a->K > 0) {
+        span(a->A, batch > 1 ? a->stride_a : 0, batch, extent(a->layout_a, a->M, a->K, a->lda), (int)esz, &x0, &x1);
+        if (overlap(w0, w1, x0, x1))
+            return true;
+        span(a->B, batch > 1 ? a->stride_b : 0, batch, extent(a->layout_b, a->K, a->N, a->ldb), (int)esz, &x0, &x1);
+        if (overlap(w0, w1, x0, x1))
+            return true;
+    }
+    return false;
+}
+
 } // namespace
 } // namespace dmu
 
@@ -388,20 +529,7 @@ extern "C" int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, vo
     if (rc != DMU_OK || !plan.launch)
         return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e;
-    switch (plan.combo) {
-    case 0: e = launch_f16_f32(plan.cfg, plan.p, s); break;
-    case 1: e = launch_f16_f16(plan.cfg, plan.p, s); break;
-    case 2: e = launch_bf16_bf16(plan.cfg, plan.p, s); break;
-    case 3: e = launch_bf16_f32(plan.cfg, plan.p, s); break;
-    case 4: e = launch_i8_i32(plan.cfg, plan.p, s); break;
-    case 5: e = launch_i8_f32(plan.cfg, plan.p, s); break;
-    case 6: e = launch_i8_f16(plan.cfg, plan.p, s); break;
-    case 7: e = launch_i8_bf16(plan.cfg, plan.p, s); break;
-    case 8: e = launch_e4m3_f32(plan.cfg, plan.p, s); break;
-    case 9: e = launch_e4m3_f16(plan.cfg, plan.p, s); break;
-    default: e = launch_e4m3_bf16(plan.cfg, plan.p, s); break;
-    }
+    const hipError_t e = launch_plan(plan, s);
     if (e != hipSuccess) {
         set_error("dmu_gemm: launch of %s failed: %s", plan.name, hipGetErrorString(e));
         return DMU_ERR_HIP;
@@ -410,6 +538,70 @@ extern "C" int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, vo
 }
 
 extern "C" int dmu_gemm(const dmu_gemm_args *args, void *stream) { return dmu_gemm_ex(args, nullptr, stream); }
+
+extern "C" int dmu_gemm_streamk_workspace_size(const dmu_gemm_args *args, size_t *bytes)
+{
+    clear_error();
+    if (!bytes) {
+        set_error("bytes is NULL");
+        return DMU_ERR_INVALID_ARG;
+    }
+    *bytes = 0;
+    Plan plan;
+    int rc = validate(args, &plan);
+    if (rc != DMU_OK)
+        return rc;
+    SkLayout sk;
+    rc = sk_layout(&plan, args, &sk);
+    if (rc == DMU_OK)
+        *bytes = sk.bytes;
+    return rc;
+}
+
+extern "C" int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *ep, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    Plan plan;
+    int rc = validate(args, &plan);
+    if (rc == DMU_OK)
+        rc = validate_epilogue(args, ep, &plan);
+    if (rc != DMU_OK || !plan.launch)
+        return rc;
+    SkLayout sk;
+    if ((rc = sk_layout(&plan, args, &sk)) != DMU_OK)
+        return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (sk.workers == 0) { // the fallback kernel, or K == 0: the data-parallel launch
+        e = launch_plan(plan, s);
+    } else {
+        if (!workspace || ((uintptr_t)workspace % 256) || workspace_bytes < sk.bytes) {
+            set_error("dmu_gemm_streamk: workspace must be 256-byte aligned and hold %zu bytes", sk.bytes);
+            return DMU_ERR_INVALID_ARG;
+        }
+        if (workspace_overlaps(args, workspace, sk.bytes)) {
+            set_error("dmu_gemm_streamk: the workspace overlaps an operand");
+            return DMU_ERR_INVALID_ARG;
+        }
+        char *w = static_cast<char *>(workspace);
+        StreamKParams k;
+        k.flags = reinterpret_cast<uint32_t *>(w);
+        k.error = reinterpret_cast<uint32_t *>(w + sk.error_off);
+        k.partials = w + sk.partials_off;
+        k.workers = sk.workers;
+        k.nk = sk.nk;
+        k.q = sk.q;
+        k.r = sk.r;
+        k.spin_limit = SK_SPIN_LIMIT;
+        e = launch_plan_sk(plan, k, s);
+    }
+    if (e != hipSuccess) {
+        set_error("dmu_gemm_streamk: launch of %s failed: %s", plan.name, hipGetErrorString(e));
+        return DMU_ERR_HIP;
+    }
+    return DMU_OK;
+}
 
 extern "C" const char *dmu_status_string(int status)
 {

@@ -47,4 +47,20 @@ hipError_t launch_e4m3_f32(const LaunchCfg &c, const GemmParams &p, hipStream_t 
 hipError_t launch_e4m3_f16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 hipError_t launch_e4m3_bf16(const LaunchCfg &c, const GemmParams &p, hipStream_t s);
 
+// The stream-K launchers (tiled configurations only; grid = sk.workers).
+#define DMU_DECLARE_SK(name) \
+    hipError_t name##_sk(const LaunchCfg &c, const GemmParams &p, const StreamKParams &sk, hipStream_t s);
+DMU_DECLARE_SK(launch_f16_f32)
+DMU_DECLARE_SK(launch_f16_f16)
+DMU_DECLARE_SK(launch_bf16_bf16)
+DMU_DECLARE_SK(launch_bf16_f32)
+DMU_DECLARE_SK(launch_i8_i32)
+DMU_DECLARE_SK(launch_i8_f32)
+DMU_DECLARE_SK(launch_i8_f16)
+DMU_DECLARE_SK(launch_i8_bf16)
+DMU_DECLARE_SK(launch_e4m3_f32)
+DMU_DECLARE_SK(launch_e4m3_f16)
+DMU_DECLARE_SK(launch_e4m3_bf16)
+#undef DMU_DECLARE_SK
+
 } // namespace dmu

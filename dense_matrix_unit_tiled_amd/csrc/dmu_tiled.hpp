@@ -307,18 +307,18 @@ __device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams &p, int64_t b)
     return e;
 }
 
-template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-    __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tiled(GemmParams p)
-{
-    constexpr bool F8 = T == E4M3;           // one 16 x 16 x 128 MFMA per K-tile and tile
-    constexpr int E = (T == I8 || F8) ? 1 : 2;
-    constexpr int FH = F8 ? 2 : 1;           // 16-byte fragment halves an MFMA reads
-    constexpr int NW = WGM * WGN;
+// One workgroup's tile of the product: the constants of a configuration, the
+// main loop over a range of K-tiles, the epilogue and (for the stream-K
+// kernel) the exchange of partial sums.
+template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> struct Tiled {
+    static constexpr bool F8 = T == E4M3;           // one 16 x 16 x 128 MFMA per K-tile and tile
+    static constexpr int E = (T == I8 || F8) ? 1 : 2;
+    static constexpr int FH = F8 ? 2 : 1;           // 16-byte fragment halves an MFMA reads
+    static constexpr int NW = WGM * WGN;
     static_assert(NW == 8, "eight wavefronts, two per SIMD");
-    constexpr int WTM = BM / WGM, WTN = BN / WGN; // wavefront tile
-    constexpr int MT = WTM / 16, NT = WTN / 16;   // MFMA tiles per wavefront
-    constexpr int MN = MT * NT;
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN; // wavefront tile
+    static constexpr int MT = WTM / 16, NT = WTN / 16;   // MFMA tiles per wavefront
+    static constexpr int MN = MT * NT;
     static_assert(MT % 2 == 0, "a K-step runs in two halves of the tile rows");
     static_assert(AMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(BMODE != MC16 || E == 2, "transposed operands are 16-bit");
@@ -326,15 +326,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     typedef typename Mfma<T>::acc_t acc_t;
     typedef typename TileOf<AMODE, BM, NW>::type ATile;
     typedef typename TileOf<BMODE, BN, NW>::type BTile;
-    constexpr int NA = ATile::NL, NB = BTile::NL;
-    constexpr uint32_t ABYTES = (ATile::BYTES + 255) & ~255u, STAGE = (ABYTES + BTile::BYTES + 255) & ~255u;
+    static constexpr int NA = ATile::NL, NB = BTile::NL;
+    static constexpr uint32_t ABYTES = (ATile::BYTES + 255) & ~255u,
+                              STAGE = (ABYTES + BTile::BYTES + 255) & ~255u;
+    static constexpr int PARK = 16 * (16 * NT * 4 + 16); // per wavefront, epilogue
+    static_assert(NW * PARK <= 2 * STAGE, "parking area fits in the stages");
+    static constexpr uint32_t PARTIAL_BYTES = NW * MN * 1024; // one tile's accumulators
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-
-    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    // acc += the product of tile tc over K-tiles [kb, ke) (kb < ke).  smem holds
+    // two stages; K-tile kt uses stage kt mod 2.  tid is threadIdx.x (a caller
+    // that loops over tiles passes an opaque copy, so that the lane arithmetic
+    // is not hoisted out of its loop and kept in registers).
+    static __device__ __forceinline__ void mainloop(const GemmParams &p, const TileCoord tc, int kb, int ke,
+                                                    char *smem, acc_t (&acc)[MT][NT], uint32_t tid)
+    {
+    const uint32_t lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t wm = wave / WGN, wn = wave % WGN;
-    const TileCoord tc = tile_of(p, blockIdx.x);
     const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
 
     // Each operand's descriptor starts at this tile's first row (K-contiguous)
@@ -372,13 +380,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
             tb.store(c - NA, stage + ABYTES, wave, lane, sb[c - NA], kt, k_bytes);
     };
 
-    acc_t acc[MT][NT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-            acc[i][j] = acc_t{};
-
     // Operand fragments of one K-step (e4m3: both K-step halves of the K-tile,
     // which one MFMA consumes together).
     u32x4 af[MT][FH], bfr[NT][FH];
@@ -399,26 +400,26 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
             acc[i][j] = Mfma<T>::step(bfr[j][0], af[i][0], acc[i][j]);
     };
 
-    const int nk = (int)(((int64_t)p.K * E + 127) / 128);
     constexpr int NLD = NA + NB;
 
-    if (nk > 0) {
+    {
+        char *first = smem + (kb & 1) * STAGE;
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
-            load_one(c, 0);
+            load_one(c, kb);
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
-            store_one(c, smem, 0);
+            store_one(c, first, kb);
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
-            load_one(c, 1);
+            load_one(c, kb + 1);
         stage_barrier();
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-            read_a(i, smem, 0);
+            read_a(i, first, 0);
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            read_b(j, smem, 0);
+            read_b(j, first, 0);
     }
 
     // MFMA order within a K-step: two halves of the tile rows, each walked
@@ -442,7 +443,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         // other stage right after its last use (the first half's A rows at
         // once).  Every read of a stage happens before the barrier that
         // precedes its overwrite.
-        for (int kt = 0; kt < nk; ++kt) {
+        for (int kt = kb; kt < ke; ++kt) {
             char *nxt = smem + ((kt + 1) & 1) * STAGE;
 #pragma unroll
             for (int q = 0; q < HALF; ++q) {
@@ -471,7 +472,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
             }
         }
     } else
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = kb; kt < ke; ++kt) {
         const char *cur = smem + (kt & 1) * STAGE;
         char *nxt = smem + ((kt + 1) & 1) * STAGE;
         // K-step 0; each fragment of K-step 1 is read right after its last use.
@@ -524,22 +525,81 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         }
     }
 
-    // Every wavefront is past the last barrier and reads no stage any more:
-    // each parks its results in its own part of the stages.  The tile
-    // coordinates and lane are derived afresh from opaque copies of the ids, so
-    // that the compiler does not keep the values of the prologue alive (in
-    // registers the loop needs) across the K loop.
+    }
+
+    // D = epilogue(acc) for tile tc.  Every wavefront must be past the last
+    // barrier of the main loop and read no stage any more: each parks its
+    // results in its own part of the stages.
+    static __device__ __forceinline__ void epilogue(const GemmParams &p, const TileCoord te, const acc_t (&acc)[MT][NT],
+                                                    char *smem, uint32_t lane, uint32_t wave)
+    {
+        const char *Cb = p.C ? p.C + (int64_t)te.b * p.stride_c * dt_bytes(O) : nullptr;
+        char *Db = p.D + (int64_t)te.b * p.stride_d * dt_bytes(O);
+        store_staged<O, MT, NT>(p, acc, smem + wave * PARK, (int64_t)te.tm * BM + (wave / WGN) * WTM,
+                                (int64_t)te.tn * BN + (wave % WGN) * WTN, lane, Cb, Db, epi_ptrs(p, te.b));
+    }
+
+    // One tile's accumulators to / from a partial-sum slot of PARTIAL_BYTES:
+    // (wavefront, tile i, tile j) blocks of 64 lanes x 16 bytes, coalesced.
+    // The accesses are coherent at device scope (cache policy SC1): stores are
+    // written through to the coherence point and loads do not hit a stale copy
+    // in this XCD's L2 or this unit's L1, so that no cache-wide write-back or
+    // invalidation is needed around the exchange.
+    static constexpr int SC1 = 16; // cache-policy bit of the buffer instructions
+    static __device__ __forceinline__ void store_partial(char *slot, const acc_t (&acc)[MT][NT], uint32_t lane,
+                                                         uint32_t wave)
+    {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, PARTIAL_BYTES);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r, lane * 16,
+                                                       ((wave * MT + i) * NT + j) * 1024, SC1);
+    }
+    // (one row of tiles at a time: the loads of all of them would need as many
+    // registers as the accumulators)
+    static __device__ __forceinline__ void add_partial(const char *slot, acc_t (&acc)[MT][NT], uint32_t lane,
+                                                       uint32_t wave)
+    {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, PARTIAL_BYTES);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            acc_t v[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                v[j] = __builtin_bit_cast(acc_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     r, lane * 16, ((wave * MT + i) * NT + j) * 1024, SC1));
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                acc[i][j] += v[j];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
+template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+    __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tiled(GemmParams p)
+{
+    typedef Tiled<T, O, BM, BN, WGM, WGN, AMODE, BMODE> G;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+    typename G::acc_t acc[G::MT][G::NT];
+#pragma unroll
+    for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < G::NT; ++j)
+            acc[i][j] = typename G::acc_t{};
+    const int nk = (int)(((int64_t)p.K * G::E + 127) / 128);
+    if (nk > 0)
+        G::mainloop(p, tile_of(p, blockIdx.x), 0, nk, smem, acc, threadIdx.x);
+    // The tile coordinates and lane are derived afresh from opaque copies of
+    // the ids, so that the compiler does not keep the values of the prologue
+    // alive (in registers the loop needs) across the K loop.
     uint32_t wg2 = blockIdx.x, tid2 = threadIdx.x;
     asm volatile("" : "+s"(wg2));
     asm volatile("" : "+v"(tid2));
-    const TileCoord te = tile_of(p, wg2);
-    const uint32_t lane2 = tid2 & 63u, wave2 = __builtin_amdgcn_readfirstlane(tid2 >> 6);
-    const char *Cb = p.C ? p.C + (int64_t)te.b * p.stride_c * dt_bytes(O) : nullptr;
-    char *Db = p.D + (int64_t)te.b * p.stride_d * dt_bytes(O);
-    constexpr int PARK = 16 * (16 * NT * 4 + 16);
-    static_assert(NW * PARK <= 2 * STAGE, "parking area fits in the stages");
-    store_staged<O, MT, NT>(p, acc, smem + wave2 * PARK, (int64_t)te.tm * BM + (wave2 / WGN) * WTM,
-                            (int64_t)te.tn * BN + (wave2 % WGN) * WTN, lane2, Cb, Db, epi_ptrs(p, te.b));
+    G::epilogue(p, tile_of(p, wg2), acc, smem, tid2 & 63u, __builtin_amdgcn_readfirstlane(tid2 >> 6));
 }
 
 } // namespace dmu

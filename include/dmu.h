@@ -32,6 +32,7 @@
 #ifndef DMU_H
 #define DMU_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -171,6 +172,53 @@ int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, void *stream)
 
 /* Validate `args` and `ep` exactly as dmu_gemm_ex does, without touching the GPU. */
 int dmu_gemm_ex_check(const dmu_gemm_args *args, const dmu_epilogue *ep);
+
+/*
+ * Persistent stream-K schedule of the same product ("Tensor Cores, CUTLASS and
+ * CuTe", section 6.5: a persistent tile scheduler launches a fixed number of
+ * blocks that loop over the work, instead of one block per output tile;
+ * section 4.5 lists the one-block-per-tile dispatch among its kernel's gaps).
+ *
+ * One workgroup per compute unit ("worker") shares the tiles x K-tiles
+ * multiply-accumulate iterations of the tiled kernel evenly, so that a tile
+ * count that does not fill the compute units (or leaves a partial last wave)
+ * still keeps every unit busy.  A tile split between workers is completed by
+ * the worker that holds its last K-tile, which adds the others' fp32/int32
+ * partial sums in a fixed order: results are reproducible launch to launch,
+ * and equal to dmu_gemm_ex's within the accumulation-order tolerance (bit for
+ * bit for int8 and for exactly representable sums).
+ *
+ *  args, ep        as for dmu_gemm_ex (same validation, same results).
+ *  workspace       device memory of at least dmu_gemm_streamk_workspace_size
+ *                  bytes, 256-byte aligned, owned by the caller, not overlapping
+ *                  any operand.  It must be zero-filled before its first use;
+ *                  every call leaves its flag words zero again, so one
+ *                  workspace serves any number of calls in stream order.  Calls
+ *                  that overlap in time (several streams) need separate
+ *                  workspaces.  Its error word (the 32-bit word at the offset
+ *                  of the worker count x 4 rounded up to 256) is set nonzero if
+ *                  a worker waited past its limit (not expected: every worker
+ *                  is resident) -- then the result is wrong and the workspace
+ *                  must be zero-filled again.
+ *  workspace_bytes its size.
+ * The schedule is used where it pays: when the data-parallel kernel's tiles
+ * fill less than 80 % of its waves of one workgroup per compute unit (few
+ * tiles, long K).  Otherwise -- and for products that only the fallback kernel
+ * can read, and K == 0 -- the call runs the data-parallel kernel and uses no
+ * workspace (its size is then 0).  The environment variable DMU_STREAMK=always
+ * or =never overrides the choice.
+ * Returns DMU_ERR_INVALID_ARG for a missing, misaligned, small or overlapping
+ * workspace, and DMU_ERR_HIP if the device cannot be queried or the launch
+ * fails; otherwise as dmu_gemm_ex.
+ */
+int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *ep, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Workspace bytes dmu_gemm_streamk needs for these arguments on the current
+ * device (the worker count is the device's compute-unit count, at most the
+ * number of iterations).  *bytes = 0 when none is needed.  Validation as for
+ * dmu_gemm_check; DMU_ERR_HIP if the device cannot be queried. */
+int dmu_gemm_streamk_workspace_size(const dmu_gemm_args *args, size_t *bytes);
 
 /*
  * Validate `args` exactly as dmu_gemm does, without touching the GPU.

@@ -112,6 +112,30 @@ def run_dmu(p, force=None, fill=None, return_name=False, ep=None, in_place=False
     return (out, name) if return_name else out
 
 
+def run_streamk(p, ep=None, workspace=None, calls=1):
+    """Run one workload through dmu_gemm_streamk (``calls`` times with the same
+    workspace); returns (D bits, kernel name, workspace tensor or None)."""
+    torch = _torch()
+    dA, dB = to_dev(p.A), to_dev(p.B)
+    dC = to_dev(p.C) if p.C is not None else None
+    dD = torch.zeros(max(p.batch * p.stride_d, 1), dtype=out_dtype(p.out_type), device="cuda:0")
+    args = make_args(p, dA, dB, dD, dC)
+    nbytes = dmu.dmu_gemm_streamk_workspace_size(args)
+    if workspace is None and nbytes:
+        workspace = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device="cuda:0")
+    keep = []
+    e = None
+    if ep is not None:
+        vec = lambda x: None if x is None else keep.append(to_dev(x)) or keep[-1]
+        e = dmu.epilogue_args(row_scale=vec(ep.row_scale), stride_row_scale=ep.stride_rs,
+                              col_scale=vec(ep.col_scale), stride_col_scale=ep.stride_cs,
+                              bias=vec(ep.bias), stride_bias=ep.stride_bias, act=ep.act)
+    for _ in range(calls):
+        dmu.dmu_gemm_streamk(args, e, workspace, 4 * workspace.numel() if workspace is not None else 0)
+    torch.cuda.synchronize()
+    return from_dev(dD, p.out_type)[: p.batch * p.stride_d], dmu.dmu_gemm_kernel_name(args), workspace
+
+
 def run_oracle(p, nthreads=None, ep=None):
     return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, in_type=p.in_type,
                        out_type=p.out_type, layout_a=p.layout_a, layout_b=p.layout_b,

@@ -268,3 +268,13 @@ def test_e4m3_epilogue_valid(out_t):
 
 def test_e4m3_probe_info():
     assert dmu.dmu_probe_info(dmu.DMU_PROBE_MFMA_16x16x128_E4M3) == (16, 16, 128, dmu.DMU_E4M3, 4)
+
+
+def test_streamk_argument_errors_before_any_hip_call():
+    lib = ctypes.CDLL(dmu.LIB_PATH)
+    lib.dmu_gemm_streamk_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.dmu_gemm_streamk_workspace_size(ctypes.addressof(args()), None) == dmu.DMU_ERR_INVALID_ARG
+    assert dmu.dmu_gemm_streamk(args(M=-1), None, None, 0, stream=0, check=False) == dmu.DMU_ERR_INVALID_ARG
+    assert dmu.dmu_gemm_streamk(args(out_type="i32"), None, None, 0, stream=0, check=False) == \
+        dmu.DMU_ERR_UNSUPPORTED
+    assert dmu.dmu_gemm_streamk(args(M=0), None, None, 0, stream=0) == dmu.DMU_OK  # empty: nothing launched

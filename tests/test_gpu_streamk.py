@@ -1,0 +1,140 @@
+"""Parity of the stream-K schedule (dmu_gemm_streamk) with the oracle and with the
+data-parallel kernel.
+
+The persistent kernel splits the tiles' K-tiles over one workgroup per compute
+unit and adds partial sums through the workspace.  Checked through the C ABI:
+element by element against the oracle for each input type (fp16/bf16/int8/e4m3),
+on problems whose tiles are split over two, three or dozens of workers, with
+batches, a C operand and the fused epilogue; bit for bit against the
+data-parallel kernel where every sum is exact (int8, integer-valued data); bit
+for bit launch to launch; the workspace's flags back at zero and its error word
+clear after every call; sampled outputs of the full 5000 x 3000 x 2050 problem.
+"""
+import numpy as np
+import pytest
+
+import dense_matrix_unit_tiled_amd as dmu
+import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def check_workspace_clean(p, ws, name):
+    """The W flag words are zero and the error word is clear after a call.  Layout of
+    dmu_gemm_streamk: W flag words, the error word at 4 W rounded up to 256 bytes, then
+    W slots of BM x BN 32-bit partial sums (BM x BN of the stream-K tile: 256 x 128
+    where the data-parallel plan is 256 x 256)."""
+    if ws is None:
+        return
+    tile = name.split("_")[1]
+    bm, bn = {"256x256": (256, 128), "256x128": (256, 128), "128x128": (128, 128)}[tile]
+    nbytes = 4 * ws.numel()
+    round256 = lambda x: (x + 255) // 256 * 256
+    cands = [w for w in range(1, 4097) if round256(4 * w) + 256 + w * bm * bn * 4 <= nbytes
+             and round256(4 * w) + 256 + w * bm * bn * 4 > nbytes - 4 * 4]
+    assert len(cands) == 1, cands
+    W = cands[0]
+    words = ws.cpu().numpy().view(np.uint32)
+    assert not np.any(words[:W]), f"flags left set: {np.nonzero(words[:W])[0][:8]}"
+    assert words[round256(4 * W) // 4] == 0, "error word set"
+
+
+@pytest.mark.parametrize("cfg,M,N,K", [
+    ("c3", 700, 500, 1030),   # f16 -> f16, 4-byte rows (masked K tail)
+    ("c2", 512, 384, 2048),   # bf16 -> bf16, B row-major (transposed tiles)
+    ("c1", 256, 256, 8192),   # f16 -> f32: 4 tiles, each split over 64 workers
+    ("c5", 520, 264, 4096),   # int8 -> int32
+    ("c6", 520, 264, 4096),   # e4m3 -> bf16
+])
+def test_parity_with_oracle(cfg, M, N, K):
+    p = workloads.make(cfg, "random", 21, M=M, N=N, K=K)
+    if cfg == "c1":
+        p.C = None
+    got, name, ws = gu.run_streamk(p)
+    assert "generic" not in name, name
+    gu.assert_close(got, gu.run_oracle(p), p, where=gu.valid_mask(p))
+    check_workspace_clean(p, ws, name)
+
+
+@pytest.mark.parametrize("cfg", ["c5", "c2"])
+def test_exact_sums_match_data_parallel_bit_for_bit(cfg):
+    """int8 and integer-valued inputs: every partial sum is exact, so the split
+    schedule reproduces the data-parallel kernel bit for bit."""
+    kind = "random" if cfg == "c5" else "structured"
+    p = workloads.make(cfg, kind, 22, M=600, N=400, K=2560)
+    sk, name, ws = gu.run_streamk(p)
+    dp = gu.run_dmu(p, force="256x128")
+    gu.assert_bits_equal(sk, dp, where=gu.valid_mask(p))
+    check_workspace_clean(p, ws, name)
+
+
+def test_reproducible_and_workspace_reused():
+    """Three calls with one workspace give the same bits, and leave it clean."""
+    p = workloads.make("c3", "random", 23, M=1000, N=600, K=2050)  # 40 tiles of 128 x 128
+    a, name, ws = gu.run_streamk(p)
+    b, _, ws = gu.run_streamk(p, workspace=ws, calls=3)
+    gu.assert_bits_equal(a, b, where=gu.valid_mask(p))
+    check_workspace_clean(p, ws, name)
+
+
+def test_batched_with_c_and_epilogue():
+    p = workloads.make("c4s", "random", 24, M=300, N=136, K=1024, batch=3, with_c=True)
+    ep = workloads.make_epilogue(p, 5, act="gelu_tanh")
+    got, name, ws = gu.run_streamk(p, ep=ep)
+    want = gu.run_oracle(p, ep=ep)
+    bij = gu.all_bij(p)
+    idx = gu.flat_index(p, bij)
+    gu.assert_close_epilogue(got[idx], want[idx], p, ep, bij)
+    check_workspace_clean(p, ws, name)
+
+
+def test_data_parallel_choice_needs_no_workspace():
+    """Tiles that fill the waves (the 5000 x 3000 x 2050 problem: 240 for 256 units) run
+    the data-parallel kernel: workspace size 0, results as dmu_gemm."""
+    import torch
+
+    p = workloads.make("c3", "random", 27)
+    dA, dB = gu.to_dev(p.A), gu.to_dev(p.B)
+    dD = torch.zeros(p.stride_d, dtype=torch.int16, device="cuda:0")
+    args = gu.make_args(p, dA, dB, dD)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the 80 % rule is stated for 256 compute units")
+    assert dmu.dmu_gemm_streamk_workspace_size(args) == 0
+
+
+def test_fallback_shapes_need_no_workspace():
+    """Operands only the fallback can read run the data-parallel fallback, with no workspace."""
+    p = workloads.make("c1", "random", 25, M=130, N=70, K=255)  # odd K, row-major A: 2-byte rows
+    got, name, ws = gu.run_streamk(p)
+    assert "generic" in name and ws is None
+    gu.assert_close(got, gu.run_oracle(p), p, where=gu.valid_mask(p))
+
+
+def test_workspace_errors():
+    import torch
+
+    p = workloads.make("c3", "random", 26, M=700, N=500, K=1030)
+    dA, dB = gu.to_dev(p.A), gu.to_dev(p.B)
+    dD = torch.zeros(p.stride_d, dtype=torch.int16, device="cuda:0")
+    args = gu.make_args(p, dA, dB, dD)
+    n = dmu.dmu_gemm_streamk_workspace_size(args)
+    assert n > 0
+    ws = torch.zeros(n // 4 + 64, dtype=torch.int32, device="cuda:0")
+    assert dmu.dmu_gemm_streamk(args, None, ws, n - 4, check=False) == dmu.DMU_ERR_INVALID_ARG
+    assert dmu.dmu_gemm_streamk(args, None, None, n, check=False) == dmu.DMU_ERR_INVALID_ARG
+    assert dmu.dmu_gemm_streamk(args, None, ws.data_ptr() + 4, n, check=False) == dmu.DMU_ERR_INVALID_ARG
+    assert dmu.dmu_gemm_streamk(args, None, dD, n, check=False) == dmu.DMU_ERR_INVALID_ARG  # overlaps D
+
+
+def test_full_size_sampled(monkeypatch):
+    """The 5000 x 3000 x 2050 fp16 problem (240 tiles of the data-parallel kernel: full
+    enough waves that the call would choose the data-parallel kernel, so the schedule is
+    forced) on sampled outputs evaluated one by one by the oracle."""
+    monkeypatch.setenv("DMU_STREAMK", "always")
+    p = workloads.make("c3", "random", 0)
+    got, name, ws = gu.run_streamk(p)
+    bij = gu.sample_bij(p, n=384)
+    want = gu.oracle_at(p, bij)
+    gu.assert_close(got[gu.flat_index(p, bij)], want, p)
+    check_workspace_clean(p, ws, name)
