@@ -285,7 +285,10 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     o[e] = epi_one<O>(p.epi, p.act, v[e], rsv[mi][it], csv[e], bv[e], Crow != nullptr, c[e]);
-                *reinterpret_cast<ov4 *>(Drow + n) = o;
+                // streaming store: D is not read again by this kernel, and all
+                // tiles write it in one burst at the end (measured on 4096^3
+                // bf16: 113 -> 110 us)
+                __builtin_nontemporal_store(o, reinterpret_cast<ov4 *>(Drow + n));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
