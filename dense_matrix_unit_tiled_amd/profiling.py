@@ -126,7 +126,6 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
                        "fetch_factor": f_factor, "write_factor": w_factor,
                        "traffic_bytes_per_launch": fetch_b + write_b,
                        "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b})
-        json.dump(result, open(os.path.join(profiles, f"traffic_{workload_name}.json"), "w"), indent=1)
         md = [f"# HBM traffic: {workload_name}", "",
               "Commands (from the repository root on the GPU host):", "", "```",
               commands["fetch"], commands["write"], "```", "",
@@ -172,4 +171,6 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
             md += [f"LDS bank-conflict cycles / LDS active cycles = {conflict / active:.3f}."]
             result["lds_conflict_fraction"] = conflict / active
         open(os.path.join(profiles, f"{kernel_label}_{workload_name}_counters.md"), "w").write("\n".join(md) + "\n")
+    if "traffic_bytes_per_launch" in result:
+        json.dump(result, open(os.path.join(profiles, f"traffic_{workload_name}.json"), "w"), indent=1)
     return result
