@@ -78,8 +78,17 @@ template <> struct Pack16<BF16> {
 
 __device__ __forceinline__ float row_max4(float v) // over the lanes l, l^16, l^32, l^48
 {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
+    // v_permlane16_swap / v_permlane32_swap with both operands v return the
+    // values of lanes l and l^16 (l^32) in some order (probed): the max of the
+    // pair is the max over the two lanes, without an LDS round trip
+    const uint32_t x = __builtin_bit_cast(uint32_t, v);
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const uint32_t a0 = a[0], a1 = a[1];
+    v = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+    const uint32_t y = __builtin_bit_cast(uint32_t, v);
+    const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    const uint32_t b0 = b[0], b1 = b[1];
+    return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
 }
 
 template <bool B> using Bool = std::integral_constant<bool, B>;
