@@ -56,10 +56,15 @@ STREAMK_WORKLOADS = {"lksk": "lk"}
 EPILOGUE_WORKLOADS = {"c5dq": ("c5", "bf16", "gelu_tanh")}
 
 
-def source_digest() -> str:
-    """Digest of the kernel sources (a stored counter reading is valid only for these)."""
+def source_digest(workload: str = "c2") -> str:
+    """Digest of the sources a workload's kernel is built from (a stored counter reading is
+    valid only for these): every kernel source except the layout probes, and the attention
+    source only for the attention workloads."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "dense_matrix_unit_tiled_amd", "csrc", "*"))):
+        name = os.path.basename(f)
+        if name == "dmu_probe.hip" or (name == "dmu_attention.hip" and workload not in ATTENTION_WORKLOADS):
+            continue
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -70,7 +75,7 @@ def stored_traffic(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
+    if rec.get("source_digest") != source_digest(workload) or rec.get("kernel") != kernel:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -245,7 +250,7 @@ def main() -> int:
 
         kernel = kernel_for(args.workload)
         res = profiling.summarize(args.summarize, os.path.join(ROOT, "profiles"), WORKLOAD_NAMES[args.workload],
-                                  kernel, source_digest(),
+                                  kernel, source_digest(args.workload),
                                   profile_commands(args.workload, "gpurun_out/prof_" + args.workload),
                                   timed=200)
         print(json.dumps(res))

@@ -35,6 +35,7 @@ DMU_PROBE_LDS_READ_B128 = 10
 DMU_PROBE_LDS_READ_TR16 = 11
 DMU_PROBE_LDS_FRAG = 12
 DMU_PROBE_LDS_FRAG_T = 13
+DMU_PROBE_LANE_SWAP = 14
 DMU_PROBE_CVT_BF16 = 30
 DMU_PROBE_CVT_F16 = 31
 

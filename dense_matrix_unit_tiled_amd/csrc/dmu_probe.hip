@@ -75,6 +75,20 @@ __global__ void __launch_bounds__(64) probe_mfma(const char *a, const char *bt, 
     }
 }
 
+// v_permlane16_swap / v_permlane32_swap with both operands equal: lane l writes
+// the two results of each.
+__global__ void __launch_bounds__(64) probe_lane_swap(const uint32_t *in, uint32_t *out)
+{
+    const uint32_t l = threadIdx.x, v = in[l];
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    const uint32_t a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+    out[4 * l + 0] = a0;
+    out[4 * l + 1] = a1;
+    out[4 * l + 2] = b0;
+    out[4 * l + 3] = b1;
+}
+
 // LDS image of 4096 bytes: each of the 64 lanes copies 64 bytes.
 __device__ __forceinline__ void probe_fill_lds(char *lds, const char *img, uint32_t l)
 {
@@ -191,6 +205,7 @@ extern "C" int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type,
     case DMU_PROBE_LDS_READ_TR16: r = 2; break;
     case DMU_PROBE_LDS_FRAG: r = 16; break;
     case DMU_PROBE_LDS_FRAG_T: r = 64; break;
+    case DMU_PROBE_LANE_SWAP: t = DMU_I32, r = 4; break;
     case DMU_PROBE_CVT_BF16: t = DMU_F32, r = 2; break; /* 4 halves per lane */
     case DMU_PROBE_CVT_F16: t = DMU_F32, r = 2; break;
     default:
@@ -238,6 +253,9 @@ extern "C" int dmu_probe(int variant, const void *in0, const void *in1, void *ou
         break;
     case DMU_PROBE_LDS_FRAG: hipLaunchKernelGGL(probe_lds_frag, dim3(1), dim3(64), 0, s, a, o); break;
     case DMU_PROBE_LDS_FRAG_T: hipLaunchKernelGGL(probe_lds_frag_t, dim3(1), dim3(64), 0, s, a, o); break;
+    case DMU_PROBE_LANE_SWAP:
+        hipLaunchKernelGGL(probe_lane_swap, dim3(1), dim3(64), 0, s, reinterpret_cast<const uint32_t *>(a), o);
+        break;
     case DMU_PROBE_CVT_BF16:
         hipLaunchKernelGGL(probe_cvt<BF16>, dim3(1), dim3(64), 0, s, reinterpret_cast<const float *>(a),
                            reinterpret_cast<uint16_t *>(o));

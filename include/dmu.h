@@ -306,6 +306,7 @@ const char *dmu_last_error(void);
  *                           row-major (logical)                      [16 bytes]
  *  DMU_PROBE_LDS_FRAG_T     64 x 128 16-bit tile, unused             [64][8 column blocks][2 K-steps]
  *                           row-major (logical)                      [8 16-bit values]
+ *  DMU_PROBE_LANE_SWAP      uint32[64]            unused             [64][4] 32-bit words
  *  DMU_PROBE_CVT_BF16/_F16  float32[256]          unused             [256] 16-bit patterns
  *
  *  MFMA_*: lane l loads its operand fragments straight from in0/in1 with the
@@ -323,6 +324,9 @@ const char *dmu_last_error(void);
  *    staging writes of an M/N-contiguous operand and read back with its
  *    transposing fragment reads (column 16 b + l % 16, k = 32 ks + 8 (l / 16)
  *    + 0..7).
+ *  LANE_SWAP: lane l passes in0[l] as both operands of v_permlane16_swap and
+ *    of v_permlane32_swap and writes the two results of each (the attention
+ *    kernel's row max reads the pair as {value of lane l, of lane l^16 / l^32}).
  *  CVT_*: the GEMM epilogue's fp32 -> bf16 / fp16 conversion.
  * dmu_probe_info() reports m, n, k, the input type and the number of 32-bit
  * output words per lane.  `stream` as for dmu_gemm.
@@ -339,6 +343,7 @@ enum {
     DMU_PROBE_LDS_READ_TR16 = 11,
     DMU_PROBE_LDS_FRAG = 12,
     DMU_PROBE_LDS_FRAG_T = 13,
+    DMU_PROBE_LANE_SWAP = 14,
     DMU_PROBE_CVT_BF16 = 30,
     DMU_PROBE_CVT_F16 = 31
 };

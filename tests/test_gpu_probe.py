@@ -215,3 +215,18 @@ def test_epilogue_conversion_rounds_to_nearest_even(t, variant):
     want = oracle.encode(t, x.astype(np.float64))
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
+
+
+def test_lane_swap_pairs():
+    """v_permlane16_swap / v_permlane32_swap with equal operands give each lane the values of
+    lanes l and l^16 (l^32), in some order: the attention kernel's row max over 4 lanes."""
+    import torch
+
+    vals = (np.arange(64, dtype=np.uint32) * 7919 + 13).astype(np.uint32)
+    out = torch.zeros(64 * 4, dtype=torch.int32, device="cuda:0")
+    dmu.dmu_probe(dmu.DMU_PROBE_LANE_SWAP, gu.to_dev(vals.view(np.int32)), None, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32).reshape(64, 4)
+    for lane in range(64):
+        assert sorted(got[lane, :2]) == sorted([vals[lane], vals[lane ^ 16]]), lane
+        assert sorted(got[lane, 2:]) == sorted([vals[lane], vals[lane ^ 32]]), lane
