@@ -95,6 +95,28 @@ def profile_commands(workload: str, d: str) -> dict:
     }
 
 
+def algorithmic_bytes(p, ep_bytes: int = 0) -> int:
+    """Bytes one launch must move at least: A, B and D once (C once more when present), plus
+    the epilogue vectors."""
+    esz = {"f16": 2, "bf16": 2, "i8": 1, "e4m3": 1}[p.in_type]
+    osz = {"f32": 4, "i32": 4, "f16": 2, "bf16": 2}[p.out_type]
+    mn = p.batch * p.M * p.N
+    return (p.batch * (p.M + p.N) * p.K * esz + mn * osz * (2 if p.C is not None else 1) + ep_bytes)
+
+
+def roofline(flops: float, nbytes: float, seconds: float, peak_tflops: float, traffic) -> dict:
+    """The bound of the launch by its algorithmic intensity against the chip's ridge: the
+    matrix cores (TFLOP/s against the dtype's dense peak) or HBM (GB/s against 8 TB/s)."""
+    ridge = peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
+    if flops / nbytes >= ridge:
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(a, 3), "peak": peak_tflops, "unit": "TFLOP/s",
+                "frac": round(a / peak_tflops, 4), "traffic": traffic}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
 def kernel_for(workload: str) -> str:
     """Name of the kernel variant the workload's call selects (host-side query, no GPU)."""
     import dense_matrix_unit_tiled_amd as dmu
@@ -213,8 +235,8 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
         "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": batch, "seq_q": sq, "seq_k": sk,
                    "head_dim": hd, "in_type": in_t, "out_type": out_t, "kernel": kernel,
                    "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": stored_traffic(args.workload, kernel)},
+        "roofline": roofline(flops, batch * (sq + 2 * sk) * hd * 2 + batch * sq * hd * (4 if out_t == "f32" else 2),
+                             ms * 1e-3, peak, stored_traffic(args.workload, kernel)),
         "cpu_baseline": None if args.no_cpu_baseline else
         attention_cpu_baseline(batch, sq, sk, hd, Q, K, V, in_t, out_t, scale),
     }
@@ -274,11 +296,13 @@ def main() -> int:
         return run_attention(args, dmu, workloads, torch, np, to_dev)
 
     ep = None
+    ep_bytes = 0
     if args.workload in EPILOGUE_WORKLOADS:
         base, out_t, act = EPILOGUE_WORKLOADS[args.workload]
         p = workloads.with_output(workloads.make(base, "random", 0), out_t)
         e = workloads.make_epilogue(p, 0, act=act)
         ep_vecs = [to_dev(v) for v in (e.row_scale, e.col_scale, e.bias)]  # kept alive for the launches
+        ep_bytes = sum(v.size * 4 for v in (e.row_scale, e.col_scale, e.bias))
         ep = dmu.epilogue_args(row_scale=ep_vecs[0], stride_row_scale=e.stride_rs, col_scale=ep_vecs[1],
                                stride_col_scale=e.stride_cs, bias=ep_vecs[2], stride_bias=e.stride_bias,
                                act=e.act)
@@ -339,8 +363,7 @@ def main() -> int:
                    "batch": p.batch, "layout_a": p.layout_a, "layout_b": p.layout_b,
                    "in_type": p.in_type, "acc_type": p.acc_type, "out_type": p.out_type,
                    "kernel": kernel, "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        "roofline": roofline(flops, algorithmic_bytes(p, ep_bytes), ms * 1e-3, peak, traffic),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p)

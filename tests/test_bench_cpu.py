@@ -1,0 +1,36 @@
+"""bench.py's host logic (CPU only): the roofline bound of each workload and the one-GPU rule."""
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import pytest
+
+import bench
+import workloads
+
+
+def full(cfg):
+    M, N, K, b, it, ot, at, la, lb = workloads.FULL[cfg]
+    return SimpleNamespace(M=M, N=N, K=K, batch=b, in_type=it, out_type=ot, C=None)
+
+
+@pytest.mark.parametrize("cfg,bound", [("c2", "mfma"), ("c5", "mfma"), ("c6", "mfma"), ("c3", "mfma"),
+                                       ("c4s", "hbm"), ("c4o", "hbm")])
+def test_roofline_bound_by_intensity(cfg, bound):
+    p = full(cfg)
+    r = bench.roofline(2.0 * p.M * p.N * p.K * p.batch, bench.algorithmic_bytes(p), 1e-4,
+                       bench.PEAK_TFLOPS[p.in_type], None)
+    assert r["bound"] == bound
+    assert r["unit"] == ("TFLOP/s" if bound == "mfma" else "GB/s")
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-3)
+
+
+def test_algorithmic_bytes_of_the_4096_cube():
+    # A and B bf16 (2 x 32 MiB) + D bf16 (32 MiB)
+    assert bench.algorithmic_bytes(full("c2")) == 3 * 4096 * 4096 * 2
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
+                       cwd=bench.ROOT, timeout=60)
+    assert r.returncode != 0 and "one GPU" in r.stderr
