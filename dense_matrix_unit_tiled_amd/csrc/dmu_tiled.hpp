@@ -223,44 +223,21 @@ template <int R, int NW> struct TileOf<MC16, R, NW> { typedef McTile<R, NW> type
 // values, with the fused epilogue (scales, bias, C, activation), RNE
 // conversion and M/N masking on the way out.
 // ---------------------------------------------------------------------------
-template <int O, int MT, int NT, class AccT>
-__device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&acc)[MT][NT], char *lds,
-                                             int64_t m_base, int64_t n_base, uint32_t lane, const char *Cb,
-                                             char *Db, const EpiPtrs &ep)
-{
-    typedef typename Out<O>::t ot;
-    typedef decltype(acc[0][0][0]) sref;
-    typedef typename std::remove_const<typename std::remove_reference<sref>::type>::type st; // float or int
-    typedef st st4 __attribute__((ext_vector_type(4)));
-    typedef ot ov4 __attribute__((ext_vector_type(4)));
-    constexpr int COLS = 16 * NT;
-    constexpr int PITCH = COLS * 4 + 16; // bytes per parked row (+16 spreads rows over the banks)
-    constexpr int LPR = COLS / 4;        // lanes per row on the way out
-    constexpr int RPI = 64 / LPR;        // rows per store instruction
-    constexpr int ITS = 16 / RPI;        // store instructions per 16-row stripe
-    // On the way out lane l always handles the same four columns (n_base +
-    // 4 (l % LPR) ..) and, in stripe mi and store it, row 16 mi + RPI it + l / LPR:
-    // its epilogue operands are fetched once, up front, instead of in the
-    // store loop (where every fetch would stall the loop).
-    float rsv[MT][ITS], csv[4], bv[4];
+// Geometry of the parked stripes: a 16-row stripe of 16 NT accumulator
+// columns per wavefront, read back by LPR lanes per row, RPI rows per store
+// instruction, ITS instructions per stripe.
+template <int NT> struct Park {
+    static constexpr int COLS = 16 * NT;
+    static constexpr int PITCH = COLS * 4 + 16; // bytes per parked row (+16 spreads rows over the banks)
+    static constexpr int LPR = COLS / 4;
+    static constexpr int RPI = 64 / LPR;
+    static constexpr int ITS = 16 / RPI;
+    // Stripe: lane l's accumulator tile ni holds row l % 16, columns 16 ni + 4 (l / 16) ..
+    template <class AccT, int MT>
+    static __device__ __forceinline__ void put(char *lds, const AccT (&acc)[MT][NT], int mi, uint32_t lane)
     {
-        const int64_t n0 = n_base + 4 * (lane % LPR);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool in = n0 + e < p.N;
-            csv[e] = ep.cs && in ? ep.cs[n0 + e] : 1.0f;
-            bv[e] = ep.bias && in ? ep.bias[n0 + e] : 0.0f;
-        }
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-            for (int it = 0; it < ITS; ++it) {
-                const int64_t m = m_base + mi * 16 + RPI * it + lane / LPR;
-                rsv[mi][it] = ep.rs && m < p.M ? ep.rs[m] : 1.0f;
-            }
-    }
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
+        typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
+        typedef st st4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) {
             st4 v;
@@ -269,32 +246,202 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
                 v[e] = acc[mi][ni][e];
             *reinterpret_cast<st4 *>(lds + (lane & 15u) * PITCH + (ni * 16 + 4 * (lane >> 4)) * 4) = v;
         }
+    }
+};
+
+// A wavefront block wholly inside D (every row < M, every 4-column vector
+// < N and aligned), with the epilogue's form fixed at compile time.
+template <int O, int MT, int NT, bool HAS_C, bool EPI, int ACT, class AccT>
+__device__ __forceinline__ void store_interior(const GemmParams &p, const AccT (&acc)[MT][NT], char *lds,
+                                               int64_t m_base, uint32_t lane, int64_t n, const char *Cb,
+                                               char *Db, const EpiPtrs &ep)
+{
+    typedef Park<NT> K;
+    typedef typename Out<O>::t ot;
+    typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
+    typedef st st4 __attribute__((ext_vector_type(4)));
+    typedef ot ov4 __attribute__((ext_vector_type(4)));
+    const uint32_t col = (lane % K::LPR) * 4, r0 = lane / K::LPR;
+    float csv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, bv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, rsv[MT][K::ITS];
+    if constexpr (EPI) {
 #pragma unroll
-        for (int it = 0; it < ITS; ++it) {
-            const uint32_t row = RPI * it + lane / LPR, col = (lane % LPR) * 4;
-            const st4 v = *reinterpret_cast<const st4 *>(lds + row * PITCH + col * 4);
-            const int64_t m = m_base + mi * 16 + row, n = n_base + col;
+        for (int e = 0; e < 4; ++e) {
+            csv[e] = ep.cs ? ep.cs[n + e] : 1.0f;
+            bv[e] = ep.bias ? ep.bias[n + e] : 0.0f;
+        }
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int it = 0; it < K::ITS; ++it)
+                rsv[mi][it] = ep.rs ? ep.rs[m_base + mi * 16 + K::RPI * it + r0] : 1.0f;
+    }
+    const int64_t rel = (m_base + r0) * p.ldd + n; // this lane's first element of D
+    ot *D0 = reinterpret_cast<ot *>(Db) + rel;
+    const ot *C0 = HAS_C ? reinterpret_cast<const ot *>(Cb) + (m_base + r0) * p.ldc + n : nullptr;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+        ov4 c[K::ITS];
+        if constexpr (HAS_C) {
+#pragma unroll
+            for (int it = 0; it < K::ITS; ++it)
+                c[it] = *reinterpret_cast<const ov4 *>(C0 + (int64_t)(mi * 16 + K::RPI * it) * p.ldc);
+        }
+        K::put(lds, acc, mi, lane);
+#pragma unroll
+        for (int it = 0; it < K::ITS; ++it) {
+            const st4 v = *reinterpret_cast<const st4 *>(lds + (K::RPI * it + r0) * K::PITCH + col * 4);
+            ov4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = epi_one<O>(EPI, ACT, v[e], EPI ? rsv[mi][it] : 1.0f, csv[e], bv[e], HAS_C,
+                                  HAS_C ? c[it][e] : ot{});
+            // streaming store: D is not read again by this kernel, and all
+            // tiles write it in one burst at the end (measured on 4096^3
+            // bf16: 113 -> 110 us)
+            __builtin_nontemporal_store(o, reinterpret_cast<ov4 *>(D0 + (int64_t)(mi * 16 + K::RPI * it) * p.ldd));
+        }
+    }
+}
+
+// A plain block (no C, no epilogue operations) that crosses the M or N edge:
+// rows past M are skipped and a vector that crosses N is stored element by
+// element, with no other per-row decisions.
+template <int O, int MT, int NT, class AccT>
+__device__ __forceinline__ void store_edge_plain(const GemmParams &p, const AccT (&acc)[MT][NT], char *lds,
+                                                 int64_t m_base, uint32_t lane, int64_t n, char *Db)
+{
+    typedef Park<NT> K;
+    typedef typename Out<O>::t ot;
+    typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
+    typedef st st4 __attribute__((ext_vector_type(4)));
+    typedef ot ov4 __attribute__((ext_vector_type(4)));
+    const uint32_t col = (lane % K::LPR) * 4, r0 = lane / K::LPR;
+    const bool vec = p.d_vec4 && n + 3 < p.N;
+    const int nv = n >= p.N ? 0 : (p.N - n < 4 ? (int)(p.N - n) : 4); // valid elements of this lane's vector
+    ot *D0 = reinterpret_cast<ot *>(Db) + (m_base + r0) * p.ldd + n;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+        K::put(lds, acc, mi, lane);
+#pragma unroll
+        for (int it = 0; it < K::ITS; ++it) {
+            const st4 v = *reinterpret_cast<const st4 *>(lds + (K::RPI * it + r0) * K::PITCH + col * 4);
+            if (m_base + mi * 16 + K::RPI * it + r0 >= p.M)
+                continue;
+            ov4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = epi_one<O>(0, 0, v[e], 1.0f, 1.0f, 0.0f, false, ot{});
+            ot *d = D0 + (int64_t)(mi * 16 + K::RPI * it) * p.ldd;
+            if (vec) {
+                __builtin_nontemporal_store(o, reinterpret_cast<ov4 *>(d));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (e < nv)
+                        d[e] = o[e];
+            }
+        }
+    }
+}
+
+// A wavefront's MT x NT block of accumulator tiles to D, through the LDS
+// park (lds: this wavefront's PARK bytes), with the fused epilogue.
+template <int O, int MT, int NT, class AccT>
+__device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&acc)[MT][NT], char *lds,
+                                             int64_t m_base, int64_t n_base, uint32_t lane, const char *Cb,
+                                             char *Db, const EpiPtrs &ep)
+{
+    typedef Park<NT> K;
+    typedef typename Out<O>::t ot;
+    typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
+    typedef st st4 __attribute__((ext_vector_type(4)));
+    typedef ot ov4 __attribute__((ext_vector_type(4)));
+    // On the way out lane l always handles the same four columns (n_base +
+    // 4 (l % LPR) ..) and, in stripe mi and store it, row 16 mi + RPI it + l / LPR.
+    const uint32_t col = (lane % K::LPR) * 4, r0 = lane / K::LPR;
+    const int64_t n = n_base + col;
+
+    // A block wholly inside D with 4-element vectors legal needs no per-row
+    // decisions.  The epilogue's form (C or not, scales and bias or not,
+    // activation) is uniform, so it is decided once here and each form is a
+    // branch-free instantiation: per-element branches cost more than the
+    // arithmetic (the plain 4096^3 bf16 product: 112 -> 104 us; the batched
+    // 4096 x 4096 x 128 product, 32 tiles per compute unit: 524 -> 427 us).
+    if (p.d_vec4 && m_base + 16 * MT <= p.M && n_base + K::COLS <= p.N) {
+        const int form = (Cb ? 1 : 0) | (p.epi ? 2 : 0);
+        switch (form * 3 + (p.act == 1 ? 1 : p.act == 2 ? 2 : 0)) {
+        case 0: return store_interior<O, MT, NT, false, false, 0>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 1: return store_interior<O, MT, NT, false, false, 1>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 2: return store_interior<O, MT, NT, false, false, 2>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 3: return store_interior<O, MT, NT, true, false, 0>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 4: return store_interior<O, MT, NT, true, false, 1>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 5: return store_interior<O, MT, NT, true, false, 2>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 6: return store_interior<O, MT, NT, false, true, 0>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 7: return store_interior<O, MT, NT, false, true, 1>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 8: return store_interior<O, MT, NT, false, true, 2>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 9: return store_interior<O, MT, NT, true, true, 0>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        case 10: return store_interior<O, MT, NT, true, true, 1>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        default: return store_interior<O, MT, NT, true, true, 2>(p, acc, lds, m_base, lane, n, Cb, Db, ep);
+        }
+    }
+    if (!Cb && !p.epi && !p.act)
+        return store_edge_plain<O, MT, NT>(p, acc, lds, m_base, lane, n, Db);
+
+    // Any other block: per-row and per-element decisions, one row group per
+    // iteration (a loop rather than unrolled, to keep this rarely taken path
+    // small).  Row scales are fetched up front: fetched in the loop they would
+    // stall every iteration.
+    const bool vec = p.d_vec4 && n + 3 < p.N; // whole 4-element vector inside D (and aligned)
+    float rsv[MT][K::ITS], csv[4], bv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool in = n + e < p.N;
+        csv[e] = ep.cs && in ? ep.cs[n + e] : 1.0f;
+        bv[e] = ep.bias && in ? ep.bias[n + e] : 0.0f;
+    }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int it = 0; it < K::ITS; ++it) {
+            const int64_t m = m_base + mi * 16 + K::RPI * it + r0;
+            rsv[mi][it] = ep.rs && m < p.M ? ep.rs[m] : 1.0f;
+        }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+        K::put(lds, acc, mi, lane);
+#pragma nounroll
+        for (int it = 0; it < K::ITS; ++it) {
+            float rs = rsv[mi][0];
+#pragma unroll
+            for (int i = 1; i < K::ITS; ++i)
+                rs = it == i ? rsv[mi][i] : rs;
+            const uint32_t row = K::RPI * it + r0;
+            const st4 v = *reinterpret_cast<const st4 *>(lds + row * K::PITCH + col * 4);
+            const int64_t m = m_base + mi * 16 + row;
             if (m >= p.M)
                 continue;
             const ot *Crow = Cb ? reinterpret_cast<const ot *>(Cb) + m * p.ldc : nullptr;
             ot *Drow = reinterpret_cast<ot *>(Db) + m * p.ldd;
-            if (p.d_vec4 && n + 3 < p.N) {
-                ov4 c = {}, o;
-                if (Crow)
+            ov4 c = {}, o;
+            if (Crow) {
+                if (vec)
                     c = *reinterpret_cast<const ov4 *>(Crow + n);
+                else
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = epi_one<O>(p.epi, p.act, v[e], rsv[mi][it], csv[e], bv[e], Crow != nullptr, c[e]);
-                // streaming store: D is not read again by this kernel, and all
-                // tiles write it in one burst at the end (measured on 4096^3
-                // bf16: 113 -> 110 us)
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < p.N)
+                            c[e] = Crow[n + e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = epi_one<O>(p.epi, p.act, v[e], rs, csv[e], bv[e], Crow != nullptr, c[e]);
+            if (vec) {
                 __builtin_nontemporal_store(o, reinterpret_cast<ov4 *>(Drow + n));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (n + e < p.N)
-                        Drow[n + e] = epi_one<O>(p.epi, p.act, v[e], rsv[mi][it], csv[e], bv[e], Crow != nullptr,
-                                                 Crow ? Crow[n + e] : ot{});
+                        Drow[n + e] = o[e];
             }
         }
     }
@@ -332,7 +479,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     static constexpr int NA = ATile::NL, NB = BTile::NL;
     static constexpr uint32_t ABYTES = (ATile::BYTES + 255) & ~255u,
                               STAGE = (ABYTES + BTile::BYTES + 255) & ~255u;
-    static constexpr int PARK = 16 * (16 * NT * 4 + 16); // per wavefront, epilogue
+    static constexpr int PARK = 16 * Park<NT>::PITCH; // per wavefront, epilogue
     static_assert(NW * PARK <= 2 * STAGE, "parking area fits in the stages");
     static constexpr uint32_t PARTIAL_BYTES = NW * MN * 1024; // one tile's accumulators
 
