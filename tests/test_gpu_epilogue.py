@@ -42,6 +42,31 @@ def test_reduced_parity(cfg, out_t, act, kernel):
     gu.assert_close_epilogue(got[idx], want[idx], p, ep, bij)
 
 
+@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("cfg,out_t", [("c2", "bf16"), ("c5", "f32")])
+def test_every_form_on_every_tile(tile, cfg, out_t):
+    """The store code has one instantiation per epilogue form (C or not, scales and bias or
+    not, no activation / ReLU / GELU) for wavefront blocks inside D and another path for
+    blocks on the M/N edge: every form, on each tiled configuration, on a problem with
+    both kinds of block, element by element against the oracle."""
+    for with_c in (False, True):
+        p = problem(cfg, out_t, 21, with_c=with_c, M=600, N=560, K=192)
+        for vectors in (False, True):
+            for act in ("none", "relu", "gelu_tanh"):
+                ep = None
+                if vectors or act != "none":
+                    ep = workloads.make_epilogue(p, 7, act=act, row=vectors, col=vectors, bias=vectors)
+                got, name = gu.run_dmu(p, force=tile, ep=ep, return_name=True)
+                assert tile in name, name
+                want = gu.run_oracle(p, ep=ep)
+                bij = gu.all_bij(p)
+                idx = gu.flat_index(p, bij)
+                if ep is None:
+                    gu.assert_close(got[idx], want[idx], p)
+                else:
+                    gu.assert_close_epilogue(got[idx], want[idx], p, ep, bij)
+
+
 @pytest.mark.parametrize("parts", [(True, False, False), (False, True, False), (False, False, True),
                                    (True, True, False)])
 @pytest.mark.parametrize("cfg,out_t", [("c5", "bf16"), ("c2", "f32")])
