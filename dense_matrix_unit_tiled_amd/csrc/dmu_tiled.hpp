@@ -477,6 +477,12 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     typedef typename TileOf<AMODE, BM, NW>::type ATile;
     typedef typename TileOf<BMODE, BN, NW>::type BTile;
     static constexpr int NA = ATile::NL, NB = BTile::NL;
+    // Prefetch depth: K-tiles in flight in staging registers.  Two where the
+    // registers allow (every configuration but 256 x 256, whose accumulators
+    // and fragments leave room for one set): the loads of K-tile kt+3 go out
+    // while K-tile kt+1 is written to LDS, which doubles the bytes in flight
+    // per compute unit for the HBM-bound shapes.  (e4m3 keeps its own loop.)
+    static constexpr int PD = (BM * BN < 256 * 256 && !F8) ? 2 : 1;
     static constexpr uint32_t ABYTES = (ATile::BYTES + 255) & ~255u,
                               STAGE = (ABYTES + BTile::BYTES + 255) & ~255u;
     static constexpr int PARK = 16 * Park<NT>::PITCH; // per wavefront, epilogue
@@ -516,18 +522,19 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         tb.init(p.ldb * E, wave, lane);
     const uint32_t k_bytes = (uint32_t)p.K * E;
 
-    u32x4 sa[NA], sb[NB]; // the next K-tile between its global loads and its LDS writes
-    auto load_one = [&](int c, int kt) {
+    // K-tiles between their global loads and their LDS writes, PD sets
+    u32x4 sa[PD][NA], sb[PD][NB];
+    auto load_one = [&](int c, int kt, int set = 0) {
         if (c < NA)
-            sa[c] = ta.load(c, ra, kt, k_bytes);
+            sa[set][c] = ta.load(c, ra, kt, k_bytes);
         else
-            sb[c - NA] = tb.load(c - NA, rb, kt, k_bytes);
+            sb[set][c - NA] = tb.load(c - NA, rb, kt, k_bytes);
     };
-    auto store_one = [&](int c, char *stage, int kt) { // staging register c holds K-tile kt
+    auto store_one = [&](int c, char *stage, int kt, int set = 0) { // staging set holds K-tile kt
         if (c < NA)
-            ta.store(c, stage, wave, lane, sa[c], kt, k_bytes);
+            ta.store(c, stage, wave, lane, sa[set][c], kt, k_bytes);
         else
-            tb.store(c - NA, stage + ABYTES, wave, lane, sb[c - NA], kt, k_bytes);
+            tb.store(c - NA, stage + ABYTES, wave, lane, sb[set][c - NA], kt, k_bytes);
     };
 
     // Operand fragments of one K-step (e4m3: both K-step halves of the K-tile,
@@ -553,7 +560,8 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     constexpr int NLD = NA + NB;
 
     {
-        char *first = smem + (kb & 1) * STAGE;
+        // with two staging sets the stages alternate from stage 0 at kb
+        char *first = PD == 2 ? smem : smem + (kb & 1) * STAGE;
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
             load_one(c, kb);
@@ -562,7 +570,12 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
             store_one(c, first, kb);
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
-            load_one(c, kb + 1);
+            load_one(c, kb + 1, PD - 1);
+        if constexpr (PD == 2) {
+#pragma unroll
+            for (int c = 0; c < NLD; ++c)
+                load_one(c, kb + 2, 0);
+        }
         stage_barrier();
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -621,10 +634,10 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-    } else
-    for (int kt = kb; kt < ke; ++kt) {
-        const char *cur = smem + (kt & 1) * STAGE;
-        char *nxt = smem + ((kt + 1) & 1) * STAGE;
+    } else {
+    // One K-tile: K-tile kt is in stage cur, K-tile kt+1 goes from staging
+    // set `set` to stage nxt, and K-tile kt+1+PD is loaded into that set.
+    auto ktile = [&](int kt, const char *cur, char *nxt, int set) __attribute__((always_inline)) {
         // K-step 0; each fragment of K-step 1 is read right after its last use.
 #pragma unroll
         for (int q = 0; q < MN; ++q) {
@@ -637,8 +650,8 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
                 read_a(i, cur, 1);
 #pragma unroll
             for (int ci = q * NLD / SLOTS; ci < (q + 1) * NLD / SLOTS; ++ci) {
-                store_one(ci, nxt, kt + 1);
-                load_one(ci, kt + 2);
+                store_one(ci, nxt, kt + 1, set);
+                load_one(ci, kt + 1 + PD, set);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -651,8 +664,8 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
             const int slot = MN + q;
 #pragma unroll
             for (int ci = slot * NLD / SLOTS; ci < (slot + 1) * NLD / SLOTS; ++ci) {
-                store_one(ci, nxt, kt + 1);
-                load_one(ci, kt + 2);
+                store_one(ci, nxt, kt + 1, set);
+                load_one(ci, kt + 1 + PD, set);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -673,8 +686,22 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
                 read_a(i, nxt, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    if constexpr (PD == 2) {
+        // two K-tiles per iteration: the staging set and both stages are
+        // fixed for each of them
+        int kt = kb;
+        for (; kt + 1 < ke; kt += 2) {
+            ktile(kt, smem, smem + STAGE, 1);
+            ktile(kt + 1, smem + STAGE, smem, 0);
+        }
+        if (kt < ke)
+            ktile(kt, smem, smem + STAGE, 1);
+    } else {
+        for (int kt = kb; kt < ke; ++kt)
+            ktile(kt, smem + (kt & 1) * STAGE, smem + ((kt + 1) & 1) * STAGE, 0);
     }
-
+    }
     }
 
     // D = epilogue(acc) for tile tc.  Every wavefront must be past the last
