@@ -481,8 +481,8 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     // registers allow (every configuration but 256 x 256, whose accumulators
     // and fragments leave room for one set): the loads of K-tile kt+3 go out
     // while K-tile kt+1 is written to LDS, which doubles the bytes in flight
-    // per compute unit for the HBM-bound shapes.  (e4m3 keeps its own loop.)
-    static constexpr int PD = (BM * BN < 256 * 256 && !F8) ? 2 : 1;
+    // per compute unit.
+    static constexpr int PD = BM * BN < 256 * 256 ? 2 : 1;
     static constexpr uint32_t ABYTES = (ATile::BYTES + 255) & ~255u,
                               STAGE = (ABYTES + BTile::BYTES + 255) & ~255u;
     static constexpr int PARK = 16 * Park<NT>::PITCH; // per wavefront, epilogue
@@ -606,16 +606,15 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         // other stage right after its last use (the first half's A rows at
         // once).  Every read of a stage happens before the barrier that
         // precedes its overwrite.
-        for (int kt = kb; kt < ke; ++kt) {
-            char *nxt = smem + ((kt + 1) & 1) * STAGE;
+        auto ktile8 = [&](int kt, char *nxt, int set) __attribute__((always_inline)) {
 #pragma unroll
             for (int q = 0; q < HALF; ++q) {
                 mfma(row_of(q), col_of(q));
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ci = q * NLD / HALF; ci < (q + 1) * NLD / HALF; ++ci) {
-                    store_one(ci, nxt, kt + 1);
-                    load_one(ci, kt + 2);
+                    store_one(ci, nxt, kt + 1, set);
+                    load_one(ci, kt + 1 + PD, set);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -633,6 +632,18 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
                     read_a(i, nxt, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        if constexpr (PD == 2) {
+            int kt = kb;
+            for (; kt + 1 < ke; kt += 2) {
+                ktile8(kt, smem + STAGE, 1);
+                ktile8(kt + 1, smem, 0);
+            }
+            if (kt < ke)
+                ktile8(kt, smem + STAGE, 1);
+        } else {
+            for (int kt = kb; kt < ke; ++kt)
+                ktile8(kt, smem + ((kt + 1) & 1) * STAGE, 0);
         }
     } else {
     // One K-tile: K-tile kt is in stage cur, K-tile kt+1 goes from staging
