@@ -241,10 +241,16 @@ int validate(const dmu_gemm_args *a, Plan *plan)
     const bool force_generic = env && strcmp(env, "generic") == 0;
     if (amode >= 0 && bmode >= 0 && !force_generic) {
         const int64_t big = ((M + 255) / 256) * ((N + 255) / 256) * batch;
+        const int64_t nk = (K * esz + 127) / 128; // K-tiles
         if (N <= 128 && M > 128)
             tile = TILE_256x128;
         else if (big >= 240)
-            tile = TILE_256x256;
+            // Two K-tiles or fewer: each tile is little more than its
+            // epilogue, and the 256 x 128 tile (two K-tiles in flight, half
+            // the D per tile) is faster (batch 32 x 4096 x 4096 x 128 fp16 ->
+            // fp32: 427 -> 401 us); from four K-tiles on, 256 x 256 is
+            // faster or equal (same shape with K = 256: 482 vs 531 us).
+            tile = nk <= 2 ? TILE_256x128 : TILE_256x256;
         else
             tile = TILE_128x128;
         if (env && strcmp(env, "256x256") == 0) tile = TILE_256x256;

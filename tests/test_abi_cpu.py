@@ -110,6 +110,11 @@ def test_empty_problems_launch_nothing():
           out_type="i32"), "mfma_256x256_k16_k16_i8_i32"),
     (dict(M=4096, N=128, K=4096, lda=4096, ldb=128, ldd=128, batch=32, stride_a=4096 * 4096,
           stride_b=4096 * 128, stride_d=4096 * 128), "mfma_256x128_k16_t16_f16_f32"),
+    # two K-tiles or fewer: 256 x 128 even with enough tiles for 256 x 256; four: 256 x 256
+    (dict(M=4096, N=4096, K=128, lda=128, layout_b="col", ldb=128, ldd=4096, batch=32,
+          stride_a=4096 * 128, stride_b=4096 * 128, stride_d=4096 * 4096), "mfma_256x128_k16_k16_f16_f32"),
+    (dict(M=4096, N=4096, K=256, lda=256, layout_b="col", ldb=256, ldd=4096, batch=32,
+          stride_a=4096 * 256, stride_b=4096 * 256, stride_d=4096 * 4096), "mfma_256x256_k16_k16_f16_f32"),
     (dict(A=FAKE + 2), "mfma_generic64_any_any_f16_f32"),       # 2-byte aligned A
     (dict(K=255, lda=255, ldb=256), "mfma_generic64_any_any_f16_f32"),  # odd K row-major A
     (dict(K=0, lda=1), "mfma_generic64_any_any_f16_f32"),
