@@ -9,7 +9,10 @@ large on purpose: after start-up or idle the GPU needs a few hundred launches
 (some tens of ms) to raise its shader clock, and timing from a cold start
 measures that ramp instead of the kernel.  Prints one JSON
 line with the throughput, the MFMA roofline of the kernel and the CPU oracle's
-rate on a bounded row slice of the same product.
+rate on a bounded row slice of the same product (and its per-core rate), plus
+medians of individually timed launches, warm and cold (a 1 GiB buffer written
+before each), and the dense peak re-derived from this machine's compute units
+and clock.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c6|lk|lksk|c4fa]
                   [--no-cpu-baseline] [--copy-calibration MiB]
@@ -56,14 +59,21 @@ STREAMK_WORKLOADS = {"lksk": "lk"}
 EPILOGUE_WORKLOADS = {"c5dq": ("c5", "bf16", "gelu_tanh")}
 
 
+# Host-only sources: argument checks, kernel selection, launch plumbing.  They do not change
+# a kernel's memory traffic, and a change of the kernel they select shows in its name, which
+# a stored reading is also checked against.
+HOST_SOURCES = {"dmu_host.hip", "dmu_host.hpp"}
+
+
 def source_digest(workload: str = "c2") -> str:
-    """Digest of the sources a workload's kernel is built from (a stored counter reading is
-    valid only for these): every kernel source except the layout probes, and the attention
-    source only for the attention workloads."""
+    """Digest of the device code a workload's kernel is built from (a stored counter reading is
+    valid only for it): every kernel source except the layout probes and the host-only files,
+    and the attention source only for the attention workloads."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "dense_matrix_unit_tiled_amd", "csrc", "*"))):
         name = os.path.basename(f)
-        if name == "dmu_probe.hip" or (name == "dmu_attention.hip" and workload not in ATTENTION_WORKLOADS):
+        if name == "dmu_probe.hip" or name in HOST_SOURCES or \
+                (name == "dmu_attention.hip" and workload not in ATTENTION_WORKLOADS):
             continue
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
@@ -152,11 +162,11 @@ def cpu_baseline(p, budget_s: float = 15.0):
 
     threads = oracle.default_threads()
 
-    def run(rows):
+    def run(rows, nthreads=threads):
         A = p.A[: rows * p.lda] if p.layout_a == "row" else p.A
         t0 = time.perf_counter()
         oracle.gemm(rows, p.N, p.K, A, p.lda, p.B, p.ldb, in_type=p.in_type, out_type=p.out_type,
-                    layout_a=p.layout_a, layout_b=p.layout_b, ldd=p.N, nthreads=threads)
+                    layout_a=p.layout_a, layout_b=p.layout_b, ldd=p.N, nthreads=nthreads)
         return time.perf_counter() - t0
 
     rows = threads
@@ -165,9 +175,14 @@ def cpu_baseline(p, budget_s: float = 15.0):
     rows2 = max(threads, (rows2 // threads) * threads)
     t2 = run(rows2)
     flops = 2.0 * rows2 * p.N * p.K
+    # one thread on a few rows: the per-core rate
+    r1 = min(p.M, 8)
+    t1 = run(r1, 1)
     return {"value": round(flops / t2 / 1e12, 6), "unit": "TFLOPS", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{rows2 - 1} of the {p.M}x{p.N}x{p.K} product "
-                      f"({rows2}x{p.N}x{p.K} MACs, {t2:.1f} s, fp64 sums, {threads} threads)"}
+                      f"({rows2}x{p.N}x{p.K} MACs, {t2:.1f} s, fp64 sums, {threads} threads)",
+            "per_core_value": round(2.0 * r1 * p.N * p.K / t1 / 1e12, 6),
+            "per_core_sample": f"rows 0..{r1 - 1}, one thread, {t1:.2f} s"}
 
 
 def attention_cpu_baseline(batch, sq, sk, hd, Q, K, V, in_t, out_t, scale, budget_s: float = 15.0):
@@ -216,6 +231,7 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
     for _ in range(args.warmup):
         dmu.dmu_attention(a, stream)
     torch.cuda.synchronize()
+    lt = launch_times(lambda: dmu.dmu_attention(a, stream), stream, torch)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
@@ -237,11 +253,58 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
                    "pct_of_peak": round(100 * tflops / peak, 2)},
         "roofline": roofline(flops, batch * (sq + 2 * sk) * hd * 2 + batch * sq * hd * (4 if out_t == "f32" else 2),
                              ms * 1e-3, peak, stored_traffic(args.workload, kernel)),
+        "launch_times": lt,
+        "peak_derived": peak_derived(dmu, in_t),
         "cpu_baseline": None if args.no_cpu_baseline else
         attention_cpu_baseline(batch, sq, sk, hd, Q, K, V, in_t, out_t, scale),
     }
     print(json.dumps(result), flush=True)
     return 0
+
+
+def launch_times(launch, stream, torch, n_warm: int = 50, n_cold: int = 20, rewarm: int = 300) -> dict:
+    """Medians of individually timed launches: warm (back to back), and cold (a 1 GiB buffer
+    written on the same stream before each launch, which evicts the inputs from the L2 caches
+    and the 256 MB last-level cache).  Run before the timed region, then warmed up again, so
+    that the timed launches stay the last ones a trace records."""
+    def per_launch(n, flush=None):
+        evs = []
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        return ts[len(ts) // 2]
+
+    warm = per_launch(n_warm)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    cold = per_launch(n_cold, flush)
+    del flush
+    for _ in range(rewarm):
+        launch()
+    torch.cuda.synchronize()
+    return {"warm_median_us": round(warm, 2), "warm_launches": n_warm, "cold_median_us": round(cold, 2),
+            "cold_launches": n_cold, "cold_flush": "1 GiB written before each launch"}
+
+
+# Dense multiply-accumulate rate per compute unit and clock of the matrix cores, in flops
+# (16 x 16 x 32 bf16/fp16: 8192 multiply-adds per 16 cycles on each of 4 SIMDs; 8-bit
+# inputs twice that).
+FLOP_PER_CLOCK_PER_CU = {"bf16": 4096, "f16": 4096, "i8": 8192, "e4m3": 8192}
+
+
+def peak_derived(dmu, dtype: str) -> dict:
+    """The dense peak re-derived on this machine: compute units x peak clock x flops per clock."""
+    cus, khz = dmu.dmu_device_info(0)
+    per = FLOP_PER_CLOCK_PER_CU[dtype]
+    return {"tflops": round(cus * khz * 1e3 * per / 1e12, 1), "compute_units": cus,
+            "max_sclk_mhz": round(khz / 1e3), "flop_per_clock_per_cu": per,
+            "source": "dmu_device_info (HIP device attributes)"}
 
 
 def copy_calibration(args, torch):
@@ -328,6 +391,7 @@ def main() -> int:
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
+    lt = launch_times(launch, stream, torch)
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -364,6 +428,8 @@ def main() -> int:
                    "in_type": p.in_type, "acc_type": p.acc_type, "out_type": p.out_type,
                    "kernel": kernel, "pct_of_peak": round(100 * tflops / peak, 2)},
         "roofline": roofline(flops, algorithmic_bytes(p, ep_bytes), ms * 1e-3, peak, traffic),
+        "launch_times": lt,
+        "peak_derived": peak_derived(dmu, p.in_type),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p)

@@ -3,8 +3,8 @@
 Argument marshalling only: every step of the product runs in the library's HIP
 kernels.  The functions keep the C names (``dmu_gemm``, ``dmu_gemm_check``,
 ``dmu_gemm_ex``, ``dmu_gemm_ex_check``, ``dmu_attention``, ``dmu_attention_check``,
-``dmu_gemm_kernel_name``,
-``dmu_status_string``, ``dmu_last_error``, ``dmu_probe``, ``dmu_probe_info``);
+``dmu_gemm_streamk``, ``dmu_gemm_streamk_workspace_size``, ``dmu_gemm_kernel_name``,
+``dmu_device_info``, ``dmu_status_string``, ``dmu_last_error``, ``dmu_probe``, ``dmu_probe_info``);
 ``gemm_args`` and ``epilogue_args`` fill the argument structs from torch tensors
 (or raw integer device addresses).  PyTorch supplies device
 memory and streams only.
@@ -121,6 +121,8 @@ def _load():
     lib.dmu_gemm_streamk_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.dmu_gemm_streamk_workspace_size.restype = i32
     lib.dmu_gemm_kernel_name.argtypes, lib.dmu_gemm_kernel_name.restype = [P], ctypes.c_char_p
+    lib.dmu_device_info.argtypes = [i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    lib.dmu_device_info.restype = i32
     lib.dmu_status_string.argtypes, lib.dmu_status_string.restype = [i32], ctypes.c_char_p
     lib.dmu_last_error.argtypes, lib.dmu_last_error.restype = [], ctypes.c_char_p
     lib.dmu_probe.argtypes, lib.dmu_probe.restype = [i32, vp, vp, vp, vp], i32
@@ -252,6 +254,15 @@ def dmu_gemm_check(args: dmu_gemm_args) -> int:
 def dmu_gemm_kernel_name(args: dmu_gemm_args) -> str | None:
     r = _load().dmu_gemm_kernel_name(ctypes.byref(args))
     return None if r is None else r.decode()
+
+
+def dmu_device_info(device: int = 0):
+    """(compute units, peak shader clock in kHz) of a HIP device; raises DmuError on failure."""
+    cu, khz = ctypes.c_int(), ctypes.c_int()
+    st = _load().dmu_device_info(device, ctypes.byref(cu), ctypes.byref(khz))
+    if st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return cu.value, khz.value
 
 
 def dmu_status_string(status: int) -> str:

@@ -609,6 +609,26 @@ extern "C" int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *e
     return DMU_OK;
 }
 
+extern "C" int dmu_device_info(int device, int *compute_units, int *max_clock_khz)
+{
+    clear_error();
+    if (!compute_units || !max_clock_khz || device < 0) {
+        set_error("dmu_device_info: NULL output or negative device");
+        return DMU_ERR_INVALID_ARG;
+    }
+    int cu = 0, khz = 0;
+    hipError_t e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, device);
+    if (e != hipSuccess) {
+        set_error("dmu_device_info: %s", hipGetErrorString(e));
+        return DMU_ERR_HIP;
+    }
+    *compute_units = cu;
+    *max_clock_khz = khz;
+    return DMU_OK;
+}
+
 extern "C" const char *dmu_status_string(int status)
 {
     switch (status) {

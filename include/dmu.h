@@ -281,6 +281,17 @@ int dmu_attention_check(const dmu_attention_args *args);
  */
 const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
 
+/*
+ * Compute units and peak shader clock (kHz) of HIP device `device`, as the
+ * runtime reports them -- the inputs of a dense peak derived on the machine
+ * itself (compute units x clock x multiply-adds per clock and unit).  Both
+ * outputs are host pointers owned by the caller.  Returns DMU_OK;
+ * DMU_ERR_INVALID_ARG for a NULL output or a negative device (message in
+ * dmu_last_error()); DMU_ERR_HIP when the runtime cannot answer (no such
+ * device).  Initialises the HIP runtime; launches nothing.
+ */
+int dmu_device_info(int device, int *compute_units, int *max_clock_khz);
+
 /* Static description of a return code. */
 const char *dmu_status_string(int status);
 

@@ -27,6 +27,16 @@ def test_exports_every_declared_function():
     assert not missing, missing
 
 
+def test_device_info_argument_errors():
+    """NULL outputs and negative devices are rejected before any HIP call."""
+    lib = dmu.library()
+    c = ctypes.c_int()
+    assert lib.dmu_device_info(0, None, ctypes.byref(c)) == dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_device_info(0, ctypes.byref(c), None) == dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_device_info(-1, ctypes.byref(c), ctypes.byref(c)) == dmu.DMU_ERR_INVALID_ARG
+    assert "negative device" in dmu.dmu_last_error()
+
+
 def test_struct_layout_matches_header():
     # 4 int64 + 5 int32 (+4 pad) + 4 x (pointer + 2 int64)
     assert ctypes.sizeof(dmu.dmu_gemm_args) == 32 + 24 + 4 * 24

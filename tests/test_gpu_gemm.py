@@ -282,3 +282,13 @@ def test_dword_aligned_rows_masked_k_tail(cfg, K, pad):
     assert "_kd_" in name, name
     gu.assert_close(got, gu.run_oracle(p), p, where=gu.valid_mask(p))
     gu.assert_bits_equal(got, gu.run_dmu(p, force="generic"), where=gu.valid_mask(p))
+
+
+def test_device_info_matches_the_runtime():
+    """The compute units and peak clock the bench derives its on-machine peak from."""
+    import dense_matrix_unit_tiled_amd as dmu
+
+    torch = gu._torch()
+    cus, khz = dmu.dmu_device_info(0)
+    assert cus == torch.cuda.get_device_properties(0).multi_processor_count
+    assert 500_000 <= khz <= 5_000_000
