@@ -276,8 +276,14 @@ int dmu_attention_check(const dmu_attention_args *args);
 
 /*
  * Name of the kernel variant dmu_gemm would launch for `args` (a static
- * string, e.g. "mfma_256x256_nn_bf16"), or NULL if the arguments are invalid
- * or the call would launch nothing.  Host-only; no GPU access.
+ * string: "mfma_<tile>_<A mode>_<B mode>_<in>_<out>", e.g.
+ * "mfma_256x256_k16_t16_bf16_bf16" -- 256 x 256 tiles, A K-contiguous with
+ * 16-byte rows, B M/N-contiguous 16-bit -- or "mfma_generic64_any_any_f16_f32"
+ * for the fallback), or NULL if the arguments are invalid or the call would
+ * launch nothing.  The tile is 256 x 128 when N <= 128 < M; otherwise, when
+ * 240 or more 256 x 256 tiles cover the problem, 256 x 256 if K spans more
+ * than two 128-byte K-tiles and 256 x 128 if it spans at most two; 128 x 128
+ * for smaller problems; e4m3 never takes 256 x 256.  Host-only; no GPU access.
  */
 const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
 
