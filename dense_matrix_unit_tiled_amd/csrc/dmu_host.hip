@@ -269,6 +269,7 @@ int validate(const dmu_gemm_args *a, Plan *plan)
     plan->cfg.tile = tile;
     plan->cfg.amode = amode < 0 ? 0 : amode;
     plan->cfg.bmode = bmode < 0 ? 0 : bmode;
+    plan->cfg.workers = 0;
     plan->name = kernel_names().at[tile][plan->cfg.amode][plan->cfg.bmode][combo];
     GemmParams &p = plan->p;
     p.A = static_cast<const char *>(a->A);
@@ -378,6 +379,64 @@ void sk_retile(Plan *plan, const dmu_gemm_args *a)
     plan->name = kernel_names().at[plan->cfg.tile][plan->cfg.amode][plan->cfg.bmode][plan->combo];
 }
 
+// Compute units of the current device, asked once per device.
+int device_cus(const char *who, int *out)
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        set_error("%s: no current HIP device", who);
+        return DMU_ERR_HIP;
+    }
+    if (__atomic_load_n(&cus[dev], __ATOMIC_RELAXED) == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            set_error("%s: cannot read the compute-unit count", who);
+            return DMU_ERR_HIP;
+        }
+        __atomic_store_n(&cus[dev], n, __ATOMIC_RELAXED);
+    }
+    *out = __atomic_load_n(&cus[dev], __ATOMIC_RELAXED);
+    return DMU_OK;
+}
+
+// The persistent form of the tiled kernel (gemm_persist: one workgroup per
+// compute unit loops over the tiles and loads the next tile's first K-tile
+// before the current tile's epilogue) replaces the one-workgroup-per-tile
+// launch for short K loops (at most four K-tiles) with at least four tiles per
+// compute unit, where the per-tile start-up and the launch of each workgroup
+// weigh most (measured on the 256-unit chip, same box: batch 32 x 4096 x 4096
+// x 128 fp16 -> fp32, 64 tiles of two K-tiles per unit, 405.8 -> 379.6 us;
+// long loops lose a little: 8192^3 int8, 4 tiles of 64 K-tiles per unit,
+// 425.7 -> 428.2 us; 8192^3 e4m3, 8 per unit, 435.9 -> 440.4 us).
+// DMU_PERSIST=always or never overrides the choice (tests and sweeps).
+constexpr int64_t PERSIST_MIN_TILES_PER_CU = 4, PERSIST_MAX_KTILES = 4;
+
+int persist_layout(Plan *plan, const dmu_gemm_args *a)
+{
+    plan->cfg.workers = 0;
+    if (!plan->launch || plan->cfg.tile == TILE_GENERIC || a->K == 0)
+        return DMU_OK;
+    const char *mode = getenv("DMU_PERSIST");
+    if (mode && strcmp(mode, "never") == 0)
+        return DMU_OK;
+    int cus = 0;
+    const int rc = device_cus("dmu_gemm", &cus);
+    if (rc != DMU_OK)
+        return rc;
+    const int64_t tiles = plan->p.total_tiles, nk = (a->K * elem_bytes(a->in_type) + 127) / 128;
+    const bool always = mode && strcmp(mode, "always") == 0;
+    if (!always && (tiles < PERSIST_MIN_TILES_PER_CU * cus || nk > PERSIST_MAX_KTILES))
+        return DMU_OK;
+    // one workgroup per compute unit, a multiple of the 8 XCDs so that each
+    // worker's tiles stay on its XCD; never more workers than tiles
+    int64_t w = cus >= 8 ? (cus / 8) * 8 : cus;
+    if (w > tiles)
+        w = tiles;
+    plan->cfg.workers = (int)w;
+    return DMU_OK;
+}
+
 // Stream-K pays when the data-parallel tiles leave compute units idle: it is
 // chosen when those tiles fill less than 80 % of their waves (measured on the
 // 256-unit chip: 1024 x 1024 x 16384 bf16, 64 tiles, 123 -> 50 us; the
@@ -397,21 +456,11 @@ int sk_layout(Plan *plan, const dmu_gemm_args *a, SkLayout *sk)
     const int64_t nk = (a->K * elem_bytes(a->in_type) + 127) / 128;
     if (nk == 0)
         return DMU_OK; // K == 0: D = C, data-parallel
-    static int cus[64] = {0}; // compute units per device, asked once
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-        set_error("dmu_gemm_streamk: no current HIP device");
-        return DMU_ERR_HIP;
-    }
-    if (__atomic_load_n(&cus[dev], __ATOMIC_RELAXED) == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-            set_error("dmu_gemm_streamk: cannot read the compute-unit count");
-            return DMU_ERR_HIP;
-        }
-        __atomic_store_n(&cus[dev], n, __ATOMIC_RELAXED);
-    }
-    const uint64_t n = (uint64_t)__atomic_load_n(&cus[dev], __ATOMIC_RELAXED);
+    int cu_count = 0;
+    const int crc = device_cus("dmu_gemm_streamk", &cu_count);
+    if (crc != DMU_OK)
+        return crc;
+    const uint64_t n = (uint64_t)cu_count;
     if (!(mode && strcmp(mode, "always") == 0)) {
         const uint64_t tiles = plan->p.total_tiles, waves = (tiles + n - 1) / n;
         if ((double)tiles >= SK_MIN_IDLE_FILL * (double)(waves * n))
@@ -534,6 +583,8 @@ extern "C" int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, vo
         rc = validate_epilogue(args, ep, &plan);
     if (rc != DMU_OK || !plan.launch)
         return rc;
+    if ((rc = persist_layout(&plan, args)) != DMU_OK)
+        return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e = launch_plan(plan, s);
     if (e != hipSuccess) {
@@ -580,6 +631,8 @@ extern "C" int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *e
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (sk.workers == 0) { // the fallback kernel, or K == 0: the data-parallel launch
+        if ((rc = persist_layout(&plan, args)) != DMU_OK)
+            return rc;
         e = launch_plan(plan, s);
     } else {
         if (!workspace || ((uintptr_t)workspace % 256) || workspace_bytes < sk.bytes) {

@@ -25,9 +25,10 @@ enum TileCfg {
 };
 
 struct LaunchCfg {
-    int tile;  // TileCfg
-    int amode; // Mode of A (ignored for TILE_GENERIC)
-    int bmode; // Mode of B
+    int tile;    // TileCfg
+    int amode;   // Mode of A (ignored for TILE_GENERIC)
+    int bmode;   // Mode of B
+    int workers; // > 0: the persistent form of the tiled kernel on this many workgroups
 };
 
 inline int tile_bm(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_128x128 ? 128 : 256); }

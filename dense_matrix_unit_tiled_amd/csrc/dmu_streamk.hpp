@@ -84,7 +84,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         const TileCoord tc = tile_coord(p, t);
         uint32_t tid_m = threadIdx.x;
         asm volatile("" : "+v"(tid_m));
-        G::mainloop(p, tc, kb, ke, smem, acc, tid_m);
+        typename G::Staging st;
+        G::mainloop(p, tc, kb, ke, smem, acc, tid_m, st);
         uint32_t tid_e = threadIdx.x; // the lane arithmetic of what follows, afresh
         asm volatile("" : "+v"(tid_e));
         const uint32_t lane = tid_e & 63u, wave = __builtin_amdgcn_readfirstlane(tid_e >> 6);

@@ -489,12 +489,54 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     static_assert(NW * PARK <= 2 * STAGE, "parking area fits in the stages");
     static constexpr uint32_t PARTIAL_BYTES = NW * MN * 1024; // one tile's accumulators
 
-    // acc += the product of tile tc over K-tiles [kb, ke) (kb < ke).  smem holds
-    // two stages; K-tile kt uses stage kt mod 2.  tid is threadIdx.x (a caller
-    // that loops over tiles passes an opaque copy, so that the lane arithmetic
-    // is not hoisted out of its loop and kept in registers).
+    // Staging registers, owned by the caller so that the persistent kernel can
+    // load the next tile's first K-tile before the current tile's epilogue.
+    struct Staging {
+        u32x4 sa[PD][NA];
+        u32x4 sb[PD][NB];
+    };
+    // Load K-tile kb of tile tc into staging set 0 (what the main loop's
+    // prologue would load first).
+    static __device__ __forceinline__ void prefetch(const GemmParams &p, const TileCoord tc, int kb, Staging &st,
+                                                    uint32_t tid)
+    {
+        const uint32_t lane = tid & 63u;
+        const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+        const char *Ab = p.A + (int64_t)tc.b * p.stride_a * E;
+        const char *Bb = p.B + (int64_t)tc.b * p.stride_b * E;
+        const int64_t a_start = AMODE != MC16 ? m0 * p.lda * E : m0 * E;
+        const int64_t b_start = BMODE != MC16 ? n0 * p.ldb * E : n0 * E;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)((p.a_bytes - a_start + 3) & ~3ll));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)((p.b_bytes - b_start + 3) & ~3ll));
+        ATile ta;
+        BTile tb;
+        if constexpr (AMODE == MC16)
+            ta.init(p.lda * E, p.M - m0, wave, lane);
+        else
+            ta.init(p.lda * E, wave, lane);
+        if constexpr (BMODE == MC16)
+            tb.init(p.ldb * E, p.N - n0, wave, lane);
+        else
+            tb.init(p.ldb * E, wave, lane);
+        const uint32_t k_bytes = (uint32_t)p.K * E;
+#pragma unroll
+        for (int c = 0; c < NA; ++c)
+            st.sa[0][c] = ta.load(c, ra, kb, k_bytes);
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+            st.sb[0][c] = tb.load(c, rb, kb, k_bytes);
+    }
+
+    // acc += the product of tile tc over K-tiles [kb, ke) (kb < ke), with the
+    // caller's staging registers st (PRE: K-tile kb is already in set 0, loaded
+    // by prefetch).  smem holds two stages; K-tile kt uses stage kt mod 2.
+    // tid is threadIdx.x (a caller that loops over tiles passes an opaque copy,
+    // so that the lane arithmetic is not hoisted out of its loop and kept in
+    // registers).
+    template <bool PRE = false>
     static __device__ __forceinline__ void mainloop(const GemmParams &p, const TileCoord tc, int kb, int ke,
-                                                    char *smem, acc_t (&acc)[MT][NT], uint32_t tid)
+                                                    char *smem, acc_t (&acc)[MT][NT], uint32_t tid, Staging &st)
     {
     const uint32_t lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -523,7 +565,8 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     const uint32_t k_bytes = (uint32_t)p.K * E;
 
     // K-tiles between their global loads and their LDS writes, PD sets
-    u32x4 sa[PD][NA], sb[PD][NB];
+    auto &sa = st.sa;
+    auto &sb = st.sb;
     auto load_one = [&](int c, int kt, int set = 0) {
         if (c < NA)
             sa[set][c] = ta.load(c, ra, kt, k_bytes);
@@ -562,9 +605,11 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     {
         // with two staging sets the stages alternate from stage 0 at kb
         char *first = PD == 2 ? smem : smem + (kb & 1) * STAGE;
+        if constexpr (!PRE) {
 #pragma unroll
-        for (int c = 0; c < NLD; ++c)
-            load_one(c, kb);
+            for (int c = 0; c < NLD; ++c)
+                load_one(c, kb);
+        }
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
             store_one(c, first, kb);
@@ -779,8 +824,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         for (int j = 0; j < G::NT; ++j)
             acc[i][j] = typename G::acc_t{};
     const int nk = (int)(((int64_t)p.K * G::E + 127) / 128);
-    if (nk > 0)
-        G::mainloop(p, tile_of(p, blockIdx.x), 0, nk, smem, acc, threadIdx.x);
+    if (nk > 0) {
+        typename G::Staging st;
+        G::mainloop(p, tile_of(p, blockIdx.x), 0, nk, smem, acc, threadIdx.x, st);
+    }
     // The tile coordinates and lane are derived afresh from opaque copies of
     // the ids, so that the compiler does not keep the values of the prologue
     // alive (in registers the loop needs) across the K loop.
@@ -788,6 +835,50 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     asm volatile("" : "+s"(wg2));
     asm volatile("" : "+v"(tid2));
     G::epilogue(p, tile_of(p, wg2), acc, smem, tid2 & 63u, __builtin_amdgcn_readfirstlane(tid2 >> 6));
+}
+
+
+// The persistent form of the tiled kernel ("Tensor Cores, CUTLASS and CuTe"
+// section 6.5: a fixed number of blocks looping over the output tiles): W
+// workgroups, one per compute unit, take the tiles of the one-per-tile launch
+// in turn (virtual workgroup ids w, w + W, ..., which keep each worker on its
+// XCD when W is a multiple of 8).  Before a tile's epilogue, the worker loads
+// the first K-tile of its next tile into the staging registers, so that those
+// loads are in flight while D is written, and no workgroup launch separates
+// the tiles.  Same main loop and epilogue: bit-identical to gemm_tiled.
+template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+    __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_persist(GemmParams p)
+{
+    typedef Tiled<T, O, BM, BN, WGM, WGN, AMODE, BMODE> G;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+    typename G::Staging st;
+    const uint32_t W = gridDim.x, total = p.total_tiles;
+    const int nk = (int)(((int64_t)p.K * G::E + 127) / 128);
+    uint32_t t = blockIdx.x;
+    if (t >= total)
+        return; // more workers than tiles (uniform: before any barrier)
+    if (nk > 0)
+        G::prefetch(p, tile_of(p, t), 0, st, threadIdx.x);
+    for (; t < total; t += W) {
+        typename G::acc_t acc[G::MT][G::NT];
+#pragma unroll
+        for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+            for (int j = 0; j < G::NT; ++j)
+                acc[i][j] = typename G::acc_t{};
+        uint32_t tid_m = threadIdx.x;
+        asm volatile("" : "+v"(tid_m));
+        if (nk > 0)
+            G::template mainloop<true>(p, tile_of(p, t), 0, nk, smem, acc, tid_m, st);
+        uint32_t tid_e = threadIdx.x, t2 = t;
+        asm volatile("" : "+v"(tid_e));
+        asm volatile("" : "+s"(t2));
+        if (nk > 0 && t2 + W < total)
+            G::prefetch(p, tile_of(p, t2 + W), 0, st, tid_e);
+        G::epilogue(p, tile_of(p, t2), acc, smem, tid_e & 63u, __builtin_amdgcn_readfirstlane(tid_e >> 6));
+        __syncthreads(); // every wavefront is done with its park before the next tile's stages
+    }
 }
 
 } // namespace dmu

@@ -292,3 +292,30 @@ def test_device_info_matches_the_runtime():
     cus, khz = dmu.dmu_device_info(0)
     assert cus == torch.cuda.get_device_properties(0).multi_processor_count
     assert 500_000 <= khz <= 5_000_000
+
+
+# more tiles than one workgroup per compute unit, so that workers loop over several tiles
+PERSIST_CASES = [
+    ("c2", "128x128", dict(M=2000, N=4100, K=72)),            # 16 x 33 tiles, ragged edges
+    ("c2", "256x256", dict(M=2000, N=8200, K=72)),            # 8 x 33 tiles
+    ("c5", "256x128", dict(M=2000, N=4100, K=128)),           # int8, 8 x 33 tiles
+    ("c3", None, dict(M=2000, N=4100, K=130)),                # rows 4-byte aligned, K tail
+    ("c4s", None, dict(M=300, N=260, K=128, batch=40)),       # 3 x 3 tiles x 40 batches
+    ("c1", "128x128", dict(M=2000, N=4000, K=64)),            # with C
+]
+
+
+@pytest.mark.parametrize("cfg,kernel,shape", PERSIST_CASES, ids=[f"{c}-{k}" for c, k, _ in PERSIST_CASES])
+def test_persistent_form_matches(cfg, kernel, shape, monkeypatch):
+    """The persistent form (a fixed set of workgroups looping over the tiles, the next tile's first
+    K-tile loaded before the current tile's epilogue), forced on problems with more tiles than
+    workers, ragged edges and batches: against the oracle, and bit-identical to the
+    one-workgroup-per-tile launch."""
+    p = workloads.make(cfg, "random", 5, **shape)
+    monkeypatch.setenv("DMU_PERSIST", "never")
+    ref = gu.run_dmu(p, force=kernel)
+    monkeypatch.setenv("DMU_PERSIST", "always")
+    got = gu.run_dmu(p, force=kernel)
+    assert np.array_equal(got, ref)
+    want = gu.run_oracle(p)
+    gu.assert_close(got, want, p, where=gu.valid_mask(p))
