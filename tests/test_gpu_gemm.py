@@ -319,3 +319,25 @@ def test_persistent_form_matches(cfg, kernel, shape, monkeypatch):
     assert np.array_equal(got, ref)
     want = gu.run_oracle(p)
     gu.assert_close(got, want, p, where=gu.valid_mask(p))
+
+
+# long K loops under the forced persistent form (the default keeps it for four K-tiles or fewer)
+PERSIST_LONG_K = [
+    ("c2", "256x256", dict(M=2000, N=8200, K=1000)),          # bf16, 8 x 33 tiles, 16 K-tiles, K tail
+    ("c6", "256x128", dict(M=2000, N=4200, K=1024)),          # e4m3, 8 x 33 tiles, 8 K-tiles
+    ("c5", "256x256", dict(M=2100, N=8200, K=640)),           # int8, 9 x 33 tiles, 5 K-tiles
+]
+
+
+@pytest.mark.parametrize("cfg,kernel,shape", PERSIST_LONG_K, ids=[f"{c}-{k}" for c, k, _ in PERSIST_LONG_K])
+def test_persistent_form_long_k(cfg, kernel, shape, monkeypatch):
+    """The persistent form forced on K loops longer than its default's limit: bit-identical to the
+    one-workgroup-per-tile launch, and on sampled outputs against the oracle."""
+    p = workloads.make(cfg, "random", 7, **shape)
+    monkeypatch.setenv("DMU_PERSIST", "never")
+    ref = gu.run_dmu(p, force=kernel)
+    monkeypatch.setenv("DMU_PERSIST", "always")
+    got = gu.run_dmu(p, force=kernel)
+    assert np.array_equal(got, ref)
+    bij = gu.sample_bij(p, n=256, seed=3)
+    gu.assert_close(got[gu.flat_index(p, bij)], gu.oracle_at(p, bij), p)
