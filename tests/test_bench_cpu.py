@@ -1,4 +1,6 @@
 """bench.py's host logic (CPU only): the roofline bound of each workload and the one-GPU rule."""
+import json
+import os
 import subprocess
 import sys
 from types import SimpleNamespace
@@ -34,3 +36,20 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
                        cwd=bench.ROOT, timeout=60)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("cfg", sorted(bench.WORKLOAD_NAMES))
+def test_committed_traffic_matches_current_kernels(cfg):
+    """A stored HBM-traffic reading describes the device code it was taken on: every committed
+    counter record carries the digest of the current kernel sources (a kernel change without
+    new counter runs fails here), and its text summary names the same digest and kernel."""
+    base = os.path.join(bench.ROOT, "profiles", f"traffic_{bench.WORKLOAD_NAMES[cfg]}")
+    if not os.path.exists(base + ".json"):
+        pytest.skip(f"no counter record for {cfg}")
+    rec = json.load(open(base + ".json"))
+    assert rec["source_digest"] == bench.source_digest(cfg)
+    assert rec["traffic_bytes_per_launch"] == pytest.approx(
+        rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"], rel=1e-9)
+    text = open(base + ".md").read()
+    assert f"`{rec['source_digest']}`" in text
+    assert bench.stored_traffic(cfg, rec["kernel"]) == rec["traffic_bytes_per_launch"]
