@@ -53,3 +53,21 @@ def test_committed_traffic_matches_current_kernels(cfg):
     text = open(base + ".md").read()
     assert f"`{rec['source_digest']}`" in text
     assert bench.stored_traffic(cfg, rec["kernel"]) == rec["traffic_bytes_per_launch"]
+
+
+@pytest.mark.parametrize("cfg", sorted(set(workloads.FULL) & set(bench.WORKLOAD_NAMES)))
+def test_committed_profiles_name_the_selected_kernel(cfg):
+    """The committed rocprofv3 summaries of a workload describe the kernel that the library's
+    selection picks for its full-size problem today (no GPU needed: device-looking addresses are
+    never dereferenced by the selection)."""
+    import dense_matrix_unit_tiled_amd as dmu
+    M, N, K, b, it, ot, at, la, lb = workloads.FULL[cfg]
+    fake = 1 << 40
+    a = dmu.gemm_args(M, N, K, fake, K if la == "row" else M, fake + (1 << 36), N if lb == "row" else K,
+                      fake + (2 << 36), N, in_type=it, out_type=ot, acc_type=at, layout_a=la, layout_b=lb,
+                      batch=b, stride_a=M * K, stride_b=K * N, stride_d=M * N)
+    kernel = dmu.dmu_gemm_kernel_name(a)
+    name = bench.WORKLOAD_NAMES[cfg]
+    assert os.path.exists(os.path.join(bench.ROOT, "profiles", f"{kernel}_{name}_kernel_trace.md"))
+    rec = json.load(open(os.path.join(bench.ROOT, "profiles", f"traffic_{name}.json")))
+    assert rec["kernel"] == kernel
