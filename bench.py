@@ -16,7 +16,7 @@ and clock.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c6|lk|lksk|c4fa]
                   [--no-cpu-baseline] [--copy-calibration MiB]
-  python bench.py --summarize DIR [--workload W]   (rocprofv3 output -> profiles/)
+  python bench.py --summarize DIR [--workload W] [--bench-line FILE]   (rocprofv3 output -> profiles/)
 """
 from __future__ import annotations
 
@@ -79,15 +79,56 @@ def source_digest(workload: str = "c2") -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None."""
+def stored_record(workload: str, kernel: str):
+    """The committed rocprofv3 counter record of a workload (profiles/traffic_<workload>.json), or
+    None when there is none or it was taken on other device code or another kernel."""
     path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD_NAMES[workload]}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("source_digest") != source_digest(workload) or rec.get("kernel") != kernel:
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None."""
+    rec = stored_record(workload, kernel)
+    return None if rec is None else rec.get("traffic_bytes_per_launch")
+
+
+def stored_counters(workload: str, kernel: str):
+    """The matrix-core and LDS counter figures of the committed record (the same counter runs as
+    the traffic), or None: MFMA busy fraction, LDS bank-conflict cycles and their share of the LDS
+    active cycles, the shader clock over the dispatch, and the record they come from."""
+    rec = stored_record(workload, kernel)
+    if rec is None or "mfma_busy_fraction" not in rec:
+        return None
+    out = {"mfma_busy": round(rec["mfma_busy_fraction"], 4),
+           "lds_bank_conflict_cycles": rec.get("lds_bank_conflict_cycles"),
+           "lds_bank_conflict_frac": None if rec.get("lds_conflict_fraction") is None
+           else round(rec["lds_conflict_fraction"], 5),
+           "sclk_ghz": None if rec.get("gui_active_ghz") is None else round(rec["gui_active_ghz"], 3),
+           "dispatch_us": None if rec.get("counter_dispatch_us") is None else round(rec["counter_dispatch_us"], 2),
+           "source": f"profiles/traffic_{WORKLOAD_NAMES[workload]}.json (rocprofv3 --pmc, "
+                     f"device-code digest {rec['source_digest']})"}
+    return out
+
+
+# The pages' own figures for the 4096^3 bf16 product, on the A100 they were written for: context
+# for the MI355X numbers, not a target ("Tensor Cores, CUTLASS and CuTe", opening section: the
+# BF16 tensor-core and FP32 peaks; section 4.1: the work, the minimum traffic and the time at the
+# tensor-core peak).
+CONTEXT_A100 = {
+    "gpu": "A100 (the page's own machine)",
+    "bf16_tensor_core_peak_tflops": 312.0,
+    "fp32_peak_tflops": 19.5,
+    "gemm_4096_gflop": 137.4,
+    "gemm_4096_min_traffic_mb": 100.7,
+    "gemm_4096_time_at_peak_ms": 0.44,
+    "source": "Tensor Cores, CUTLASS and CuTe: opening section (peaks) and section 4.1 (the 4096^3 "
+              "problem: work, minimum traffic, time at the tensor-core peak)",
+}
 
 
 def profile_commands(workload: str, d: str) -> dict:
@@ -114,17 +155,22 @@ def algorithmic_bytes(p, ep_bytes: int = 0) -> int:
     return (p.batch * (p.M + p.N) * p.K * esz + mn * osz * (2 if p.C is not None else 1) + ep_bytes)
 
 
-def roofline(flops: float, nbytes: float, seconds: float, peak_tflops: float, traffic) -> dict:
+def roofline(flops: float, nbytes: float, seconds: float, peak_tflops: float, traffic, counters=None) -> dict:
     """The bound of the launch by its algorithmic intensity against the chip's ridge: the
-    matrix cores (TFLOP/s against the dtype's dense peak) or HBM (GB/s against 8 TB/s)."""
+    matrix cores (TFLOP/s against the dtype's dense peak) or HBM (GB/s against 8 TB/s), with the
+    committed counter figures of the same kernel (MFMA busy, LDS bank conflicts, clock) when
+    they describe the current device code."""
     ridge = peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
     if flops / nbytes >= ridge:
         a = flops / seconds / 1e12
-        return {"bound": "mfma", "achieved": round(a, 3), "peak": peak_tflops, "unit": "TFLOP/s",
-                "frac": round(a / peak_tflops, 4), "traffic": traffic}
-    a = nbytes / seconds / 1e9
-    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(a / PEAK_HBM_GBS, 4), "traffic": traffic}
+        r = {"bound": "mfma", "achieved": round(a, 3), "peak": peak_tflops, "unit": "TFLOP/s",
+             "frac": round(a / peak_tflops, 4), "traffic": traffic}
+    else:
+        a = nbytes / seconds / 1e9
+        r = {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(a / PEAK_HBM_GBS, 4), "traffic": traffic}
+    r["counters"] = counters
+    return r
 
 
 def kernel_for(workload: str) -> str:
@@ -252,7 +298,8 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
                    "head_dim": hd, "in_type": in_t, "out_type": out_t, "kernel": kernel,
                    "pct_of_peak": round(100 * tflops / peak, 2)},
         "roofline": roofline(flops, batch * (sq + 2 * sk) * hd * 2 + batch * sq * hd * (4 if out_t == "f32" else 2),
-                             ms * 1e-3, peak, stored_traffic(args.workload, kernel)),
+                             ms * 1e-3, peak, stored_traffic(args.workload, kernel),
+                             stored_counters(args.workload, kernel)),
         "launch_times": lt,
         "peak_derived": peak_derived(dmu, in_t),
         "cpu_baseline": None if args.no_cpu_baseline else
@@ -262,11 +309,18 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
     return 0
 
 
-def launch_times(launch, stream, torch, n_warm: int = 50, n_cold: int = 20, rewarm: int = 300) -> dict:
-    """Medians of individually timed launches: warm (back to back), and cold (a 1 GiB buffer
-    written on the same stream before each launch, which evicts the inputs from the L2 caches
-    and the 256 MB last-level cache).  Run before the timed region, then warmed up again, so
-    that the timed launches stay the last ones a trace records."""
+# Back-to-back launches before the individually timed ones, whatever --warmup is: the shader
+# clock settles only after a few hundred launches (about 300 for the 4096^3 product).
+LAUNCH_TIMES_RAMP = 400
+
+
+def launch_times(launch, stream, torch, n_warm: int = 50, n_cold: int = 20, rewarm: int = 300,
+                 ramp: int = LAUNCH_TIMES_RAMP) -> dict:
+    """Medians of individually timed launches: warm (back to back, after `ramp` untimed launches
+    that bring the clock up), and cold (a 1 GiB buffer written on the same stream before each
+    launch, which evicts the inputs from the L2 caches and the 256 MB last-level cache).  Run
+    before the timed region, then warmed up again, so that the timed launches stay the last ones
+    a trace records."""
     def per_launch(n, flush=None):
         evs = []
         for i in range(n):
@@ -281,6 +335,9 @@ def launch_times(launch, stream, torch, n_warm: int = 50, n_cold: int = 20, rewa
         ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
         return ts[len(ts) // 2]
 
+    for _ in range(ramp):
+        launch()
+    torch.cuda.synchronize()
     warm = per_launch(n_warm)
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
     cold = per_launch(n_cold, flush)
@@ -288,8 +345,9 @@ def launch_times(launch, stream, torch, n_warm: int = 50, n_cold: int = 20, rewa
     for _ in range(rewarm):
         launch()
     torch.cuda.synchronize()
-    return {"warm_median_us": round(warm, 2), "warm_launches": n_warm, "cold_median_us": round(cold, 2),
-            "cold_launches": n_cold, "cold_flush": "1 GiB written before each launch"}
+    return {"warm_median_us": round(warm, 2), "warm_launches": n_warm, "ramp_launches": ramp,
+            "cold_median_us": round(cold, 2), "cold_launches": n_cold,
+            "cold_flush": "1 GiB written before each launch"}
 
 
 # Dense multiply-accumulate rate per compute unit and clock of the matrix cores, in flops
@@ -329,15 +387,25 @@ def main() -> int:
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="summarize rocprofv3 output under DIR into profiles/ and exit")
+    ap.add_argument("--bench-line", metavar="FILE", default=None,
+                    help="with --summarize: the output of a plain bench.py run of the workload in the same "
+                         "session, kept beside the summaries")
     args = ap.parse_args()
     if args.summarize:
         from dense_matrix_unit_tiled_amd import profiling
 
         kernel = kernel_for(args.workload)
+        line = None
+        if args.bench_line:
+            rows = [json.loads(x) for x in open(args.bench_line) if x.startswith("{")]
+            line = rows[-1] if rows else None
+            if line is None or line.get("config", {}).get("workload") != WORKLOAD_NAMES[args.workload]:
+                print(f"bench.py: {args.bench_line} holds no bench line of {args.workload}", file=sys.stderr)
+                return 2
         res = profiling.summarize(args.summarize, os.path.join(ROOT, "profiles"), WORKLOAD_NAMES[args.workload],
                                   kernel, source_digest(args.workload),
                                   profile_commands(args.workload, "gpurun_out/prof_" + args.workload),
-                                  timed=200)
+                                  timed=200, bench_line=line)
         print(json.dumps(res))
         return 0
     if args.gpus != 1:
@@ -384,6 +452,7 @@ def main() -> int:
     print(f"# workload {WORKLOAD_NAMES[args.workload]} kernel {kernel}", file=sys.stderr, flush=True)
 
     launch = (lambda: dmu.dmu_gemm(a, stream)) if ep is None else (lambda: dmu.dmu_gemm_ex(a, ep, stream))
+    ws_bytes = 0
     if args.workload in STREAMK_WORKLOADS:
         ws_bytes = dmu.dmu_gemm_streamk_workspace_size(a)
         ws = torch.zeros(max(ws_bytes, 4) // 4 + 1, dtype=torch.int32, device="cuda:0")  # zero-filled once
@@ -404,6 +473,9 @@ def main() -> int:
     print(f"# timed {args.steps} launches: {ms * 1e3:.2f} us each", file=sys.stderr, flush=True)
 
     copy_calibration(args, torch)
+    sk_failed = None
+    if args.workload in STREAMK_WORKLOADS and ws_bytes:
+        sk_failed = dmu.dmu_gemm_streamk_error(ws, stream, check=False)
 
     flops = float(p.flops)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -427,16 +499,22 @@ def main() -> int:
                    "batch": p.batch, "layout_a": p.layout_a, "layout_b": p.layout_b,
                    "in_type": p.in_type, "acc_type": p.acc_type, "out_type": p.out_type,
                    "kernel": kernel, "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": roofline(flops, algorithmic_bytes(p, ep_bytes), ms * 1e-3, peak, traffic),
+        "roofline": roofline(flops, algorithmic_bytes(p, ep_bytes), ms * 1e-3, peak, traffic,
+                             stored_counters(args.workload, kernel)),
         "launch_times": lt,
         "peak_derived": peak_derived(dmu, p.in_type),
     }
+    if sk_failed is not None:
+        result["streamk_wait_failed"] = sk_failed  # a wait that gave up leaves a wrong D (never expected)
+    if args.workload == "c2":
+        result["context_a100"] = dict(CONTEXT_A100, this_run_ms=round(ms, 6),
+                                      this_run_vs_a100_time_at_peak=round(CONTEXT_A100["gemm_4096_time_at_peak_ms"] / ms, 3))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
-    return 0
+    return 1 if sk_failed else 0
 
 
 if __name__ == "__main__":

@@ -31,6 +31,10 @@ import os
 from collections import defaultdict
 
 COPY_MIB = 256
+# A shader clock is derived from GRBM_GUI_ACTIVE only over dispatches at least this long, and only
+# when it does not exceed the chip's peak shader clock.
+MIN_CLOCK_DISPATCH_US = 50.0
+MAX_SCLK_GHZ = 2.4
 
 
 def _rows(pattern: str):
@@ -78,10 +82,16 @@ def is_copy(name: str) -> bool:
 
 
 def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, source_digest: str,
-              commands: dict, timed: int = 200, counted: int = 100) -> dict:
-    """Write profiles/<label>_<workload>_*.md and traffic_<workload>.json; return the figures."""
+              commands: dict, timed: int = 200, counted: int = 100, bench_line: dict | None = None) -> dict:
+    """Write profiles/<label>_<workload>_*.md and traffic_<workload>.json; return the figures.
+    ``bench_line``: the JSON line of a plain bench.py run of the same workload in the same session
+    (same GPU, just before the profiled runs), kept beside the figures it is compared with."""
     os.makedirs(profiles, exist_ok=True)
     result = {"workload": workload_name, "kernel": kernel_label, "source_digest": source_digest}
+    if bench_line is not None:
+        result["bench_same_session"] = {k: bench_line.get(k) for k in ("value", "unit", "ms_per_step", "steps",
+                                                                         "warmup")}
+        result["bench_same_session"]["kernel"] = bench_line.get("config", {}).get("kernel")
 
     # kernel trace statistics
     stats = _rows(os.path.join(d, "trace", "**", "*kernel_stats.csv"))
@@ -105,6 +115,11 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
             result["avg_us"] = avg
             lines += ["", f"Library-kernel dispatches timed by the benchmark (the last {n}, after the warm-up that "
                           f"raises the clock): average {avg:.2f} us."]
+            if bench_line is not None:
+                lines += ["", f"A plain `python3 bench.py --workload ...` run in the same session, just before: "
+                              f"{bench_line['ms_per_step'] * 1e3:.2f} us per step (HIP events over "
+                              f"{bench_line['steps']} back-to-back launches, after {bench_line['warmup']} "
+                              f"warm-up launches), {bench_line['value']} {bench_line['unit']}."]
         open(os.path.join(profiles, f"{kernel_label}_{workload_name}_kernel_trace.md"), "w").write(
             "\n".join(lines) + "\n")
 
@@ -162,14 +177,25 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
             result["mfma_busy_fraction"] = util
             dur, _ = _timed_average_us([r for r in sq_rows if r["Counter_Name"] == "GRBM_GUI_ACTIVE"], counted)
             if dur:
+                result["counter_dispatch_us"] = dur
                 clk = grbm / 8 / (dur * 1e-6) / 1e9
-                md += [f"Dispatch duration under counter collection {dur:.2f} us; GUI_ACTIVE / 8 / duration = "
-                       f"{clk:.2f} GHz (GUI_ACTIVE cycles per second of dispatch; the busy fraction above uses "
-                       f"the same cycles)."]
-                result["gui_active_ghz"] = clk
+                if dur >= MIN_CLOCK_DISPATCH_US and clk <= MAX_SCLK_GHZ:
+                    md += [f"Dispatch duration under counter collection {dur:.2f} us; GUI_ACTIVE / 8 / duration = "
+                           f"{clk:.2f} GHz (GUI_ACTIVE cycles per second of dispatch; the busy fraction above "
+                           f"uses the same cycles)."]
+                    result["gui_active_ghz"] = clk
+                else:
+                    # GUI_ACTIVE also counts the cycles the command processor spends setting up and
+                    # draining the dispatch, outside the dispatch's own start and end timestamps;
+                    # over a dispatch of a few microseconds they dominate, and the quotient is no clock
+                    md += [f"Dispatch duration under counter collection {dur:.2f} us: too short for a clock "
+                           f"from GUI_ACTIVE / 8 / duration ({clk:.2f} GHz would exceed the "
+                           f"{MAX_SCLK_GHZ} GHz peak or rest on set-up and drain cycles outside the "
+                           f"dispatch); no clock is reported, and the busy fraction above is a lower bound."]
         if conflict is not None and active:
             md += [f"LDS bank-conflict cycles / LDS active cycles = {conflict / active:.3f}."]
             result["lds_conflict_fraction"] = conflict / active
+            result["lds_bank_conflict_cycles"] = conflict
         open(os.path.join(profiles, f"{kernel_label}_{workload_name}_counters.md"), "w").write("\n".join(md) + "\n")
     if "traffic_bytes_per_launch" in result:
         json.dump(result, open(os.path.join(profiles, f"traffic_{workload_name}.json"), "w"), indent=1)

@@ -71,3 +71,99 @@ def test_committed_profiles_name_the_selected_kernel(cfg):
     assert os.path.exists(os.path.join(bench.ROOT, "profiles", f"{kernel}_{name}_kernel_trace.md"))
     rec = json.load(open(os.path.join(bench.ROOT, "profiles", f"traffic_{name}.json")))
     assert rec["kernel"] == kernel
+
+
+def golden_work():
+    path = os.path.join(bench.ROOT, "tests", "golden", "tensor_cores_4096_work.txt")
+    vals = {}
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def test_4096_work_matches_the_page():
+    """The 4096^3 bf16 problem's flop count, minimum traffic and intensity as the bench computes
+    them agree with the figures "Tensor Cores, CUTLASS and CuTe" prints for it (opening section
+    and section 4.1; rounded there to 137.4 GFLOP, 100.7 MB, 1365 FLOP/B), and the A100 context
+    the bench line carries quotes those same figures."""
+    g = golden_work()
+    p = full("c2")
+    flops = 2.0 * p.M * p.N * p.K
+    nbytes = bench.algorithmic_bytes(p)
+    assert round(flops / 1e9, 1) == g["gflop"]
+    assert round(nbytes / 1e6, 1) == g["min_traffic_mb"]
+    assert round(flops / nbytes) == g["intensity_flop_per_byte"]
+    assert workloads.make("c2", "structured", M=64, N=64, K=64).flops == 2 * 64 ** 3
+    ctx = bench.CONTEXT_A100
+    assert ctx["gemm_4096_gflop"] == g["gflop"] and ctx["gemm_4096_min_traffic_mb"] == g["min_traffic_mb"]
+    assert (ctx["bf16_tensor_core_peak_tflops"], ctx["fp32_peak_tflops"]) == (312.0, 19.5)
+    # the page's 0.44 ms is its work at its tensor-core peak
+    assert round(ctx["gemm_4096_gflop"] / ctx["bf16_tensor_core_peak_tflops"], 2) == ctx["gemm_4096_time_at_peak_ms"]
+
+
+def test_launch_times_ramp_does_not_depend_on_warmup():
+    """The individually timed launches follow their own ramp of at least 300 launches (the clock
+    needs about that many), whatever --warmup the caller passed."""
+    calls = []
+
+    class Ev:
+        def __init__(self, **kw):
+            self.t = 0.0
+
+        def record(self, stream):
+            self.t = float(len(calls))
+
+        def elapsed_time(self, other):
+            return 1e-3
+
+    class FakeTorch:
+        class cuda:
+            Event = Ev
+
+            @staticmethod
+            def synchronize():
+                pass
+
+        float32 = "f32"
+
+        @staticmethod
+        def empty(n, dtype=None, device=None):
+            class Buf:
+                def fill_(self, v):
+                    pass
+            return Buf()
+
+    lt = bench.launch_times(lambda: calls.append(1), None, FakeTorch)
+    assert bench.LAUNCH_TIMES_RAMP >= 300 and lt["ramp_launches"] == bench.LAUNCH_TIMES_RAMP
+    assert len(calls) == bench.LAUNCH_TIMES_RAMP + lt["warm_launches"] + lt["cold_launches"] + 300
+
+
+def test_roofline_carries_the_counters():
+    r = bench.roofline(1e12, 1e9, 1e-3, 2500.0, 5e8, {"mfma_busy": 0.7})
+    assert r["counters"] == {"mfma_busy": 0.7} and r["traffic"] == 5e8
+
+
+def test_short_dispatch_gives_no_clock(tmp_path):
+    """GRBM_GUI_ACTIVE over a dispatch of a few microseconds is mostly set-up and drain: no clock
+    is derived from it (the former summary of the 256^3 product read an impossible 4.63 GHz)."""
+    from dense_matrix_unit_tiled_amd import profiling
+
+    sq = tmp_path / "sq" / "x"
+    sq.mkdir(parents=True)
+    rows = []
+    for i, (ctr, val) in enumerate([("SQ_VALU_MFMA_BUSY_CYCLES", 3.277e4), ("GRBM_GUI_ACTIVE", 2.78e5),
+                                    ("SQ_LDS_BANK_CONFLICT", 0.0), ("SQ_LDS_IDX_ACTIVE", 1.6e4)]):
+        rows.append(dict(Dispatch_Id=1, Kernel_Name="void dmu::gemm_tiled<...>", Counter_Name=ctr,
+                         Counter_Value=val, Start_Timestamp=0, End_Timestamp=7510))
+    import csv
+    with open(sq / "run_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+    cmds = {k: "cmd" for k in ("trace", "fetch", "write", "sq")}
+    res = profiling.summarize(str(tmp_path), str(tmp_path / "out"), "w", "k", "d", cmds)
+    assert "gui_active_ghz" not in res and res["counter_dispatch_us"] == pytest.approx(7.51)
+    text = open(tmp_path / "out" / "k_w_counters.md").read()
+    assert "too short for a clock" in text
