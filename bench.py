@@ -196,7 +196,7 @@ def kernel_for(workload: str) -> str:
     name = dmu.dmu_gemm_kernel_name(a)
     if workload in STREAMK_WORKLOADS and "generic" not in name:
         # the stream-K kernel runs 256 x 128 tiles where the data-parallel plan has 256 x 256
-        name = "streamk_" + name.replace("mfma_256x256", "mfma_256x128")
+        name = "streamk_" + name.replace("mfma_256x256w4", "mfma_256x128").replace("mfma_256x256", "mfma_256x128")
     return name
 
 

@@ -3,7 +3,8 @@
 Argument marshalling only: every step of the product runs in the library's HIP
 kernels.  The functions keep the C names (``dmu_gemm``, ``dmu_gemm_check``,
 ``dmu_gemm_ex``, ``dmu_gemm_ex_check``, ``dmu_attention``, ``dmu_attention_check``,
-``dmu_gemm_streamk``, ``dmu_gemm_streamk_workspace_size``, ``dmu_gemm_kernel_name``,
+``dmu_gemm_streamk``, ``dmu_gemm_streamk_workspace_size``, ``dmu_gemm_streamk_error``,
+``dmu_gemm_kernel_name``,
 ``dmu_device_info``, ``dmu_status_string``, ``dmu_last_error``, ``dmu_probe``, ``dmu_probe_info``);
 ``gemm_args`` and ``epilogue_args`` fill the argument structs from torch tensors
 (or raw integer device addresses).  PyTorch supplies device
@@ -14,11 +15,14 @@ there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdmu.so")
+# The library this binding loads: the in-tree build, or another build of the same sources named by
+# the environment variable DMU_LIBRARY (the LDS-poisoning debug build, a build kept for comparison).
+LIB_PATH = os.environ.get("DMU_LIBRARY") or os.path.join(HERE, "libdmu.so")
 
 DMU_F16, DMU_BF16, DMU_F32, DMU_I8, DMU_I32, DMU_E4M3 = 1, 2, 3, 4, 5, 6
 DMU_ROW_MAJOR, DMU_COL_MAJOR = 0, 1
@@ -36,6 +40,7 @@ DMU_PROBE_LDS_READ_TR16 = 11
 DMU_PROBE_LDS_FRAG = 12
 DMU_PROBE_LDS_FRAG_T = 13
 DMU_PROBE_LANE_SWAP = 14
+DMU_PROBE_LDS_READ_TR8 = 15
 DMU_PROBE_CVT_BF16 = 30
 DMU_PROBE_CVT_F16 = 31
 
@@ -97,16 +102,20 @@ _lib = None
 
 def _load():
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with dense_matrix_unit_tiled_amd.build.build()")
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with dense_matrix_unit_tiled_amd.build.build()")
     # PyTorch ships its own HIP runtime.  Importing it first makes the library's
     # libamdhip64 dependency resolve to that already-loaded copy, so the process
     # holds one HIP runtime and torch's device pointers and streams are valid here.
     import torch  # noqa: F401
 
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER(dmu_gemm_args)
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.dmu_gemm.argtypes, lib.dmu_gemm.restype = [P, vp], i32
@@ -120,6 +129,8 @@ def _load():
     lib.dmu_gemm_streamk.argtypes, lib.dmu_gemm_streamk.restype = [P, PE, vp, ctypes.c_size_t, vp], i32
     lib.dmu_gemm_streamk_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.dmu_gemm_streamk_workspace_size.restype = i32
+    lib.dmu_gemm_streamk_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int)]
+    lib.dmu_gemm_streamk_error.restype = i32
     lib.dmu_gemm_kernel_name.argtypes, lib.dmu_gemm_kernel_name.restype = [P], ctypes.c_char_p
     lib.dmu_device_info.argtypes = [i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     lib.dmu_device_info.restype = i32
@@ -128,8 +139,20 @@ def _load():
     lib.dmu_probe.argtypes, lib.dmu_probe.restype = [i32, vp, vp, vp, vp], i32
     ip = ctypes.POINTER(ctypes.c_int)
     lib.dmu_probe_info.argtypes, lib.dmu_probe_info.restype = [i32, ip, ip, ip, ip, ip], i32
-    _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def library_override(path):
+    """Route every call of this binding to another build of the library (for example the
+    LDS-poisoning debug build) for the duration of a ``with`` block."""
+    global _lib
+    saved = _load()
+    _lib = _open(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def library():
@@ -220,6 +243,19 @@ def dmu_gemm_streamk(args: dmu_gemm_args, ep: dmu_epilogue | None, workspace, wo
     if check and st != DMU_OK:
         raise DmuError(st, dmu_last_error())
     return st
+
+
+def dmu_gemm_streamk_error(workspace, stream=None, check: bool = True) -> bool:
+    """Whether a wait inside an earlier dmu_gemm_streamk call on ``workspace`` gave up (that
+    call's D is then wrong, and the workspace must be zero-filled again).  Waits for
+    ``stream``.  With ``check`` a failed wait raises DmuError."""
+    failed = ctypes.c_int(0)
+    st = _load().dmu_gemm_streamk_error(_addr(workspace), _stream(stream), ctypes.byref(failed))
+    if st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    if check and failed.value:
+        raise DmuError(DMU_ERR_HIP, "a stream-K wait ran past its limit: D is wrong; zero-fill the workspace")
+    return bool(failed.value)
 
 
 def attention_args(batch, seq_q, seq_k, head_dim, Q, ldq, K, ldk, V, ldv, O, ldo, *, in_type, out_type, scale,

@@ -1,7 +1,9 @@
 """Build ``libdmu.so`` (the gfx950 GEMM library) in-tree with hipcc.
 
 Every ``csrc/*.hip`` unit is compiled for gfx950 in parallel into ``_build/``
-and linked into ``dense_matrix_unit_tiled_amd/libdmu.so``.
+and linked into ``dense_matrix_unit_tiled_amd/libdmu.so``.  The LDS-poisoning
+debug build of the same sources (``-DDMU_LDS_POISON=1``, see dmu_tiled.hpp) goes
+to ``_build_poison/`` and ``libdmu_poison.so``; only its test loads it.
 """
 from __future__ import annotations
 
@@ -17,6 +19,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libdmu.so")
+POISON_LIB_PATH = os.path.join(HERE, "libdmu_poison.so")
+VARIANTS = {None: (BUILD, LIB_PATH, []),
+            "poison": (os.path.join(ROOT, "_build_poison"), POISON_LIB_PATH, ["-DDMU_LDS_POISON=1"])}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU instructions are disabled for all device code: this library
@@ -50,9 +55,10 @@ def resource_usage(text: str) -> list:
     return out
 
 
-def _compile(src: str) -> tuple:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+def _compile(job) -> tuple:
+    src, build_dir, defines = job
+    obj = os.path.join(build_dir, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *DEVICE_FLAGS, *defines, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -64,21 +70,29 @@ def _compile(src: str) -> tuple:
     return obj, usage
 
 
-def build(jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, variants=(None, "poison")) -> str:
+    """Compile every unit of each variant (the product library, then the debug build) in one
+    pool and link each; returns the product library's path."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = jobs or min(len(srcs), max(1, len(os.sched_getaffinity(0))), 16)
+    work = []
+    for v in variants:
+        build_dir, _, defines = VARIANTS[v]
+        os.makedirs(build_dir, exist_ok=True)
+        work += [(src, build_dir, defines) for src in srcs]
+    jobs = jobs or min(len(work), max(1, len(os.sched_getaffinity(0))), 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, srcs))
-    objs = [o for o, _ in results]
-    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as fh:
-        for _, usage in results:
-            for u in usage:
-                fh.write(" ".join(f"{k}={v}" for k, v in u.items()) + "\n")
-    tmp = LIB_PATH + ".tmp"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
-                   check=True)
-    os.replace(tmp, LIB_PATH)
+        results = list(ex.map(_compile, work))
+    for v in variants:
+        build_dir, lib_path, _ = VARIANTS[v]
+        mine = [r for r, w in zip(results, work) if w[1] == build_dir]
+        with open(os.path.join(build_dir, "resource_usage.txt"), "w") as fh:
+            for _, usage in mine:
+                for u in usage:
+                    fh.write(" ".join(f"{k}={v}" for k, v in u.items()) + "\n")
+        tmp = lib_path + ".tmp"
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in mine]],
+                       check=True)
+        os.replace(tmp, lib_path)
     return LIB_PATH
 
 

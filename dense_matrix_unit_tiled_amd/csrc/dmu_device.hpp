@@ -71,6 +71,21 @@ template <> struct Mfma<BF16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y),
                                                        c, 0, 0, 0);
     }
+    // In place, the accumulator in AGPRs (the four-wavefront tile): c = X Y + c,
+    // and the first K-step's form c = X Y (accumulator operand 0, so no
+    // register write precedes the instruction).  Written as assembly because
+    // the compiler, given the builtin, renames the accumulator tuple between
+    // the instructions and copies it through VGPRs.  Volatile, so that these
+    // keep their order with respect to the wait that guards the accumulator
+    // reads after the K loop.
+    static __device__ __forceinline__ void step_a(u32x4 x, u32x4 y, acc_t &c)
+    {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+    }
+    static __device__ __forceinline__ void step_a0(u32x4 x, u32x4 y, acc_t &c)
+    {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(x), "v"(y));
+    }
 };
 template <> struct Mfma<F16> {
     typedef f32x4 acc_t;
@@ -79,6 +94,15 @@ template <> struct Mfma<F16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
                                                       0, 0, 0);
     }
+    // in place, the accumulator in AGPRs (as for bf16)
+    static __device__ __forceinline__ void step_a(u32x4 x, u32x4 y, acc_t &c)
+    {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+    }
+    static __device__ __forceinline__ void step_a0(u32x4 x, u32x4 y, acc_t &c)
+    {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(c) : "v"(x), "v"(y));
+    }
 };
 template <> struct Mfma<I8> {
     typedef i32x4 acc_t;
@@ -86,6 +110,15 @@ template <> struct Mfma<I8> {
     {
         return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, x), __builtin_bit_cast(i32x4, y), c, 0,
                                                      0, 0);
+    }
+    // in place, the accumulator in AGPRs (as for bf16)
+    static __device__ __forceinline__ void step_a(u32x4 x, u32x4 y, acc_t &c)
+    {
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+    }
+    static __device__ __forceinline__ void step_a0(u32x4 x, u32x4 y, acc_t &c)
+    {
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(c) : "v"(x), "v"(y));
     }
 };
 

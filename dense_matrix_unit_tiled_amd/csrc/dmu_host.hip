@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+
 #include "../../include/dmu.h"
 #include "dmu_host.hpp"
 
@@ -83,7 +84,7 @@ struct NameTable {
 const NameTable &kernel_names()
 {
     static const NameTable table = [] {
-        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64"};
+        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64", "256x256w4"};
         static const char *const MODE_NAMES[] = {"k16", "kd", "t16"};
         NameTable t;
         for (int a = 0; a < NUM_TILE_CFGS; ++a)
@@ -253,10 +254,16 @@ int validate(const dmu_gemm_args *a, Plan *plan)
             tile = nk <= 2 ? TILE_256x128 : TILE_256x256;
         else
             tile = TILE_128x128;
+        // (The four-wavefront 256 x 256 tile, a third fewer LDS fragment bytes
+        // per flop, is not chosen by default: measured in interleaved pairs on
+        // one box, 4096^3 bf16 NN 99.0 us on eight wavefronts against 99.6 us,
+        // 8192^3 int8 TN 424 against 434 us, 5000 x 3000 x 2050 fp16 TN 66
+        // against 72 us.  DMU_FORCE_KERNEL=256x256w4 selects it.)
         if (env && strcmp(env, "256x256") == 0) tile = TILE_256x256;
+        if (env && strcmp(env, "256x256w4") == 0) tile = TILE_256x256W4;
         if (env && strcmp(env, "256x128") == 0) tile = TILE_256x128;
         if (env && strcmp(env, "128x128") == 0) tile = TILE_128x128;
-        if (a->in_type == DMU_E4M3 && tile == TILE_256x256)
+        if (a->in_type == DMU_E4M3 && (tile == TILE_256x256 || tile == TILE_256x256W4))
             tile = TILE_256x128; // e4m3 fragments need the registers of a 64 x 64 wavefront tile
     }
     const int64_t bm = tile_bm(tile), bn = tile_bn(tile);
@@ -354,20 +361,34 @@ int validate_epilogue(const dmu_gemm_args *a, const dmu_epilogue *ep, Plan *plan
     return DMU_OK;
 }
 
-// Stream-K workspace layout: flags (one 32-bit word per worker), the error
-// word, then one BM x BN slot of 32-bit accumulators per worker.
+// Stream-K workspace layout: the error word (first 256 bytes), the flags (one
+// 32-bit word per worker, from byte 256), then one BM x BN slot of 32-bit
+// accumulators per worker (from the next multiple of 256 bytes).
 struct SkLayout {
     uint32_t workers; // 0: the call runs the data-parallel kernel
     uint32_t nk, q, r; // K-tiles per tile; iterations = q workers + r
-    size_t error_off, partials_off, slot_bytes, bytes;
+    size_t flags_off, partials_off, slot_bytes, bytes;
 };
 
 constexpr uint32_t SK_SPIN_LIMIT = 1u << 22; // polls (each after a short sleep), well over a second
 
+// Polls of a flag before a wait gives up: SK_SPIN_LIMIT, or DMU_STREAMK_SPIN_LIMIT
+// (a test hook: a tiny limit makes the waits give up while every kernel still
+// exits normally).
+uint32_t sk_spin_limit()
+{
+    const char *env = getenv("DMU_STREAMK_SPIN_LIMIT");
+    if (!env || !*env)
+        return SK_SPIN_LIMIT;
+    char *end = nullptr;
+    const unsigned long v = strtoul(env, &end, 10);
+    return (end && *end == 0 && v <= SK_SPIN_LIMIT) ? (uint32_t)v : SK_SPIN_LIMIT;
+}
+
 // Stream-K runs the 256 x 128 tile where the data-parallel plan has 256 x 256.
 void sk_retile(Plan *plan, const dmu_gemm_args *a)
 {
-    if (!plan->launch || plan->cfg.tile != TILE_256x256)
+    if (!plan->launch || (plan->cfg.tile != TILE_256x256 && plan->cfg.tile != TILE_256x256W4))
         return;
     const int64_t tm = (a->M + 255) / 256, tn = (a->N + 127) / 128;
     if (tm * tn * a->batch >= ((int64_t)1 << 31))
@@ -415,8 +436,8 @@ constexpr int64_t PERSIST_MIN_TILES_PER_CU = 4, PERSIST_MAX_KTILES = 4;
 int persist_layout(Plan *plan, const dmu_gemm_args *a)
 {
     plan->cfg.workers = 0;
-    if (!plan->launch || plan->cfg.tile == TILE_GENERIC || a->K == 0)
-        return DMU_OK;
+    if (!plan->launch || plan->cfg.tile == TILE_GENERIC || plan->cfg.tile == TILE_256x256W4 || a->K == 0)
+        return DMU_OK; // (the four-wavefront tile has no persistent form)
     const char *mode = getenv("DMU_PERSIST");
     if (mode && strcmp(mode, "never") == 0)
         return DMU_OK;
@@ -468,7 +489,7 @@ int sk_layout(Plan *plan, const dmu_gemm_args *a, SkLayout *sk)
     }
     sk_retile(plan, a);
     const Plan &pl = *plan;
-    if (pl.cfg.tile == TILE_256x256)
+    if (pl.cfg.tile == TILE_256x256 || pl.cfg.tile == TILE_256x256W4)
         return DMU_OK; // too many tiles to retile: data-parallel
     const uint64_t iters = (uint64_t)pl.p.total_tiles * (uint64_t)nk;
     if (iters >= ((uint64_t)1 << 31))
@@ -478,10 +499,25 @@ int sk_layout(Plan *plan, const dmu_gemm_args *a, SkLayout *sk)
     sk->q = (uint32_t)(iters / sk->workers);
     sk->r = (uint32_t)(iters % sk->workers);
     sk->slot_bytes = (size_t)tile_bm(pl.cfg.tile) * tile_bn(pl.cfg.tile) * 4;
-    sk->error_off = ((size_t)sk->workers * 4 + 255) & ~(size_t)255;
-    sk->partials_off = sk->error_off + 256;
+    sk->flags_off = 256;
+    sk->partials_off = (sk->flags_off + (size_t)sk->workers * 4 + 255) & ~(size_t)255;
     sk->bytes = sk->partials_off + (size_t)sk->workers * sk->slot_bytes;
     return DMU_OK;
+}
+
+// The stream-K kernel's view of a workspace laid out as `sk` describes.
+StreamKParams sk_params(const SkLayout &sk, char *w)
+{
+    StreamKParams k;
+    k.error = reinterpret_cast<uint32_t *>(w);
+    k.flags = reinterpret_cast<uint32_t *>(w + sk.flags_off);
+    k.partials = w + sk.partials_off;
+    k.workers = sk.workers;
+    k.nk = sk.nk;
+    k.q = sk.q;
+    k.r = sk.r;
+    k.spin_limit = sk_spin_limit();
+    return k;
 }
 
 hipError_t launch_plan(const Plan &plan, hipStream_t s)
@@ -643,22 +679,37 @@ extern "C" int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *e
             set_error("dmu_gemm_streamk: the workspace overlaps an operand");
             return DMU_ERR_INVALID_ARG;
         }
-        char *w = static_cast<char *>(workspace);
-        StreamKParams k;
-        k.flags = reinterpret_cast<uint32_t *>(w);
-        k.error = reinterpret_cast<uint32_t *>(w + sk.error_off);
-        k.partials = w + sk.partials_off;
-        k.workers = sk.workers;
-        k.nk = sk.nk;
-        k.q = sk.q;
-        k.r = sk.r;
-        k.spin_limit = SK_SPIN_LIMIT;
-        e = launch_plan_sk(plan, k, s);
+        e = launch_plan_sk(plan, sk_params(sk, static_cast<char *>(workspace)), s);
     }
     if (e != hipSuccess) {
         set_error("dmu_gemm_streamk: launch of %s failed: %s", plan.name, hipGetErrorString(e));
         return DMU_ERR_HIP;
     }
+    return DMU_OK;
+}
+
+extern "C" int dmu_gemm_streamk_error(const void *workspace, void *stream, int *failed)
+{
+    clear_error();
+    if (!failed || !workspace) {
+        set_error("dmu_gemm_streamk_error: NULL %s", failed ? "workspace" : "failed");
+        return DMU_ERR_INVALID_ARG;
+    }
+    *failed = 0;
+    if ((uintptr_t)workspace % 256) {
+        set_error("dmu_gemm_streamk_error: workspace is not 256-byte aligned");
+        return DMU_ERR_INVALID_ARG;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        set_error("dmu_gemm_streamk_error: %s", hipGetErrorString(e));
+        return DMU_ERR_HIP;
+    }
+    *failed = word != 0;
     return DMU_OK;
 }
 

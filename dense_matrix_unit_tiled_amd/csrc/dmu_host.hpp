@@ -17,11 +17,12 @@ int check_launch(const char *what);
 // Kernel shapes of the tiled kernel (gemm_tiled, 8 wavefronts) and the
 // fallback (gemm_generic).
 enum TileCfg {
-    TILE_256x256 = 0, // wavefronts 2 x 4, 128 x 64 each
-    TILE_256x128 = 1, // wavefronts 4 x 2, 64 x 64 each
-    TILE_128x128 = 2, // wavefronts 2 x 4, 64 x 32 each
-    TILE_GENERIC = 3, // 64 x 64, element loads
-    NUM_TILE_CFGS = 4
+    TILE_256x256 = 0,   // wavefronts 2 x 4, 128 x 64 each
+    TILE_256x128 = 1,   // wavefronts 4 x 2, 64 x 64 each
+    TILE_128x128 = 2,   // wavefronts 2 x 4, 64 x 32 each
+    TILE_GENERIC = 3,   // 64 x 64, element loads
+    TILE_256x256W4 = 4, // wavefronts 2 x 2, 128 x 128 each, accumulators in AGPRs (16-bit and int8 inputs)
+    NUM_TILE_CFGS = 5
 };
 
 struct LaunchCfg {
@@ -32,7 +33,10 @@ struct LaunchCfg {
 };
 
 inline int tile_bm(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_128x128 ? 128 : 256); }
-inline int tile_bn(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_256x256 ? 256 : 128); }
+inline int tile_bn(int tile)
+{
+    return tile == TILE_GENERIC ? 64 : ((tile == TILE_256x256 || tile == TILE_256x256W4) ? 256 : 128);
+}
 
 // One launcher per (input type, output type); each returns hipSuccess or the
 // launch error.  The grid is p.total_tiles workgroups.

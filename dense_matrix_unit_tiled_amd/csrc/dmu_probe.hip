@@ -123,6 +123,20 @@ __global__ void __launch_bounds__(64) probe_lds_tr16(const char *img, const int3
     out[l * 2 + 1] = w[1];
 }
 
+// ds_read_b64_tr_b8: lane l reads at addr[l] (aligned to 8 bytes, in bounds).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+__global__ void __launch_bounds__(64) probe_lds_tr8(const char *img, const int32_t *addr, uint32_t *out)
+{
+    __shared__ __attribute__((aligned(16))) char lds[4096];
+    const uint32_t l = threadIdx.x;
+    probe_fill_lds(lds, img, l);
+    __syncthreads();
+    const uint32_t off = (uint32_t)addr[l] & (4096u - 8u);
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(lds + off));
+    out[l * 2 + 0] = (uint32_t)v[0];
+    out[l * 2 + 1] = (uint32_t)v[1];
+}
+
 // The tiled kernel's K-contiguous LDS format: a 32-row x 128-byte tile is
 // written with the kernel's staging writes (transfer q, lane l carrying row
 // 8q + l/8, chunk l%8) and read back with its fragment reads for row blocks 0
@@ -203,6 +217,7 @@ extern "C" int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type,
     case DMU_PROBE_MFMA_16x16x128_E4M3: mm = 16, nn = 16, kk = 128, t = DMU_E4M3, r = 4; break;
     case DMU_PROBE_LDS_READ_B128: r = 4; break;
     case DMU_PROBE_LDS_READ_TR16: r = 2; break;
+    case DMU_PROBE_LDS_READ_TR8: r = 2; break;
     case DMU_PROBE_LDS_FRAG: r = 16; break;
     case DMU_PROBE_LDS_FRAG_T: r = 64; break;
     case DMU_PROBE_LANE_SWAP: t = DMU_I32, r = 4; break;
@@ -226,7 +241,7 @@ extern "C" int dmu_probe(int variant, const void *in0, const void *in1, void *ou
     int rc = dmu_probe_info(variant, nullptr, nullptr, nullptr, nullptr, nullptr);
     if (rc != DMU_OK)
         return rc;
-    const bool needs_in1 = variant <= DMU_PROBE_LDS_READ_TR16;
+    const bool needs_in1 = variant <= DMU_PROBE_LDS_READ_TR16 || variant == DMU_PROBE_LDS_READ_TR8;
     if (!in0 || !out || (needs_in1 && !in1)) {
         set_error("dmu_probe: null pointer");
         return DMU_ERR_INVALID_ARG;
@@ -250,6 +265,9 @@ extern "C" int dmu_probe(int variant, const void *in0, const void *in1, void *ou
         break;
     case DMU_PROBE_LDS_READ_TR16:
         hipLaunchKernelGGL(probe_lds_tr16, dim3(1), dim3(64), 0, s, a, reinterpret_cast<const int32_t *>(b), o);
+        break;
+    case DMU_PROBE_LDS_READ_TR8:
+        hipLaunchKernelGGL(probe_lds_tr8, dim3(1), dim3(64), 0, s, a, reinterpret_cast<const int32_t *>(b), o);
         break;
     case DMU_PROBE_LDS_FRAG: hipLaunchKernelGGL(probe_lds_frag, dim3(1), dim3(64), 0, s, a, o); break;
     case DMU_PROBE_LDS_FRAG_T: hipLaunchKernelGGL(probe_lds_frag_t, dim3(1), dim3(64), 0, s, a, o); break;

@@ -34,7 +34,9 @@
 //              the hardware dispatches first on each XCD; with one workgroup
 //              per compute unit all of them are resident anyway.  Each wait is
 //              bounded: past the limit the worker records an error word in the
-//              workspace and goes on, so every wavefront always exits.
+//              workspace and goes on, so every wavefront always exits (the
+//              result is then wrong, and the host query of the error word,
+//              dmu_gemm_streamk_error, reports it).
 #pragma once
 
 #include "dmu_tiled.hpp"
@@ -103,14 +105,19 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
                 for (uint32_t v = streamk_owner(sk, ts); v < w; ++v) {
                     if (tid == 0) {
                         uint32_t n = 0;
+                        bool seen = true;
                         while (__hip_atomic_load(&sk.flags[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
                             __builtin_amdgcn_s_sleep(4);
                             if (++n >= sk.spin_limit) {
                                 __hip_atomic_store(sk.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                seen = false;
                                 break;
                             }
                         }
-                        __hip_atomic_store(&sk.flags[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        // a flag that was never seen stays as the late worker leaves it: the
+                        // error word tells the caller to clear the workspace again
+                        if (seen)
+                            __hip_atomic_store(&sk.flags[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                     __syncthreads(); // the device-coherent loads below are issued after the flag was seen
                     G::add_partial(sk.partials + (size_t)v * G::PARTIAL_BYTES, acc, lane, wave);

@@ -49,6 +49,17 @@
 
 #include <type_traits>
 
+// LDS-poisoning debug build (compiled with DMU_LDS_POISON=1; never the product
+// library): right after the barrier that retires a stage, each wavefront
+// overwrites its own staging slots of that stage with all-ones bytes (NaN in
+// fp16, bf16 and e4m3, -1 in int8), long before the next K-tile's data lands
+// there.  A fragment read that strayed past its barrier would then feed the
+// poison into D, so parity of this build with the product build bit for bit
+// shows that every stage is read only inside its window.
+#ifndef DMU_LDS_POISON
+#define DMU_LDS_POISON 0
+#endif
+
 namespace dmu {
 
 // ---------------------------------------------------------------------------
@@ -113,6 +124,11 @@ template <int R, int NW, bool MASK> struct KcTile {
         }
         *reinterpret_cast<u32x4 *>(tile + (wave * NL + i) * 1024 + wlane) = v;
     }
+    // Transfer i's 16 bytes of this lane, unmasked (the poisoning debug build).
+    __device__ __forceinline__ void store_raw(int i, char *tile, uint32_t wave, u32x4 v) const
+    {
+        *reinterpret_cast<u32x4 *>(tile + (wave * NL + i) * 1024 + wlane) = v;
+    }
     // Rows [r0, r0 + 16) (r0 a multiple of 16), K-step ks (0, 1): lane l reads
     // row r0 + l % 16, logical bytes 64 ks + 16 (l / 16) .. +15 of the K-tile.
     static __device__ __forceinline__ u32x4 frag(const char *tile, uint32_t r0, uint32_t ks, uint32_t lane)
@@ -174,6 +190,10 @@ template <int R, int NW> struct McTile {
     {
         *reinterpret_cast<u32x4 *>(tile + wofs[i]) = v;
     }
+    __device__ __forceinline__ void store_raw(int i, char *tile, uint32_t, u32x4 v) const
+    {
+        *reinterpret_cast<u32x4 *>(tile + wofs[i]) = v;
+    }
     // Columns [c0, c0 + 16), K-step ks: lane l gets column c0 + l % 16 and
     // k = 32 ks + 8 (l / 16) + 0..7, by two transposing reads (k .. k+3, then
     // k+4 .. k+7).  Lane j of each 16-lane group g addresses
@@ -223,16 +243,41 @@ template <int R, int NW> struct TileOf<MC16, R, NW> { typedef McTile<R, NW> type
 // values, with the fused epilogue (scales, bias, C, activation), RNE
 // conversion and M/N masking on the way out.
 // ---------------------------------------------------------------------------
-// Geometry of the parked stripes: a 16-row stripe of 16 NT accumulator
-// columns per wavefront, read back by LPR lanes per row, RPI rows per store
-// instruction, ITS instructions per stripe.
+// Geometry of the parked stripes.  A stripe is 16 rows of 16 NT accumulator
+// columns (fp32 / int32) per wavefront, rows of ROWB bytes without padding,
+// the 16-byte chunks of row r permuted by XOR with r (mod the chunks per row).
+//
+// LDS bank rules: the conflict counters of the K loop's staging writes and
+// fragment reads and of several park layouts are fitted by a ds_write_b128
+// served 8 consecutive lanes per cycle over 32 banks of 4 bytes, and a
+// ds_read_b128 served 16 lanes per cycle over 64 banks in quad-structured
+// groups -- lanes {0-3, 12-15, 20-23, 24-27}, and the groups obtained from it
+// by flipping lane bits 2 and 5.
+//   writes  lane l puts row l % 16, chunk 4 ni + l / 16: the 8 lanes of a
+//           write group hold rows r .. r+7 at one chunk, which the XOR
+//           spreads over the 8 chunk slots of 128 bytes;
+//   reads   lane l takes row l / CH + RPI it, chunk l % CH: a read group
+//           spans two adjacent rows 2j, 2j + 1 (the same XOR above bit 0),
+//           and takes chunks with bit 2 = bit 3 from one and bit 2 != bit 3
+//           from the other, which the XOR keeps apart.
+// Each aligned block of CH lanes reads (and stores to D) one whole row, so
+// every store instruction writes whole rows with consecutive lanes.
 template <int NT> struct Park {
+    static_assert(NT == 2 || NT == 4 || NT == 8, "wavefront tiles of 32, 64 or 128 columns");
     static constexpr int COLS = 16 * NT;
-    static constexpr int PITCH = COLS * 4 + 16; // bytes per parked row (+16 spreads rows over the banks)
-    static constexpr int LPR = COLS / 4;
-    static constexpr int RPI = 64 / LPR;
-    static constexpr int ITS = 16 / RPI;
-    // Stripe: lane l's accumulator tile ni holds row l % 16, columns 16 ni + 4 (l / 16) ..
+    static constexpr int ROWB = COLS * 4;     // bytes per parked row
+    static constexpr int CH = COLS / 4;       // 16-byte chunks per row: 8, 16 or 32
+    static constexpr int RPI = 64 / CH;       // rows per read instruction
+    static constexpr int ITS = 16 / RPI;      // reads per stripe
+    static constexpr int RSTEP = RPI;         // a lane's row step between reads
+    static constexpr int BYTES = 16 * ROWB;
+    static __device__ __forceinline__ uint32_t addr(uint32_t r, uint32_t chunk)
+    {
+        return r * ROWB + ((chunk ^ (r & (CH - 1))) << 4);
+    }
+    static __device__ __forceinline__ uint32_t rd_row(uint32_t l) { return l / CH; }
+    static __device__ __forceinline__ uint32_t rd_chunk(uint32_t l) { return l % CH; }
+    // Stripe mi: lane l's accumulator tile ni holds row l % 16, columns 16 ni + 4 (l / 16) ..
     template <class AccT, int MT>
     static __device__ __forceinline__ void put(char *lds, const AccT (&acc)[MT][NT], int mi, uint32_t lane)
     {
@@ -244,8 +289,14 @@ template <int NT> struct Park {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 v[e] = acc[mi][ni][e];
-            *reinterpret_cast<st4 *>(lds + (lane & 15u) * PITCH + (ni * 16 + 4 * (lane >> 4)) * 4) = v;
+            *reinterpret_cast<st4 *>(lds + addr(lane & 15u, 4 * ni + (lane >> 4))) = v;
         }
+    }
+    // Read it of a stripe: this lane's 4 values of row rd_row(l) + RSTEP it.
+    template <class st4>
+    static __device__ __forceinline__ st4 get(const char *lds, int it, uint32_t lane)
+    {
+        return *reinterpret_cast<const st4 *>(lds + addr(rd_row(lane) + RSTEP * it, rd_chunk(lane)));
     }
 };
 
@@ -261,7 +312,7 @@ __device__ __forceinline__ void store_interior(const GemmParams &p, const AccT (
     typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
     typedef st st4 __attribute__((ext_vector_type(4)));
     typedef ot ov4 __attribute__((ext_vector_type(4)));
-    const uint32_t col = (lane % K::LPR) * 4, r0 = lane / K::LPR;
+    const uint32_t col = K::rd_chunk(lane) * 4, r0 = K::rd_row(lane);
     float csv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, bv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, rsv[MT][K::ITS];
     if constexpr (EPI) {
 #pragma unroll
@@ -273,7 +324,7 @@ __device__ __forceinline__ void store_interior(const GemmParams &p, const AccT (
         for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
             for (int it = 0; it < K::ITS; ++it)
-                rsv[mi][it] = ep.rs ? ep.rs[m_base + mi * 16 + K::RPI * it + r0] : 1.0f;
+                rsv[mi][it] = ep.rs ? ep.rs[m_base + mi * 16 + K::RSTEP * it + r0] : 1.0f;
     }
     const int64_t rel = (m_base + r0) * p.ldd + n; // this lane's first element of D
     ot *D0 = reinterpret_cast<ot *>(Db) + rel;
@@ -284,12 +335,12 @@ __device__ __forceinline__ void store_interior(const GemmParams &p, const AccT (
         if constexpr (HAS_C) {
 #pragma unroll
             for (int it = 0; it < K::ITS; ++it)
-                c[it] = *reinterpret_cast<const ov4 *>(C0 + (int64_t)(mi * 16 + K::RPI * it) * p.ldc);
+                c[it] = *reinterpret_cast<const ov4 *>(C0 + (int64_t)(mi * 16 + K::RSTEP * it) * p.ldc);
         }
         K::put(lds, acc, mi, lane);
 #pragma unroll
         for (int it = 0; it < K::ITS; ++it) {
-            const st4 v = *reinterpret_cast<const st4 *>(lds + (K::RPI * it + r0) * K::PITCH + col * 4);
+            const st4 v = K::template get<st4>(lds, it, lane);
             ov4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -298,7 +349,7 @@ __device__ __forceinline__ void store_interior(const GemmParams &p, const AccT (
             // streaming store: D is not read again by this kernel, and all
             // tiles write it in one burst at the end (measured on 4096^3
             // bf16: 113 -> 110 us)
-            __builtin_nontemporal_store(o, reinterpret_cast<ov4 *>(D0 + (int64_t)(mi * 16 + K::RPI * it) * p.ldd));
+            __builtin_nontemporal_store(o, reinterpret_cast<ov4 *>(D0 + (int64_t)(mi * 16 + K::RSTEP * it) * p.ldd));
         }
     }
 }
@@ -315,7 +366,7 @@ __device__ __forceinline__ void store_edge_plain(const GemmParams &p, const AccT
     typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
     typedef st st4 __attribute__((ext_vector_type(4)));
     typedef ot ov4 __attribute__((ext_vector_type(4)));
-    const uint32_t col = (lane % K::LPR) * 4, r0 = lane / K::LPR;
+    const uint32_t col = K::rd_chunk(lane) * 4, r0 = K::rd_row(lane);
     const bool vec = p.d_vec4 && n + 3 < p.N;
     const int nv = n >= p.N ? 0 : (p.N - n < 4 ? (int)(p.N - n) : 4); // valid elements of this lane's vector
     ot *D0 = reinterpret_cast<ot *>(Db) + (m_base + r0) * p.ldd + n;
@@ -324,14 +375,14 @@ __device__ __forceinline__ void store_edge_plain(const GemmParams &p, const AccT
         K::put(lds, acc, mi, lane);
 #pragma unroll
         for (int it = 0; it < K::ITS; ++it) {
-            const st4 v = *reinterpret_cast<const st4 *>(lds + (K::RPI * it + r0) * K::PITCH + col * 4);
-            if (m_base + mi * 16 + K::RPI * it + r0 >= p.M)
+            const st4 v = K::template get<st4>(lds, it, lane);
+            if (m_base + mi * 16 + K::RSTEP * it + r0 >= p.M)
                 continue;
             ov4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 o[e] = epi_one<O>(0, 0, v[e], 1.0f, 1.0f, 0.0f, false, ot{});
-            ot *d = D0 + (int64_t)(mi * 16 + K::RPI * it) * p.ldd;
+            ot *d = D0 + (int64_t)(mi * 16 + K::RSTEP * it) * p.ldd;
             if (vec) {
                 __builtin_nontemporal_store(o, reinterpret_cast<ov4 *>(d));
             } else {
@@ -357,8 +408,8 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
     typedef st st4 __attribute__((ext_vector_type(4)));
     typedef ot ov4 __attribute__((ext_vector_type(4)));
     // On the way out lane l always handles the same four columns (n_base +
-    // 4 (l % LPR) ..) and, in stripe mi and store it, row 16 mi + RPI it + l / LPR.
-    const uint32_t col = (lane % K::LPR) * 4, r0 = lane / K::LPR;
+    // 4 rd_chunk(l) ..) and, in stripe mi and store it, row 16 mi + RSTEP it + rd_row(l).
+    const uint32_t col = K::rd_chunk(lane) * 4, r0 = K::rd_row(lane);
     const int64_t n = n_base + col;
 
     // A block wholly inside D with 4-element vectors legal needs no per-row
@@ -403,7 +454,7 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
         for (int it = 0; it < K::ITS; ++it) {
-            const int64_t m = m_base + mi * 16 + K::RPI * it + r0;
+            const int64_t m = m_base + mi * 16 + K::RSTEP * it + r0;
             rsv[mi][it] = ep.rs && m < p.M ? ep.rs[m] : 1.0f;
         }
 #pragma unroll
@@ -415,8 +466,8 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const AccT (&a
 #pragma unroll
             for (int i = 1; i < K::ITS; ++i)
                 rs = it == i ? rsv[mi][i] : rs;
-            const uint32_t row = K::RPI * it + r0;
-            const st4 v = *reinterpret_cast<const st4 *>(lds + row * K::PITCH + col * 4);
+            const uint32_t row = K::RSTEP * it + r0;
+            const st4 v = K::template get<st4>(lds, it, lane);
             const int64_t m = m_base + mi * 16 + row;
             if (m >= p.M)
                 continue;
@@ -465,7 +516,13 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     static constexpr int E = (T == I8 || F8) ? 1 : 2;
     static constexpr int FH = F8 ? 2 : 1;           // 16-byte fragment halves an MFMA reads
     static constexpr int NW = WGM * WGN;
-    static_assert(NW == 8, "eight wavefronts, two per SIMD");
+    static_assert(NW == 8 || NW == 4, "eight wavefronts (two per SIMD) or four (one per SIMD)");
+    // Four wavefronts: 128 x 128 wavefront tiles, whose 256 accumulator
+    // registers live in the AGPRs (one wavefront per SIMD holds 512 registers);
+    // the MFMAs update them in place, and the first K-step of a range writes
+    // them from a zero accumulator operand (no initialisation of the
+    // accumulators precedes the main loop).
+    static constexpr bool AG = NW == 4;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN; // wavefront tile
     static constexpr int MT = WTM / 16, NT = WTN / 16;   // MFMA tiles per wavefront
     static constexpr int MN = MT * NT;
@@ -473,6 +530,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     static_assert(AMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(BMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(!F8 || MN <= 16, "e4m3 fragments (8 registers per tile) fit beside the accumulators");
+    static_assert(!AG || !F8, "the four-wavefront tile takes the 16-bit and int8 instructions");
     typedef typename Mfma<T>::acc_t acc_t;
     typedef typename TileOf<AMODE, BM, NW>::type ATile;
     typedef typename TileOf<BMODE, BN, NW>::type BTile;
@@ -482,10 +540,10 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     // and fragments leave room for one set): the loads of K-tile kt+3 go out
     // while K-tile kt+1 is written to LDS, which doubles the bytes in flight
     // per compute unit.
-    static constexpr int PD = BM * BN < 256 * 256 ? 2 : 1;
+    static constexpr int PD = (BM * BN < 256 * 256) ? 2 : 1;
     static constexpr uint32_t ABYTES = (ATile::BYTES + 255) & ~255u,
                               STAGE = (ABYTES + BTile::BYTES + 255) & ~255u;
-    static constexpr int PARK = 16 * Park<NT>::PITCH; // per wavefront, epilogue
+    static constexpr int PARK = Park<NT>::BYTES; // per wavefront, epilogue
     static_assert(NW * PARK <= 2 * STAGE, "parking area fits in the stages");
     static constexpr uint32_t PARTIAL_BYTES = NW * MN * 1024; // one tile's accumulators
 
@@ -579,6 +637,18 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         else
             tb.store(c - NA, stage + ABYTES, wave, lane, sb[set][c - NA], kt, k_bytes);
     };
+    // the debug build's poison of this wavefront's slots of a retired stage
+    auto poison = [&](char *stage) {
+        if constexpr (DMU_LDS_POISON) {
+            const u32x4 ones = {~0u, ~0u, ~0u, ~0u};
+#pragma unroll
+            for (int c = 0; c < NA; ++c)
+                ta.store_raw(c, stage, wave, ones);
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+                tb.store_raw(c, stage + ABYTES, wave, ones);
+        }
+    };
 
     // Operand fragments of one K-step (e4m3: both K-step halves of the K-tile,
     // which one MFMA consumes together).
@@ -593,12 +663,19 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         for (int h = 0; h < FH; ++h)
             bfr[j][h] = BTile::frag(stage + ABYTES, wn * WTN + j * 16, F8 ? h : ks, lane);
     };
-    auto mfma = [&](int i, int j) {
+    // zero: std::true_type for the first K-step of the range on AGPR
+    // accumulators (the product starts from a zero accumulator operand)
+    auto mfma = [&](int i, int j, auto zero) {
         if constexpr (F8)
             acc[i][j] = Mfma<E4M3>::step2(bfr[j][0], bfr[j][1], af[i][0], af[i][1], acc[i][j]);
+        else if constexpr (AG && decltype(zero)::value)
+            Mfma<T>::step_a0(bfr[j][0], af[i][0], acc[i][j]);
+        else if constexpr (AG)
+            Mfma<T>::step_a(bfr[j][0], af[i][0], acc[i][j]);
         else
             acc[i][j] = Mfma<T>::step(bfr[j][0], af[i][0], acc[i][j]);
     };
+    const std::false_type acc_in{};
 
     constexpr int NLD = NA + NB;
 
@@ -654,7 +731,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         auto ktile8 = [&](int kt, char *nxt, int set) __attribute__((always_inline)) {
 #pragma unroll
             for (int q = 0; q < HALF; ++q) {
-                mfma(row_of(q), col_of(q));
+                mfma(row_of(q), col_of(q), acc_in);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ci = q * NLD / HALF; ci < (q + 1) * NLD / HALF; ++ci) {
@@ -664,10 +741,11 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
                 __builtin_amdgcn_sched_barrier(0);
             }
             stage_barrier();
+            poison(nxt == smem ? smem + STAGE : smem); // K-tile kt's stage: read no more
 #pragma unroll
             for (int q = HALF; q < MN; ++q) {
                 const int i = row_of(q), j = col_of(q), h = q - HALF;
-                mfma(i, j);
+                mfma(i, j, acc_in);
                 __builtin_amdgcn_sched_barrier(0);
                 if (h < HM)
                     read_a(h, nxt, 0);
@@ -693,12 +771,13 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     } else {
     // One K-tile: K-tile kt is in stage cur, K-tile kt+1 goes from staging
     // set `set` to stage nxt, and K-tile kt+1+PD is loaded into that set.
-    auto ktile = [&](int kt, const char *cur, char *nxt, int set) __attribute__((always_inline)) {
+    // zero: std::true_type for the range's first K-tile on AGPR accumulators.
+    auto ktile = [&](auto zero, int kt, char *cur, char *nxt, int set) __attribute__((always_inline)) {
         // K-step 0; each fragment of K-step 1 is read right after its last use.
 #pragma unroll
         for (int q = 0; q < MN; ++q) {
             const int i = row_of(q), j = col_of(q);
-            mfma(i, j);
+            mfma(i, j, zero);
             __builtin_amdgcn_sched_barrier(0); // reads below reuse the registers this MFMA reads
             if (q == last_b(j))
                 read_b(j, cur, 1);
@@ -715,7 +794,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
 #pragma unroll
         for (int q = 0; q < HALF; ++q) {
             const int i = row_of(q), j = col_of(q);
-            mfma(i, j);
+            mfma(i, j, acc_in);
             __builtin_amdgcn_sched_barrier(0);
             const int slot = MN + q;
 #pragma unroll
@@ -726,13 +805,14 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
             __builtin_amdgcn_sched_barrier(0);
         }
         stage_barrier();
+        poison(cur); // K-tile kt's stage: its last fragment reads are done
         // Second half: K-step 0 of K-tile kt+1 from the other stage -- first the
         // A fragments of the rows already done, one per MFMA, then each
         // remaining fragment right after its last use.
 #pragma unroll
         for (int q = HALF; q < MN; ++q) {
             const int i = row_of(q), j = col_of(q), h = q - HALF;
-            mfma(i, j);
+            mfma(i, j, acc_in);
             __builtin_amdgcn_sched_barrier(0);
             if (h < HM)
                 read_a(h, nxt, 0);
@@ -743,20 +823,40 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if constexpr (PD == 2) {
+    if constexpr (AG) {
+        // the first K-tile peeled: its K-step 0 writes the accumulators from zero
+        static_assert(PD == 1, "one staging set on the four-wavefront tile");
+        ktile(std::true_type{}, kb, smem + (kb & 1) * STAGE, smem + ((kb + 1) & 1) * STAGE, 0);
+        for (int kt = kb + 1; kt < ke; ++kt)
+            ktile(acc_in, kt, smem + (kt & 1) * STAGE, smem + ((kt + 1) & 1) * STAGE, 0);
+    } else if constexpr (PD == 2) {
         // two K-tiles per iteration: the staging set and both stages are
         // fixed for each of them
         int kt = kb;
         for (; kt + 1 < ke; kt += 2) {
-            ktile(kt, smem, smem + STAGE, 1);
-            ktile(kt + 1, smem + STAGE, smem, 0);
+            ktile(acc_in, kt, smem, smem + STAGE, 1);
+            ktile(acc_in, kt + 1, smem + STAGE, smem, 0);
         }
         if (kt < ke)
-            ktile(kt, smem, smem + STAGE, 1);
+            ktile(acc_in, kt, smem, smem + STAGE, 1);
     } else {
         for (int kt = kb; kt < ke; ++kt)
-            ktile(kt, smem + (kt & 1) * STAGE, smem + ((kt + 1) & 1) * STAGE, 0);
+            ktile(acc_in, kt, smem + (kt & 1) * STAGE, smem + ((kt + 1) & 1) * STAGE, 0);
     }
+    }
+    if constexpr (AG) {
+        // The MFMAs above are assembly the compiler does not see as matrix
+        // instructions, so it cannot space the first reads of their results
+        // (v_accvgpr_read in the epilogue) from the last writes: 32 wait states
+        // here, after every MFMA (all are volatile, as is this), and the
+        // accumulators pass through empty volatile statements after it, so no
+        // read of them moves above the wait.
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                asm volatile("" : "+a"(acc[i][j]));
     }
     }
 
@@ -811,22 +911,32 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     }
 };
 
+// Eight wavefronts run two per SIMD, four one per SIMD (with the AGPRs).
 template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
 __global__ void __launch_bounds__(64 * WGM * WGN)
-    __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tiled(GemmParams p)
+    __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4))) gemm_tiled(GemmParams p)
 {
     typedef Tiled<T, O, BM, BN, WGM, WGN, AMODE, BMODE> G;
     __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
     typename G::acc_t acc[G::MT][G::NT];
-#pragma unroll
-    for (int i = 0; i < G::MT; ++i)
-#pragma unroll
-        for (int j = 0; j < G::NT; ++j)
-            acc[i][j] = typename G::acc_t{};
     const int nk = (int)(((int64_t)p.K * G::E + 127) / 128);
+    if constexpr (!G::AG) {
+#pragma unroll
+        for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+            for (int j = 0; j < G::NT; ++j)
+                acc[i][j] = typename G::acc_t{};
+    }
     if (nk > 0) {
         typename G::Staging st;
         G::mainloop(p, tile_of(p, blockIdx.x), 0, nk, smem, acc, threadIdx.x, st);
+    } else if constexpr (G::AG) {
+        // K == 0: D = C (the main loop writes the accumulators otherwise)
+#pragma unroll
+        for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+            for (int j = 0; j < G::NT; ++j)
+                acc[i][j] = typename G::acc_t{};
     }
     // The tile coordinates and lane are derived afresh from opaque copies of
     // the ids, so that the compiler does not keep the values of the prologue

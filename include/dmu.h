@@ -195,11 +195,17 @@ int dmu_gemm_ex_check(const dmu_gemm_args *args, const dmu_epilogue *ep);
  *                  every call leaves its flag words zero again, so one
  *                  workspace serves any number of calls in stream order.  Calls
  *                  that overlap in time (several streams) need separate
- *                  workspaces.  Its error word (the 32-bit word at the offset
- *                  of the worker count x 4 rounded up to 256) is set nonzero if
- *                  a worker waited past its limit (not expected: every worker
- *                  is resident) -- then the result is wrong and the workspace
- *                  must be zero-filled again.
+ *                  workspaces.  Layout: an error word (the first 32-bit word;
+ *                  bytes 0-255 are reserved for it), one 32-bit flag per
+ *                  worker from byte 256, then one slot of partial sums per
+ *                  worker from the next multiple of 256 bytes.  Each wait of a
+ *                  worker for another is bounded; a wait that runs past its
+ *                  limit (not expected: every worker is resident) sets the
+ *                  error word and the kernel completes with a WRONG result.
+ *                  The launch itself still returns DMU_OK (it is
+ *                  asynchronous): query dmu_gemm_streamk_error after the
+ *                  call; when it reports a failure, discard D and zero-fill
+ *                  the workspace again before its next use.
  *  workspace_bytes its size.
  * The schedule is used where it pays: when the data-parallel kernel's tiles
  * fill less than 80 % of its waves of one workgroup per compute unit (few
@@ -213,6 +219,19 @@ int dmu_gemm_ex_check(const dmu_gemm_args *args, const dmu_epilogue *ep);
  */
 int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *ep, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/*
+ * Whether a wait inside an earlier dmu_gemm_streamk call on `workspace` ran
+ * past its limit (so that call's D is wrong).  Waits for `stream` (the stream
+ * of those calls; NULL is the default stream), then reads the workspace's
+ * error word: *failed = 1 if it is set, else 0.  The word stays set until the
+ * caller zero-fills the workspace.  `workspace` is a device pointer, 256-byte
+ * aligned; `failed` a host pointer owned by the caller.  Returns DMU_OK,
+ * DMU_ERR_INVALID_ARG for a NULL or misaligned pointer (before any HIP call),
+ * or DMU_ERR_HIP if the copy or the synchronisation fails.
+ */
+int dmu_gemm_streamk_error(const void *workspace, void *stream, int *failed);
+
 
 /* Workspace bytes dmu_gemm_streamk needs for these arguments on the current
  * device (the worker count is the device's compute-unit count, at most the
@@ -275,7 +294,10 @@ int dmu_attention(const dmu_attention_args *args, void *stream);
 int dmu_attention_check(const dmu_attention_args *args);
 
 /*
- * Name of the kernel variant dmu_gemm would launch for `args` (a static
+ * Name of the kernel variant dmu_gemm would launch for `args` -- in the manner
+ * of the walkthrough's kernel name ("hgemm_mma_m16n8k16_mma2x4_warp4x4_kernel",
+ * opening listing: the instruction shape, the instruction tiles per warp and
+ * the warp tiles are spelled out in the name) -- as a static
  * string: "mfma_<tile>_<A mode>_<B mode>_<in>_<out>", e.g.
  * "mfma_256x256_k16_t16_bf16_bf16" -- 256 x 256 tiles, A K-contiguous with
  * 16-byte rows, B M/N-contiguous 16-bit -- or "mfma_generic64_any_any_f16_f32"
@@ -283,14 +305,20 @@ int dmu_attention_check(const dmu_attention_args *args);
  * launch nothing.  The tile is 256 x 128 when N <= 128 < M; otherwise, when
  * 240 or more 256 x 256 tiles cover the problem, 256 x 256 if K spans more
  * than two 128-byte K-tiles and 256 x 128 if it spans at most two; 128 x 128
- * for smaller problems; e4m3 never takes 256 x 256.  Host-only; no GPU access.
+ * for smaller problems; e4m3 never takes 256 x 256.  The environment
+ * variable DMU_FORCE_KERNEL=256x256 | 256x256w4 | 256x128 | 128x128 | generic
+ * overrides the choice ("256x256w4": the 256 x 256 tile on four wavefronts of
+ * 128 x 128 with AGPR accumulators, 16-bit and int8 inputs; never chosen by
+ * default).  Host-only; no GPU access.
  */
 const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
 
 /*
  * Compute units and peak shader clock (kHz) of HIP device `device`, as the
  * runtime reports them -- the inputs of a dense peak derived on the machine
- * itself (compute units x clock x multiply-adds per clock and unit).  Both
+ * itself (compute units x clock x multiply-adds per clock and unit), the
+ * derivation "Tensor Cores, CUTLASS and CuTe" makes in its opening section for
+ * its own GPU (multiprocessors x tensor-core FMAs per clock x 2 x clock).  Both
  * outputs are host pointers owned by the caller.  Returns DMU_OK;
  * DMU_ERR_INVALID_ARG for a NULL output or a negative device (message in
  * dmu_last_error()); DMU_ERR_HIP when the runtime cannot answer (no such
@@ -298,10 +326,14 @@ const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
  */
 int dmu_device_info(int device, int *compute_units, int *max_clock_khz);
 
-/* Static description of a return code. */
+/* Static description of a return code.  The host entry point of "Tensor Cores,
+ * CUTLASS and CuTe" section 4.4 rejects a bad call with a message before any
+ * kernel runs; across a C ABI that is a status code (dmu_status) plus the
+ * message below.  Host-only; no GPU access. */
 const char *dmu_status_string(int status);
 
-/* Detail of the last failing call on this thread ("" if none).  The pointer
+/* Detail of the last failing call on this thread ("" if none), the message
+ * part of the error reporting described at dmu_status_string.  The pointer
  * stays valid until the next call into the library on this thread. */
 const char *dmu_last_error(void);
 
@@ -319,6 +351,7 @@ const char *dmu_last_error(void);
  *                           (in_type bits)        row-major          [64 lanes][regs] 32-bit
  *  DMU_PROBE_LDS_READ_B128  LDS image, 4096 B     int32 byte         [64][16 bytes]
  *  DMU_PROBE_LDS_READ_TR16  LDS image, 4096 B     address per lane   [64][8 bytes]
+ *  DMU_PROBE_LDS_READ_TR8   LDS image, 4096 B     address per lane   [64][8 bytes]
  *  DMU_PROBE_LDS_FRAG       32 x 128-byte tile,   unused             [64][2 row blocks][2 K-steps]
  *                           row-major (logical)                      [16 bytes]
  *  DMU_PROBE_LDS_FRAG_T     64 x 128 16-bit tile, unused             [64][8 column blocks][2 K-steps]
@@ -333,7 +366,8 @@ const char *dmu_last_error(void);
  *    per lane, the GEMM kernels' two 16-byte fragments of a 128-byte row: bytes
  *    16 (l / 16) .. +15 and 64 + 16 (l / 16) .. +15 of row l % 16.
  *  LDS_READ_*: the image is copied to LDS; lane l reads at in1[l] (masked to
- *    an aligned in-bounds address) with ds_read_b128 / ds_read_b64_tr_b16.
+ *    an aligned in-bounds address) with ds_read_b128 / ds_read_b64_tr_b16 /
+ *    ds_read_b64_tr_b8.
  *  LDS_FRAG: the tile is stored with the tiled kernel's staging writes of a
  *    K-contiguous operand and read back with its fragment reads (rows 16 b +
  *    l % 16, bytes 64 ks + 16 (l / 16) .. +15).
@@ -361,6 +395,7 @@ enum {
     DMU_PROBE_LDS_FRAG = 12,
     DMU_PROBE_LDS_FRAG_T = 13,
     DMU_PROBE_LANE_SWAP = 14,
+    DMU_PROBE_LDS_READ_TR8 = 15,
     DMU_PROBE_CVT_BF16 = 30,
     DMU_PROBE_CVT_F16 = 31
 };

@@ -112,9 +112,10 @@ def run_dmu(p, force=None, fill=None, return_name=False, ep=None, in_place=False
     return (out, name) if return_name else out
 
 
-def run_streamk(p, ep=None, workspace=None, calls=1):
+def run_streamk(p, ep=None, workspace=None, calls=1, check_error=True):
     """Run one workload through dmu_gemm_streamk (``calls`` times with the same
-    workspace); returns (D bits, kernel name, workspace tensor or None)."""
+    workspace); returns (D bits, kernel name, workspace tensor or None).  With
+    ``check_error`` the workspace's error word (dmu_gemm_streamk_error) must be clear."""
     torch = _torch()
     dA, dB = to_dev(p.A), to_dev(p.B)
     dC = to_dev(p.C) if p.C is not None else None
@@ -133,6 +134,8 @@ def run_streamk(p, ep=None, workspace=None, calls=1):
     for _ in range(calls):
         dmu.dmu_gemm_streamk(args, e, workspace, 4 * workspace.numel() if workspace is not None else 0)
     torch.cuda.synchronize()
+    if workspace is not None and check_error:
+        assert not dmu.dmu_gemm_streamk_error(workspace, check=False), "a stream-K wait gave up"
     return from_dev(dD, p.out_type)[: p.batch * p.stride_d], dmu.dmu_gemm_kernel_name(args), workspace
 
 

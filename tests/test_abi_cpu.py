@@ -113,6 +113,8 @@ def test_empty_problems_launch_nothing():
 @pytest.mark.parametrize("kw,expect", [
     (dict(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096, in_type="bf16", out_type="bf16"),
      "mfma_256x256_k16_t16_bf16_bf16"),
+    (dict(M=4096, N=4096, K=4096, lda=4096, layout_b="col", ldb=4096, ldd=4096, in_type="bf16",
+          out_type="bf16"), "mfma_256x256_k16_k16_bf16_bf16"),
     (dict(in_type="f16", out_type="f32"), "mfma_128x128_k16_t16_f16_f32"),
     (dict(M=5000, N=3000, K=2050, lda=2050, layout_b="col", ldb=2050, ldd=3000, in_type="f16",
           out_type="f16", acc_type="f16"), "mfma_256x256_kd_kd_f16_f16"),
@@ -293,3 +295,16 @@ def test_streamk_argument_errors_before_any_hip_call():
     assert dmu.dmu_gemm_streamk(args(out_type="i32"), None, None, 0, stream=0, check=False) == \
         dmu.DMU_ERR_UNSUPPORTED
     assert dmu.dmu_gemm_streamk(args(M=0), None, None, 0, stream=0) == dmu.DMU_OK  # empty: nothing launched
+
+
+def test_streamk_error_query_argument_errors_before_any_hip_call():
+    """A NULL result pointer or a misaligned workspace is rejected before the query touches the
+    GPU (a NULL workspace names the library's own scratch, a GPU-side path)."""
+    lib = dmu.library()
+    failed = ctypes.c_int(7)
+    assert lib.dmu_gemm_streamk_error(FAKE, None, None) == dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_gemm_streamk_error(FAKE + 4, None, ctypes.byref(failed)) == dmu.DMU_ERR_INVALID_ARG
+    assert "aligned" in dmu.dmu_last_error()
+    assert failed.value == 0
+    with pytest.raises(dmu.DmuError):
+        dmu.dmu_gemm_streamk_error(FAKE + 4, stream=0)

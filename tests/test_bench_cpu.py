@@ -167,3 +167,20 @@ def test_short_dispatch_gives_no_clock(tmp_path):
     assert "gui_active_ghz" not in res and res["counter_dispatch_us"] == pytest.approx(7.51)
     text = open(tmp_path / "out" / "k_w_counters.md").read()
     assert "too short for a clock" in text
+
+
+@pytest.mark.parametrize("cfg", sorted(bench.WORKLOAD_NAMES))
+def test_committed_trace_not_slower_than_its_session_bench(cfg):
+    """Where a profile carries the bench line of its own session, the kernel-trace average of the
+    timed dispatches does not exceed that run's time per step by more than 1 % (the trace backs
+    the line's roofline fraction).  The headline workload must carry one."""
+    path = os.path.join(bench.ROOT, "profiles", f"traffic_{bench.WORKLOAD_NAMES[cfg]}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"no counter record for {cfg}")
+    rec = json.load(open(path))
+    if "bench_same_session" not in rec:
+        assert cfg != "c2", "the 4096^3 profile must carry its session's bench line"
+        pytest.skip("profile taken without a bench line")
+    b = rec["bench_same_session"]
+    assert b["kernel"] == rec["kernel"]
+    assert rec["avg_us"] <= b["ms_per_step"] * 1e3 * 1.01

@@ -27,7 +27,7 @@ REDUCED = {
     "c4o": dict(M=300, N=128, K=520, batch=2),
     "c5": dict(M=300, N=260, K=384),
 }
-KERNELS = [None, "256x256", "128x128", "256x128", "generic"]
+KERNELS = [None, "256x256", "256x256w4", "128x128", "256x128", "generic"]
 
 
 @pytest.mark.parametrize("cfg", list(REDUCED))
@@ -56,7 +56,7 @@ def closed_form(p) -> np.ndarray:
     i = np.arange(p.M)[None, :, None]
     j = np.arange(p.N)[None, None, :]
     b = np.arange(p.batch)[:, None, None]
-    if p.name in ("c1", "c2", "c5"):
+    if p.name in ("c1", "c2", "c5", "c5nn"):
         return p.K * (i % 16) * (j % 8) + 0 * b
     if p.name == "c3":
         n_i = (p.K // 16) + ((i % 16) < (p.K % 16))
@@ -94,12 +94,30 @@ def test_full_size_random_sampled(cfg):
     gu.assert_close(got[gu.flat_index(p, bij)], want, p)
 
 
-def test_tiled_equals_fallback_bitwise():
+@pytest.mark.parametrize("kernel", [None, "256x256w4"])
+def test_tiled_equals_fallback_bitwise(kernel):
+    """Every output element goes through the same K-step sequence of the same matrix
+    instruction in each tiled form and in the fallback: bit-identical results."""
     for cfg in ("c2", "c3", "c4s", "c5"):
         p = workloads.make(cfg, "random", 3, **REDUCED[cfg])
-        a = gu.run_dmu(p)
+        a = gu.run_dmu(p, force=kernel)
         b = gu.run_dmu(p, force="generic")
         gu.assert_bits_equal(a, b, where=gu.valid_mask(p))
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c5"])
+def test_four_wavefront_tile_full_size(cfg):
+    """The four-wavefront 256 x 256 tile (accumulators in AGPRs) on the full problems: structured
+    inputs bit for bit against their closed forms, random inputs on sampled outputs."""
+    s = workloads.make(cfg, "structured")
+    got, name = gu.run_dmu(s, force="256x256w4", return_name=True)
+    assert "256x256w4" in name, name
+    bad = np.argwhere(as_values(s, got) != closed_form(s))
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    p = workloads.make(cfg, "random", 0)
+    got = gu.run_dmu(p, force="256x256w4")
+    bij = gu.sample_bij(p, n=384)
+    gu.assert_close(got[gu.flat_index(p, bij)], gu.oracle_at(p, bij), p)
 
 
 @pytest.mark.parametrize("in_t,out_t", [("f16", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("i8", "i32")])

@@ -21,23 +21,24 @@ pytestmark = pytest.mark.gpu
 
 
 def check_workspace_clean(p, ws, name):
-    """The W flag words are zero and the error word is clear after a call.  Layout of
-    dmu_gemm_streamk: W flag words, the error word at 4 W rounded up to 256 bytes, then
-    W slots of BM x BN 32-bit partial sums (BM x BN of the stream-K tile: 256 x 128
-    where the data-parallel plan is 256 x 256)."""
+    """The error word and the W flag words are zero after a call.  Layout of
+    dmu_gemm_streamk: the error word (bytes 0-255), W flag words from byte 256, then
+    from the next multiple of 256 bytes W slots of BM x BN 32-bit partial sums (BM x BN
+    of the stream-K tile: 256 x 128 where the data-parallel plan is 256 x 256)."""
     if ws is None:
         return
     tile = name.split("_")[1]
     bm, bn = {"256x256": (256, 128), "256x128": (256, 128), "128x128": (128, 128)}[tile]
     nbytes = 4 * ws.numel()
     round256 = lambda x: (x + 255) // 256 * 256
-    cands = [w for w in range(1, 4097) if round256(4 * w) + 256 + w * bm * bn * 4 <= nbytes
-             and round256(4 * w) + 256 + w * bm * bn * 4 > nbytes - 4 * 4]
+    size = lambda w: round256(256 + 4 * w) + w * bm * bn * 4
+    cands = [w for w in range(1, 4097) if nbytes - 4 * 4 < size(w) <= nbytes]
     assert len(cands) == 1, cands
     W = cands[0]
     words = ws.cpu().numpy().view(np.uint32)
-    assert not np.any(words[:W]), f"flags left set: {np.nonzero(words[:W])[0][:8]}"
-    assert words[round256(4 * W) // 4] == 0, "error word set"
+    assert words[0] == 0, "error word set"
+    assert not np.any(words[64: 64 + W]), f"flags left set: {np.nonzero(words[64: 64 + W])[0][:8]}"
+    assert not dmu.dmu_gemm_streamk_error(ws, check=False)
 
 
 @pytest.mark.parametrize("cfg,M,N,K", [
@@ -137,4 +138,43 @@ def test_full_size_sampled(monkeypatch):
     bij = gu.sample_bij(p, n=384)
     want = gu.oracle_at(p, bij)
     gu.assert_close(got[gu.flat_index(p, bij)], want, p)
+    check_workspace_clean(p, ws, name)
+
+
+def test_error_word_is_reported():
+    """The host query reads the workspace's error word: clear after a good call, set when a
+    worker has recorded a wait past its limit (planted here from the host, as the kernel
+    would leave it), and the binding raises on it."""
+    import torch
+
+    p = workloads.make("c1", "random", 28, M=256, N=256, K=4096)
+    p.C = None
+    got, name, ws = gu.run_streamk(p)
+    assert ws is not None
+    assert dmu.dmu_gemm_streamk_error(ws) is False
+    ws[0] = 1  # the error word (first 32-bit word)
+    torch.cuda.synchronize()
+    assert dmu.dmu_gemm_streamk_error(ws, check=False) is True
+    with pytest.raises(dmu.DmuError):
+        dmu.dmu_gemm_streamk_error(ws)
+    ws.zero_()
+    assert dmu.dmu_gemm_streamk_error(ws) is False
+
+
+def test_waits_that_give_up_are_reported(monkeypatch):
+    """Every wait is made to give up at its first unset flag (DMU_STREAMK_SPIN_LIMIT=0, the
+    host-side test hook; every kernel still runs to its end): the call's result may then be
+    wrong, but never without the error word saying so."""
+    monkeypatch.setenv("DMU_STREAMK_SPIN_LIMIT", "0")
+    p = workloads.make("c1", "random", 29, M=256, N=256, K=8192)  # 4 tiles, each split over 64 workers
+    p.C = None
+    got, name, ws = gu.run_streamk(p, check_error=False)
+    failed = dmu.dmu_gemm_streamk_error(ws, check=False)
+    want = gu.run_oracle(p)
+    if not failed:
+        gu.assert_close(got, want, p, where=gu.valid_mask(p))
+    ws.zero_()  # a failed call leaves late flags behind: the workspace is cleared again
+    monkeypatch.delenv("DMU_STREAMK_SPIN_LIMIT")
+    got2, _, ws = gu.run_streamk(p, workspace=ws)
+    gu.assert_close(got2, want, p, where=gu.valid_mask(p))
     check_workspace_clean(p, ws, name)

@@ -12,6 +12,7 @@ centre the pages' discussion:
   c4s  batch 32 of S = Q K^T, Q and K 4096 x 128 (B column-major), fp32 output
   c4o  batch 32 of O = P V, P 4096 x 4096 softmax rows, V 4096 x 128, fp32 output
   c5   int8 8192^3, A row-major, B column-major, int32 output
+  c5nn int8 8192^3, A and B row-major (an 8-bit operand that is not K-contiguous), int32 output
   c6   FP8 e4m3 8192^3, A row-major, B column-major, fp32 accumulate, bf16 output
   lk   bf16 1024 x 1024 x 16384 (long K, few output tiles), A and B row-major, bf16 output
 
@@ -26,7 +27,7 @@ from typing import Optional
 
 import numpy as np
 
-CONFIG_IDS = {"c1": 1, "c2": 2, "c3": 3, "c4s": 41, "c4o": 42, "c5": 5, "c6": 6, "lk": 7}
+CONFIG_IDS = {"c1": 1, "c2": 2, "c3": 3, "c4s": 41, "c4o": 42, "c5": 5, "c5nn": 51, "c6": 6, "lk": 7}
 
 # (M, N, K, batch, in_type, out_type, acc_type, layout_a, layout_b)
 FULL = {
@@ -36,6 +37,7 @@ FULL = {
     "c4s": (4096, 4096, 128, 32, "f16", "f32", "f32", "row", "col"),
     "c4o": (4096, 128, 4096, 32, "f16", "f32", "f32", "row", "row"),
     "c5": (8192, 8192, 8192, 1, "i8", "i32", "i32", "row", "col"),
+    "c5nn": (8192, 8192, 8192, 1, "i8", "i32", "i32", "row", "row"),
     "c6": (8192, 8192, 8192, 1, "e4m3", "bf16", "f32", "row", "col"),
     "lk": (1024, 1024, 16384, 1, "bf16", "bf16", "f32", "row", "row"),
 }
@@ -159,12 +161,12 @@ def _slices(cfg, kind, seed, M, N, K, batch):
                 z /= z.sum(axis=1, keepdims=True)
                 return z
             return softmax_rows, (lambda q: rb.uniform(-1, 1, (K, N)))
-        if cfg == "c5":
+        if cfg in ("c5", "c5nn"):
             return (lambda q: ra.integers(-128, 128, (M, K))), (lambda q: rb.integers(-128, 128, (K, N)))
         if cfg == "c6":  # N(0, 1) rounded to e4m3 (|x| stays far below its largest value, 448)
             return (lambda q: ra.standard_normal((M, K))), (lambda q: rb.standard_normal((K, N)))
     elif kind == "structured":
-        if cfg in ("c1", "c2", "c5", "c6", "lk"):
+        if cfg in ("c1", "c2", "c5", "c5nn", "c6", "lk"):
             return (lambda q: np.broadcast_to(i % 16, (M, K))), (lambda q: np.broadcast_to(j % 8, (K, N)))
         if cfg == "c3":
             return (lambda q: (kk_row % 16 == i % 16).astype(np.float64)), \
