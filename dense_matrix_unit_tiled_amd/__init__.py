@@ -4,6 +4,7 @@ Argument marshalling only: every step of the product runs in the library's HIP
 kernels.  The functions keep the C names (``dmu_gemm``, ``dmu_gemm_check``,
 ``dmu_gemm_ex``, ``dmu_gemm_ex_check``, ``dmu_attention``, ``dmu_attention_check``,
 ``dmu_gemm_streamk``, ``dmu_gemm_streamk_workspace_size``, ``dmu_gemm_streamk_error``,
+``dmu_gemm_streamk_noalloc``,
 ``dmu_gemm_kernel_name``,
 ``dmu_device_info``, ``dmu_status_string``, ``dmu_last_error``, ``dmu_probe``, ``dmu_probe_info``);
 ``gemm_args`` and ``epilogue_args`` fill the argument structs from torch tensors
@@ -129,6 +130,7 @@ def _open(path):
     lib.dmu_gemm_streamk.argtypes, lib.dmu_gemm_streamk.restype = [P, PE, vp, ctypes.c_size_t, vp], i32
     lib.dmu_gemm_streamk_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.dmu_gemm_streamk_workspace_size.restype = i32
+    lib.dmu_gemm_streamk_noalloc.argtypes, lib.dmu_gemm_streamk_noalloc.restype = [P, PE, vp], i32
     lib.dmu_gemm_streamk_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int)]
     lib.dmu_gemm_streamk_error.restype = i32
     lib.dmu_gemm_kernel_name.argtypes, lib.dmu_gemm_kernel_name.restype = [P], ctypes.c_char_p
@@ -245,9 +247,24 @@ def dmu_gemm_streamk(args: dmu_gemm_args, ep: dmu_epilogue | None, workspace, wo
     return st
 
 
+# Bytes of the scratch array the library holds on each GPU for dmu_gemm_streamk_noalloc.
+DMU_STREAMK_SCRATCH_BYTES = 33 * 1024 * 1024
+
+
+def dmu_gemm_streamk_noalloc(args: dmu_gemm_args, ep: dmu_epilogue | None, stream=None, check: bool = True) -> int:
+    """The stream-K schedule of D = epilogue(A*B + C) on the library's own scratch (no workspace,
+    no allocation; calls that overlap in time on one GPU race)."""
+    st = _load().dmu_gemm_streamk_noalloc(ctypes.byref(args), None if ep is None else ctypes.byref(ep),
+                                          _stream(stream))
+    if check and st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return st
+
+
 def dmu_gemm_streamk_error(workspace, stream=None, check: bool = True) -> bool:
     """Whether a wait inside an earlier dmu_gemm_streamk call on ``workspace`` gave up (that
-    call's D is then wrong, and the workspace must be zero-filled again).  Waits for
+    call's D is then wrong, and the workspace must be zero-filled again); ``workspace`` None
+    asks about the last dmu_gemm_streamk_noalloc call on the current device.  Waits for
     ``stream``.  With ``check`` a failed wait raises DmuError."""
     failed = ctypes.c_int(0)
     st = _load().dmu_gemm_streamk_error(_addr(workspace), _stream(stream), ctypes.byref(failed))

@@ -11,9 +11,21 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/dmu.h"
 #include "dmu_host.hpp"
+
+// ---------------------------------------------------------------------------
+// Library-held scratch of dmu_gemm_streamk_noalloc: the stream-K workspace
+// (error word, flags, partial-sum slots) in a file-scope device array, so that
+// callers that cannot allocate (code under graph capture, tight serving loops)
+// still get the schedule.  Each GPU holds its own copy, at its own address,
+// until the process ends.  In host code the array's name is only a stand-in:
+// its device address is asked for once per device (hipGetSymbolAddress, with
+// that device current) and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[DMU_STREAMK_SCRATCH_BYTES];
 
 namespace dmu {
 
@@ -579,6 +591,40 @@ bool workspace_overlaps(const dmu_gemm_args *a, const void *ws, size_t bytes)
     return false;
 }
 
+// Device address of the library scratch (the file-scope array above) on each device.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char *g_scratch[MAX_DEVICES]; // device address of `scratch` per device (nullptr: not asked yet)
+
+int scratch_of_current_device(const char *who, char **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        set_error("%s: no current HIP device", who);
+        return DMU_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_error("%s: address of the library scratch: %s", who, hipGetErrorString(e));
+            return DMU_ERR_HIP;
+        }
+        g_scratch[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch[dev];
+    return DMU_OK;
+}
+
+// Zeroes n 32-bit words (a kernel rather than hipMemsetAsync, so that the call
+// can be captured into a graph).
+__global__ void __launch_bounds__(256) zero_words(uint32_t *w, uint32_t n)
+{
+    for (uint32_t i = threadIdx.x; i < n; i += 256)
+        w[i] = 0;
+}
+
 } // namespace
 } // namespace dmu
 
@@ -688,17 +734,66 @@ extern "C" int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *e
     return DMU_OK;
 }
 
+extern "C" int dmu_gemm_streamk_noalloc(const dmu_gemm_args *args, const dmu_epilogue *ep, void *stream)
+{
+    clear_error();
+    Plan plan;
+    int rc = validate(args, &plan);
+    if (rc == DMU_OK)
+        rc = validate_epilogue(args, ep, &plan);
+    if (rc != DMU_OK || !plan.launch)
+        return rc;
+    SkLayout sk;
+    if ((rc = sk_layout(&plan, args, &sk)) != DMU_OK)
+        return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (sk.workers == 0) { // the data-parallel kernel: no scratch
+        if ((rc = persist_layout(&plan, args)) != DMU_OK)
+            return rc;
+        e = launch_plan(plan, s);
+    } else {
+        if (sk.bytes > (size_t)DMU_STREAMK_SCRATCH_BYTES) {
+            set_error("dmu_gemm_streamk_noalloc: the schedule needs %zu bytes of scratch, more than the "
+                      "library's %zu (use dmu_gemm_streamk with a workspace)",
+                      sk.bytes, (size_t)DMU_STREAMK_SCRATCH_BYTES);
+            return DMU_ERR_UNSUPPORTED;
+        }
+        char *w = nullptr;
+        if ((rc = scratch_of_current_device("dmu_gemm_streamk_noalloc", &w)) != DMU_OK)
+            return rc;
+        // the error word and the flags start at zero: a failed earlier call may have left them set
+        const uint32_t nwords = (uint32_t)(sk.partials_off / 4);
+        hipLaunchKernelGGL(zero_words, dim3(1), dim3(256), 0, s, reinterpret_cast<uint32_t *>(w), nwords);
+        e = hipGetLastError();
+        if (e == hipSuccess)
+            e = launch_plan_sk(plan, sk_params(sk, w), s);
+    }
+    if (e != hipSuccess) {
+        set_error("dmu_gemm_streamk_noalloc: launch of %s failed: %s", plan.name, hipGetErrorString(e));
+        return DMU_ERR_HIP;
+    }
+    return DMU_OK;
+}
+
 extern "C" int dmu_gemm_streamk_error(const void *workspace, void *stream, int *failed)
 {
     clear_error();
-    if (!failed || !workspace) {
-        set_error("dmu_gemm_streamk_error: NULL %s", failed ? "workspace" : "failed");
+    if (!failed) {
+        set_error("dmu_gemm_streamk_error: NULL failed");
         return DMU_ERR_INVALID_ARG;
     }
     *failed = 0;
     if ((uintptr_t)workspace % 256) {
         set_error("dmu_gemm_streamk_error: workspace is not 256-byte aligned");
         return DMU_ERR_INVALID_ARG;
+    }
+    if (!workspace) { // the library scratch of dmu_gemm_streamk_noalloc on the current device
+        char *w = nullptr;
+        const int rc = scratch_of_current_device("dmu_gemm_streamk_error", &w);
+        if (rc != DMU_OK)
+            return rc;
+        workspace = w;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint32_t word = 0;

@@ -226,12 +226,37 @@ int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *ep, void *wo
  * of those calls; NULL is the default stream), then reads the workspace's
  * error word: *failed = 1 if it is set, else 0.  The word stays set until the
  * caller zero-fills the workspace.  `workspace` is a device pointer, 256-byte
- * aligned; `failed` a host pointer owned by the caller.  Returns DMU_OK,
- * DMU_ERR_INVALID_ARG for a NULL or misaligned pointer (before any HIP call),
- * or DMU_ERR_HIP if the copy or the synchronisation fails.
+ * aligned, or NULL for the library scratch of dmu_gemm_streamk_noalloc on the
+ * current device (the last such call's word); `failed` a host pointer owned
+ * by the caller.  Returns DMU_OK, DMU_ERR_INVALID_ARG for a NULL `failed` or a
+ * misaligned workspace (before any HIP call), or DMU_ERR_HIP if the copy or
+ * the synchronisation fails.
  */
 int dmu_gemm_streamk_error(const void *workspace, void *stream, int *failed);
 
+/*
+ * dmu_gemm_streamk without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * schedule's error word, flags and partial sums live in a scratch array that
+ * the library holds in device memory, DMU_STREAMK_SCRATCH_BYTES on each GPU it
+ * runs on, until the process ends.  Same arguments, validation, choice of
+ * schedule and results as dmu_gemm_streamk (bit for bit: the same kernels on
+ * the same workspace layout).  Each call first clears the scratch's error word
+ * and flags with a small kernel on `stream` (no hipMemsetAsync, so the call can
+ * be captured), then runs the schedule.  The first call on a device asks the
+ * runtime for that device's address of the array.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (several streams, several host threads) race and give wrong
+ * results; serialise them (one stream) or use dmu_gemm_streamk with separate
+ * workspaces.  dmu_gemm_streamk_error(NULL, stream, &failed) reports whether
+ * the last call's waits gave up.
+ * Returns DMU_ERR_UNSUPPORTED when the schedule would need more than
+ * DMU_STREAMK_SCRATCH_BYTES (more than 256 workers of 256 x 128 tiles); no
+ * memory is allocated on any path.  Otherwise as dmu_gemm_streamk.
+ */
+#define DMU_STREAMK_SCRATCH_BYTES (33u * 1024u * 1024u)
+int dmu_gemm_streamk_noalloc(const dmu_gemm_args *args, const dmu_epilogue *ep, void *stream);
 
 /* Workspace bytes dmu_gemm_streamk needs for these arguments on the current
  * device (the worker count is the device's compute-unit count, at most the
