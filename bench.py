@@ -14,7 +14,7 @@ medians of individually timed launches, warm and cold (a 1 GiB buffer written
 before each), and the dense peak re-derived from this machine's compute units
 and clock.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5dq|c6|lk|lksk|c4fa]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4s|c4o|c5|c5nn|c5dq|c6|lk|lksk|c4fa]
                   [--no-cpu-baseline] [--copy-calibration MiB]
   python bench.py --summarize DIR [--workload W] [--bench-line FILE]   (rocprofv3 output -> profiles/)
 """
@@ -42,6 +42,7 @@ WORKLOAD_NAMES = {
     "c4s": "batched32_gemm_4096x4096x128_f16_tn_f32out",
     "c4o": "batched32_gemm_4096x128x4096_f16_nn_f32out",
     "c5": "gemm_8192x8192x8192_i8_tn_i32out",
+    "c5nn": "gemm_8192x8192x8192_i8_nn_i32out",
     "c6": "gemm_8192x8192x8192_e4m3_tn_f32acc_bf16out",
     "lk": "gemm_1024x1024x16384_bf16_nn_f32acc_bf16out",
     "lksk": "gemm_1024x1024x16384_bf16_nn_f32acc_bf16out_streamk",
@@ -376,6 +377,75 @@ def copy_calibration(args, torch):
         torch.cuda.synchronize()
 
 
+PHASE_LOG_RECORDS = 1 << 16
+
+
+def run_phases(args, launch, stream, dmu, torch, np, kernel) -> int:
+    """Log `args.phases` back-to-back launches (after the warm-up), each into its own phase log,
+    with HIP events around each on the launch stream, and write each launch's event time and span
+    and the raw records of the median-span launch to `args.phases_file`."""
+    logs = [torch.zeros(PHASE_LOG_RECORDS * 8, dtype=torch.int64, device="cuda:0") for _ in range(args.phases)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in logs]
+    counts = []
+    torch.cuda.synchronize()
+    try:
+        for log, (e0, e1) in zip(logs, ev):
+            dmu.dmu_phase_log(log, PHASE_LOG_RECORDS)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            counts.append(dmu.dmu_phase_log_last())
+    finally:
+        dmu.dmu_phase_log(None, 0)
+    torch.cuda.synchronize()
+    cus, _ = dmu.dmu_device_info(0)
+    out = {"workload": WORKLOAD_NAMES[args.workload], "kernel": kernel, "source_digest": source_digest(args.workload),
+           "compute_units": cus, "warmup": args.warmup, "launches": []}
+    for log, (e0, e1), (n, kind) in zip(logs, ev, counts):
+        recs = log.view(-1, 8)[:n].cpu().numpy().view(np.uint64)
+        span = int(recs[:, 3].max()) - int(recs[:, 0].min()) if n else 0
+        out["launches"].append({"event_us": e0.elapsed_time(e1) * 1e3, "kind": kind, "n": int(n),
+                                "span_ticks": span, "recs": recs})
+    # only the median-span launch keeps its records (the others: event time and span)
+    order = sorted(range(len(out["launches"])), key=lambda i: out["launches"][i]["span_ticks"])
+    out["median_launch"] = order[len(order) // 2]
+    for i, L in enumerate(out["launches"]):
+        recs = L.pop("recs")
+        if i == out["median_launch"]:
+            L["records"] = [[int(x) for x in r] for r in recs]
+    path = args.phases_file
+    if os.path.dirname(path):
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(out, fh)
+    from dense_matrix_unit_tiled_amd import profiling
+    best = profiling.median_launch(out)
+    print(json.dumps(profiling.phase_summary(best["records"], best["kind"], cus, best["event_us"])), flush=True)
+    return 0
+
+
+def summarize_phases(path: str, workload: str) -> int:
+    """profiles/phases_<workload name>.{json,md} from a --phases output file."""
+    from dense_matrix_unit_tiled_amd import profiling
+    raw = json.load(open(path))
+    if raw["workload"] != WORKLOAD_NAMES[workload]:
+        print(f"bench.py: {path} holds {raw['workload']}, not {WORKLOAD_NAMES[workload]}", file=sys.stderr)
+        return 2
+    best = profiling.median_launch(raw)
+    summ = profiling.phase_summary(best["records"], best["kind"], raw["compute_units"], best["event_us"])
+    summ.update(workload=raw["workload"], kernel=raw["kernel"], source_digest=raw["source_digest"],
+                launches_logged=len(raw["launches"]))
+    base = os.path.join(ROOT, "profiles", f"phases_{raw['workload']}")
+    with open(base + ".json", "w") as fh:
+        json.dump(summ, fh, indent=1)
+    cmd = (f"python3 bench.py --workload {workload} --phases {len(raw['launches'])} --warmup {raw['warmup']} "
+           f"--phases-file {path}")
+    with open(base + ".md", "w") as fh:
+        fh.write(profiling.phase_markdown(raw["workload"], raw["kernel"], cmd, summ))
+    print(json.dumps(summ))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +457,13 @@ def main() -> int:
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="summarize rocprofv3 output under DIR into profiles/ and exit")
+    ap.add_argument("--phases", type=int, default=0, metavar="N",
+                    help="after the warm-up, log N back-to-back launches' per-workgroup phase "
+                         "timestamps into --phases-file and exit")
+    ap.add_argument("--phases-file", metavar="FILE", default="phases.json",
+                    help="output of --phases (raw records of the median-span launch)")
+    ap.add_argument("--summarize-phases", metavar="FILE", default=None,
+                    help="summarize a --phases output file into profiles/ and exit")
     ap.add_argument("--bench-line", metavar="FILE", default=None,
                     help="with --summarize: the output of a plain bench.py run of the workload in the same "
                          "session, kept beside the summaries")
@@ -408,6 +485,8 @@ def main() -> int:
                                   timed=200, bench_line=line)
         print(json.dumps(res))
         return 0
+    if args.summarize_phases:
+        return summarize_phases(args.summarize_phases, args.workload)
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
               file=sys.stderr)
@@ -424,6 +503,9 @@ def main() -> int:
         return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to("cuda:0")
 
     if args.workload in ATTENTION_WORKLOADS:
+        if args.phases:
+            print("bench.py: the phase log covers the GEMM kernels, not attention", file=sys.stderr)
+            return 2
         return run_attention(args, dmu, workloads, torch, np, to_dev)
 
     ep = None
@@ -460,6 +542,8 @@ def main() -> int:
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
+    if args.phases:
+        return run_phases(args, launch, stream, dmu, torch, np, kernel)
     lt = launch_times(launch, stream, torch)
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -138,6 +138,9 @@ def _open(path):
     lib.dmu_device_info.restype = i32
     lib.dmu_status_string.argtypes, lib.dmu_status_string.restype = [i32], ctypes.c_char_p
     lib.dmu_last_error.argtypes, lib.dmu_last_error.restype = [], ctypes.c_char_p
+    lib.dmu_phase_log.argtypes, lib.dmu_phase_log.restype = [vp, ctypes.c_size_t], i32
+    lib.dmu_phase_log_last.argtypes = [ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int)]
+    lib.dmu_phase_log_last.restype = i32
     lib.dmu_probe.argtypes, lib.dmu_probe.restype = [i32, vp, vp, vp, vp], i32
     ip = ctypes.POINTER(ctypes.c_int)
     lib.dmu_probe_info.argtypes, lib.dmu_probe_info.restype = [i32, ip, ip, ip, ip, ip], i32
@@ -316,6 +319,24 @@ def dmu_device_info(device: int = 0):
     if st != DMU_OK:
         raise DmuError(st, dmu_last_error())
     return cu.value, khz.value
+
+
+def dmu_phase_log(log, records: int) -> None:
+    """Point every following GEMM launch of the process at a phase log: a device buffer of
+    ``records`` x 8 uint64 (tensor or address), or None and 0 to turn it off.  Raises DmuError."""
+    st = _load().dmu_phase_log(_addr(log), records)
+    if st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+
+
+def dmu_phase_log_last():
+    """(records, kind) of the last GEMM launch's phase log; kind 0 none, 1 one record per
+    workgroup, 2 one per tile of the persistent kernel, 3 one per stream-K worker."""
+    n, kind = ctypes.c_size_t(), ctypes.c_int()
+    st = _load().dmu_phase_log_last(ctypes.byref(n), ctypes.byref(kind))
+    if st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return n.value, kind.value
 
 
 def dmu_status_string(status: int) -> str:

@@ -53,7 +53,8 @@ enum Dt { F16 = 1, BF16 = 2, F32 = 3, I8 = 4, I32 = 5, E4M3 = 6 };
 enum Mode {
     KC16 = 0, // K contiguous, 16-byte-aligned rows, K a multiple of 16 bytes
     KCD = 1,  // K contiguous, 4-byte-aligned rows, any K: 16-byte loads, K tail masked
-    MC16 = 2  // M (or N) contiguous, 16-byte-aligned rows, M (N) a multiple of 8
+    MC16 = 2, // M (or N) contiguous, 16-byte-aligned rows, M (N) a multiple of 8
+    MC8 = 3   // 8-bit, N contiguous (row-major B), 16-byte-aligned rows, N a multiple of 16
 };
 
 // Bytes of one element of a type code.
@@ -273,7 +274,47 @@ struct GemmParams {
     int64_t stride_rs, stride_cs, stride_bias;  // floats between batch slices
     int32_t act;                                // 0 none, 1 ReLU, 2 tanh-GELU
     int32_t epi;                                // 1 if any of rs, cs, bias is present
+    uint64_t *phases;                           // phase log (diagnostics), NULL: off
 };
+
+// ---------------------------------------------------------------------------
+// Phase log (diagnostics, off unless the host passes a log).  Thread 0 of each
+// workgroup writes one record of 8 64-bit words with plain vector stores: the
+// chip's 100 MHz constant clock (s_memrealtime) at the start, after the main
+// loop, after the stream-K partial sums (= after the main loop elsewhere) and
+// after the epilogue (or the partial store); the shader clock counter
+// (s_memtime) at start and end; HW_ID and XCC_ID; the workgroup id and the
+// K-tiles the record covers.  With a NULL log each call is one scalar branch.
+// ---------------------------------------------------------------------------
+enum PhaseSlot { PH_START = 0, PH_LOOP = 1, PH_FIX = 2, PH_END = 3, PH_CLK0 = 4, PH_CLK1 = 5, PH_HWID = 6, PH_WHO = 7 };
+
+__device__ __forceinline__ void phase_begin(uint64_t *log, uint32_t rec, uint32_t ktiles)
+{
+    if (log != nullptr && threadIdx.x == 0) {
+        uint64_t *r = log + (size_t)rec * 8;
+        r[PH_START] = __builtin_amdgcn_s_memrealtime();
+        r[PH_CLK0] = __builtin_amdgcn_s_memtime();
+        const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID, bits 0-31
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20); // XCC_ID, bits 0-31
+        r[PH_HWID] = hw | ((uint64_t)xcc << 32);
+        r[PH_WHO] = blockIdx.x | ((uint64_t)ktiles << 32);
+    }
+}
+
+__device__ __forceinline__ void phase_mark(uint64_t *log, uint32_t rec, int slot)
+{
+    if (log != nullptr && threadIdx.x == 0)
+        log[(size_t)rec * 8 + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
+__device__ __forceinline__ void phase_end(uint64_t *log, uint32_t rec)
+{
+    if (log != nullptr && threadIdx.x == 0) {
+        uint64_t *r = log + (size_t)rec * 8;
+        r[PH_END] = __builtin_amdgcn_s_memrealtime();
+        r[PH_CLK1] = __builtin_amdgcn_s_memtime();
+    }
+}
 
 // Workspace of the stream-K kernel (dmu_streamk.hpp).
 struct StreamKParams {

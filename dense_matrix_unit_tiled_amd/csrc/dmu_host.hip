@@ -90,18 +90,18 @@ const char *const COMBO_NAMES[NUM_COMBOS] = {"f16_f32", "f16_f16", "bf16_bf16", 
 
 // Names of every kernel variant, built once (thread-safe static init).
 struct NameTable {
-    char at[NUM_TILE_CFGS][3][3][NUM_COMBOS][48];
+    char at[NUM_TILE_CFGS][4][4][NUM_COMBOS][48];
 };
 
 const NameTable &kernel_names()
 {
     static const NameTable table = [] {
         static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64", "256x256w4"};
-        static const char *const MODE_NAMES[] = {"k16", "kd", "t16"};
+        static const char *const MODE_NAMES[] = {"k16", "kd", "t16", "t8"};
         NameTable t;
         for (int a = 0; a < NUM_TILE_CFGS; ++a)
-            for (int x = 0; x < 3; ++x)
-                for (int y = 0; y < 3; ++y)
+            for (int x = 0; x < 4; ++x)
+                for (int y = 0; y < 4; ++y)
                     for (int c = 0; c < NUM_COMBOS; ++c)
                         snprintf(t.at[a][x][y][c], sizeof(t.at[a][x][y][c]), "mfma_%s_%s_%s_%s", TILE_NAMES[a],
                                  a == TILE_GENERIC ? "any" : MODE_NAMES[x], a == TILE_GENERIC ? "any" : MODE_NAMES[y],
@@ -134,8 +134,9 @@ bool aligned(const void *p, int64_t ld, int64_t stride, int esz, int vb)
 }
 
 // Load mode of one operand: -1 if only the generic kernel can read it.
-//  kc: K is the contiguous dimension; mn: the operand's M (or N) size.
-int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, int64_t K, int64_t mn)
+//  kc: K is the contiguous dimension; mn: the operand's M (or N) size;
+//  is_b: the operand is B (the 8-bit transposed layout serves B only).
+int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, int64_t K, int64_t mn, bool is_b)
 {
     if (kc) {
         if (aligned(p, ld, stride, esz, 16) && (K * esz) % 16 == 0)
@@ -146,6 +147,8 @@ int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, in
     }
     if (esz == 2 && aligned(p, ld, stride, esz, 16) && mn % 8 == 0)
         return MC16;
+    if (esz == 1 && is_b && aligned(p, ld, stride, esz, 16) && mn % 16 == 0)
+        return MC8;
     return -1;
 }
 
@@ -243,8 +246,8 @@ int validate(const dmu_gemm_args *a, Plan *plan)
 
     // kernel selection
     const bool a_kc = a->layout_a == DMU_ROW_MAJOR, b_kc = a->layout_b == DMU_COL_MAJOR;
-    int amode = K > 0 ? operand_mode(a_kc, a->A, a->lda, batch > 1 ? a->stride_a : 0, esz, K, M) : -1;
-    int bmode = K > 0 ? operand_mode(b_kc, a->B, a->ldb, batch > 1 ? a->stride_b : 0, esz, K, N) : -1;
+    int amode = K > 0 ? operand_mode(a_kc, a->A, a->lda, batch > 1 ? a->stride_a : 0, esz, K, M, false) : -1;
+    int bmode = K > 0 ? operand_mode(b_kc, a->B, a->ldb, batch > 1 ? a->stride_b : 0, esz, K, N, true) : -1;
     if (amode >= 0 && extent(a->layout_a, M, K, a->lda) * esz >= ((int64_t)1 << 31))
         amode = -1; // slice too large for one buffer descriptor
     if (bmode >= 0 && extent(a->layout_b, K, N, a->ldb) * esz >= ((int64_t)1 << 31))
@@ -277,6 +280,8 @@ int validate(const dmu_gemm_args *a, Plan *plan)
         if (env && strcmp(env, "128x128") == 0) tile = TILE_128x128;
         if (a->in_type == DMU_E4M3 && (tile == TILE_256x256 || tile == TILE_256x256W4))
             tile = TILE_256x128; // e4m3 fragments need the registers of a 64 x 64 wavefront tile
+        if (a->in_type == DMU_I8 && tile == TILE_256x256W4)
+            tile = TILE_256x256; // the four-wavefront tile is built for 16-bit inputs only
     }
     const int64_t bm = tile_bm(tile), bn = tile_bn(tile);
     const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
@@ -617,6 +622,43 @@ int scratch_of_current_device(const char *who, char **out)
     return DMU_OK;
 }
 
+// Phase log (diagnostics): the caller's device buffer, written by every GEMM
+// launch of the process while set (dmu_phase_log).
+std::mutex g_phase_mu;
+uint64_t *g_phase_log = nullptr;
+size_t g_phase_cap = 0;  // records the buffer holds
+size_t g_phase_last = 0; // records the last launch wrote
+int g_phase_kind = 0;    // how they are indexed (dmu_phase_log_last)
+
+// Points the launch at the phase log if one is set: one record per workgroup of
+// the one-per-tile kernel, per tile of the persistent kernel or per stream-K
+// worker (`sk_workers` > 0); none for the fallback.
+int phase_attach(Plan *plan, uint32_t sk_workers, const char *who)
+{
+    std::lock_guard<std::mutex> lock(g_phase_mu);
+    plan->p.phases = nullptr;
+    if (!g_phase_log)
+        return DMU_OK;
+    size_t n = 0;
+    int kind = 0;
+    if (sk_workers > 0) {
+        n = sk_workers;
+        kind = 3;
+    } else if (plan->cfg.tile != TILE_GENERIC) {
+        n = plan->p.total_tiles;
+        kind = plan->cfg.workers > 0 ? 2 : 1;
+    }
+    if (n > g_phase_cap) {
+        set_error("%s: the launch writes %zu phase records, the log holds %zu", who, n, g_phase_cap);
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (n > 0)
+        plan->p.phases = g_phase_log;
+    g_phase_last = n;
+    g_phase_kind = kind;
+    return DMU_OK;
+}
+
 // Zeroes n 32-bit words (a kernel rather than hipMemsetAsync, so that the call
 // can be captured into a graph).
 __global__ void __launch_bounds__(256) zero_words(uint32_t *w, uint32_t n)
@@ -667,6 +709,8 @@ extern "C" int dmu_gemm_ex(const dmu_gemm_args *args, const dmu_epilogue *ep, vo
         return rc;
     if ((rc = persist_layout(&plan, args)) != DMU_OK)
         return rc;
+    if ((rc = phase_attach(&plan, 0, "dmu_gemm")) != DMU_OK)
+        return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e = launch_plan(plan, s);
     if (e != hipSuccess) {
@@ -715,6 +759,8 @@ extern "C" int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *e
     if (sk.workers == 0) { // the fallback kernel, or K == 0: the data-parallel launch
         if ((rc = persist_layout(&plan, args)) != DMU_OK)
             return rc;
+        if ((rc = phase_attach(&plan, 0, "dmu_gemm_streamk")) != DMU_OK)
+            return rc;
         e = launch_plan(plan, s);
     } else {
         if (!workspace || ((uintptr_t)workspace % 256) || workspace_bytes < sk.bytes) {
@@ -725,6 +771,8 @@ extern "C" int dmu_gemm_streamk(const dmu_gemm_args *args, const dmu_epilogue *e
             set_error("dmu_gemm_streamk: the workspace overlaps an operand");
             return DMU_ERR_INVALID_ARG;
         }
+        if ((rc = phase_attach(&plan, sk.workers, "dmu_gemm_streamk")) != DMU_OK)
+            return rc;
         e = launch_plan_sk(plan, sk_params(sk, static_cast<char *>(workspace)), s);
     }
     if (e != hipSuccess) {
@@ -751,6 +799,8 @@ extern "C" int dmu_gemm_streamk_noalloc(const dmu_gemm_args *args, const dmu_epi
     if (sk.workers == 0) { // the data-parallel kernel: no scratch
         if ((rc = persist_layout(&plan, args)) != DMU_OK)
             return rc;
+        if ((rc = phase_attach(&plan, 0, "dmu_gemm_streamk_noalloc")) != DMU_OK)
+            return rc;
         e = launch_plan(plan, s);
     } else {
         if (sk.bytes > (size_t)DMU_STREAMK_SCRATCH_BYTES) {
@@ -759,6 +809,8 @@ extern "C" int dmu_gemm_streamk_noalloc(const dmu_gemm_args *args, const dmu_epi
                       sk.bytes, (size_t)DMU_STREAMK_SCRATCH_BYTES);
             return DMU_ERR_UNSUPPORTED;
         }
+        if ((rc = phase_attach(&plan, sk.workers, "dmu_gemm_streamk_noalloc")) != DMU_OK)
+            return rc;
         char *w = nullptr;
         if ((rc = scratch_of_current_device("dmu_gemm_streamk_noalloc", &w)) != DMU_OK)
             return rc;
@@ -805,6 +857,38 @@ extern "C" int dmu_gemm_streamk_error(const void *workspace, void *stream, int *
         return DMU_ERR_HIP;
     }
     *failed = word != 0;
+    return DMU_OK;
+}
+
+extern "C" int dmu_phase_log(void *device_log, size_t records)
+{
+    clear_error();
+    if ((device_log == nullptr) != (records == 0)) {
+        set_error("dmu_phase_log: a log needs both a buffer and a record count (NULL and 0 turn it off)");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if ((uintptr_t)device_log % 8) {
+        set_error("dmu_phase_log: the log is not 8-byte aligned");
+        return DMU_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_phase_mu);
+    g_phase_log = static_cast<uint64_t *>(device_log);
+    g_phase_cap = records;
+    g_phase_last = 0;
+    g_phase_kind = 0;
+    return DMU_OK;
+}
+
+extern "C" int dmu_phase_log_last(size_t *records, int *kind)
+{
+    clear_error();
+    if (!records || !kind) {
+        set_error("dmu_phase_log_last: NULL output");
+        return DMU_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_phase_mu);
+    *records = g_phase_last;
+    *kind = g_phase_kind;
     return DMU_OK;
 }
 

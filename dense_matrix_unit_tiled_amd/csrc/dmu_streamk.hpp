@@ -69,8 +69,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     const uint32_t w = xcd_remap(sk.workers, blockIdx.x); // consecutive ranges share an XCD
     const uint32_t nk = sk.nk;
     const uint32_t s0 = streamk_start(sk, w), e0 = streamk_start(sk, w + 1);
-    if (s0 >= e0)
+    phase_begin(p.phases, w, e0 > s0 ? e0 - s0 : 0u);
+    if (s0 >= e0) {
+        phase_mark(p.phases, w, PH_LOOP);
+        phase_mark(p.phases, w, PH_FIX);
+        phase_end(p.phases, w);
         return; // more workers than iterations
+    }
 
     const uint32_t t_lo = s0 / nk, t_hi = (e0 - 1) / nk;
     for (uint32_t t = t_hi + 1; t-- > t_lo;) {
@@ -91,8 +96,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         uint32_t tid_e = threadIdx.x; // the lane arithmetic of what follows, afresh
         asm volatile("" : "+v"(tid_e));
         const uint32_t lane = tid_e & 63u, wave = __builtin_amdgcn_readfirstlane(tid_e >> 6);
+        phase_mark(p.phases, w, PH_LOOP);
 
         if ((uint32_t)ke < nk) {
+            phase_mark(p.phases, w, PH_FIX);
             // not the finisher: the leading part of tile t, for a higher worker
             G::store_partial(sk.partials + (size_t)w * G::PARTIAL_BYTES, acc, lane, wave);
             // each wavefront's device-coherent stores have completed, then the flag
@@ -124,10 +131,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
                 }
             }
             __syncthreads(); // every wavefront is done with the stages before the parking
+            phase_mark(p.phases, w, PH_FIX);
             G::epilogue(p, tc, acc, smem, lane, wave);
         }
         __syncthreads(); // the next tile's prologue overwrites the stages
     }
+    phase_end(p.phases, w);
 }
 
 } // namespace dmu

@@ -231,10 +231,80 @@ template <int R, int NW> struct McTile {
     }
 };
 
+// ---------------------------------------------------------------------------
+// M/N-contiguous 8-bit operand (row-major int8 or e4m3 B): the 128 K-rows of a
+// K-tile, R bytes each, K-row k at byte k (R + 16) + 128 (k / 16).  A fragment
+// (16 columns, 16 consecutive k of one 64-k half) is two ds_read_b64_tr_b8:
+// within each group of 16 lanes, if lane j addresses X[k0 + j / 2][c0 + 8 (j %
+// 2) .. +7], lane i receives X[k0 .. k0 + 7][c0 + i] (pinned by the layout
+// probe).
+//   reads   lane l (group g = l / 16) reads K-row 64 h + 16 g + (l % 16) / 2 (+ 8
+//           for the second read): the 16-byte pitch excess puts the eight K-rows
+//           of a group in eight different 16-byte slots of a 256-byte bank line,
+//           and the 128 bytes added after every 16 K-rows move the next group
+//           (16 K-rows on) to the other eight slots, so lanes l and l + 16
+//           never share a bank; only lanes 32 apart do.
+//   writes  eight consecutive lanes put 128 consecutive bytes of one K-row.
+// Every offset is a per-lane base plus a constant, as in the unswizzled tile.
+// ---------------------------------------------------------------------------
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+template <int R, int NW> struct McTile8 {
+    static_assert(R == 128 || R == 256, "transposed tile of 128 or 256 values");
+    static constexpr int P = R + 16;      // K-row pitch within a block of 16 K-rows
+    static constexpr int CPR = R / 16;    // 16-byte chunks per K-row
+    static constexpr int RPI = 64 / CPR;  // K-rows per 1 KiB transfer
+    static constexpr int NL = R / (8 * NW);
+    static_assert(NL * 8 * NW == R, "whole 1 KiB transfers per wavefront");
+    static constexpr uint32_t BYTES = 128 * P + 8 * 128;
+    static __device__ __forceinline__ uint32_t row(uint32_t k) { return k * P + (k >> 4) * 128; }
+    uint32_t voff;     // K-row l / CPR, chunk l % CPR; OOB for columns past N
+    uint32_t wofs[NL]; // LDS byte offset of each staging write
+    uint32_t first;    // byte offset of the wavefront's first K-row
+    uint32_t xstep;    // bytes between the first K-rows of consecutive transfers
+    uint32_t kstep;    // bytes per K-tile (128 K-rows)
+    __device__ __forceinline__ void init(int64_t ld_bytes, int64_t mn_valid, uint32_t wave, uint32_t lane)
+    {
+        const uint32_t chunk = lane % CPR;
+        voff = (int64_t)(16 * chunk) < mn_valid ? (lane / CPR) * (uint32_t)ld_bytes + chunk * 16 : OOB;
+        first = wave * NL * RPI * (uint32_t)ld_bytes;
+        xstep = RPI * (uint32_t)ld_bytes;
+        kstep = 128 * (uint32_t)ld_bytes;
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            wofs[i] = row((wave * NL + i) * RPI + lane / CPR) + chunk * 16;
+    }
+    __device__ __forceinline__ u32x4 load(int i, __amdgpu_buffer_rsrc_t r, int kt, uint32_t) const
+    {
+        return load16s(r, voff, first + (uint32_t)i * xstep + (uint32_t)kt * kstep);
+    }
+    __device__ __forceinline__ void store(int i, char *tile, uint32_t, uint32_t, u32x4 v, int, uint32_t) const
+    {
+        *reinterpret_cast<u32x4 *>(tile + wofs[i]) = v;
+    }
+    __device__ __forceinline__ void store_raw(int i, char *tile, uint32_t, u32x4 v) const
+    {
+        *reinterpret_cast<u32x4 *>(tile + wofs[i]) = v;
+    }
+    // Columns [c0, c0 + 16), k = 64 h + 16 (l / 16) + 0..15 (h: the 64-k half of
+    // the K-tile -- the K-step of the int8 instruction, or one of the two
+    // 16-byte operand halves of the e4m3 one): lane l gets column c0 + l % 16.
+    // The second read's K-rows (k + 8) lie in the same block of 16.
+    static __device__ __forceinline__ u32x4 frag(const char *tile, uint32_t c0, uint32_t h, uint32_t lane)
+    {
+        const uint32_t g = lane >> 4, j = lane & 15u;
+        const uint32_t a0 = row(64 * h + 16 * g + (j >> 1)) + c0 + 8 * (j & 1u);
+        const uint32_t a1 = a0 + 8 * P;
+        const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(tile + a0));
+        const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(tile + a1));
+        return u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
+    }
+};
+
 template <int MODE, int R, int NW> struct TileOf;
 template <int R, int NW> struct TileOf<KC16, R, NW> { typedef KcTile<R, NW, false> type; };
 template <int R, int NW> struct TileOf<KCD, R, NW> { typedef KcTile<R, NW, true> type; };
 template <int R, int NW> struct TileOf<MC16, R, NW> { typedef McTile<R, NW> type; };
+template <int R, int NW> struct TileOf<MC8, R, NW> { typedef McTile8<R, NW> type; };
 
 // ---------------------------------------------------------------------------
 // Epilogue through LDS for 16 x 16 tiles: each 16-row stripe of the
@@ -312,7 +382,7 @@ __device__ __forceinline__ void store_interior(const GemmParams &p, const AccT (
     typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
     typedef st st4 __attribute__((ext_vector_type(4)));
     typedef ot ov4 __attribute__((ext_vector_type(4)));
-    const uint32_t col = K::rd_chunk(lane) * 4, r0 = K::rd_row(lane);
+    const uint32_t r0 = K::rd_row(lane);
     float csv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, bv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, rsv[MT][K::ITS];
     if constexpr (EPI) {
 #pragma unroll
@@ -366,7 +436,7 @@ __device__ __forceinline__ void store_edge_plain(const GemmParams &p, const AccT
     typedef typename std::remove_const<typename std::remove_reference<decltype(acc[0][0][0])>::type>::type st;
     typedef st st4 __attribute__((ext_vector_type(4)));
     typedef ot ov4 __attribute__((ext_vector_type(4)));
-    const uint32_t col = K::rd_chunk(lane) * 4, r0 = K::rd_row(lane);
+    const uint32_t r0 = K::rd_row(lane);
     const bool vec = p.d_vec4 && n + 3 < p.N;
     const int nv = n >= p.N ? 0 : (p.N - n < 4 ? (int)(p.N - n) : 4); // valid elements of this lane's vector
     ot *D0 = reinterpret_cast<ot *>(Db) + (m_base + r0) * p.ldd + n;
@@ -529,6 +599,8 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     static_assert(MT % 2 == 0, "a K-step runs in two halves of the tile rows");
     static_assert(AMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(BMODE != MC16 || E == 2, "transposed operands are 16-bit");
+    static_assert(BMODE != MC8 || E == 1, "the 8-bit transposed layout takes 8-bit operands");
+    static_assert(AMODE != MC8, "an 8-bit transposed A goes through the fallback");
     static_assert(!F8 || MN <= 16, "e4m3 fragments (8 registers per tile) fit beside the accumulators");
     static_assert(!AG || !F8, "the four-wavefront tile takes the 16-bit and int8 instructions");
     typedef typename Mfma<T>::acc_t acc_t;
@@ -564,7 +636,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         const char *Ab = p.A + (int64_t)tc.b * p.stride_a * E;
         const char *Bb = p.B + (int64_t)tc.b * p.stride_b * E;
         const int64_t a_start = AMODE != MC16 ? m0 * p.lda * E : m0 * E;
-        const int64_t b_start = BMODE != MC16 ? n0 * p.ldb * E : n0 * E;
+        const int64_t b_start = (BMODE == MC16 || BMODE == MC8) ? n0 * E : n0 * p.ldb * E;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)((p.a_bytes - a_start + 3) & ~3ll));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)((p.b_bytes - b_start + 3) & ~3ll));
         ATile ta;
@@ -573,7 +645,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
             ta.init(p.lda * E, p.M - m0, wave, lane);
         else
             ta.init(p.lda * E, wave, lane);
-        if constexpr (BMODE == MC16)
+        if constexpr (BMODE == MC16 || BMODE == MC8)
             tb.init(p.ldb * E, p.N - n0, wave, lane);
         else
             tb.init(p.ldb * E, wave, lane);
@@ -606,7 +678,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     const char *Ab = p.A + (int64_t)tc.b * p.stride_a * E;
     const char *Bb = p.B + (int64_t)tc.b * p.stride_b * E;
     const int64_t a_start = AMODE != MC16 ? m0 * p.lda * E : m0 * E;
-    const int64_t b_start = BMODE != MC16 ? n0 * p.ldb * E : n0 * E;
+    const int64_t b_start = (BMODE == MC16 || BMODE == MC8) ? n0 * E : n0 * p.ldb * E;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)((p.a_bytes - a_start + 3) & ~3ll));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)((p.b_bytes - b_start + 3) & ~3ll));
 
@@ -616,7 +688,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         ta.init(p.lda * E, p.M - m0, wave, lane);
     else
         ta.init(p.lda * E, wave, lane);
-    if constexpr (BMODE == MC16)
+    if constexpr (BMODE == MC16 || BMODE == MC8)
         tb.init(p.ldb * E, p.N - n0, wave, lane);
     else
         tb.init(p.ldb * E, wave, lane);
@@ -920,6 +992,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
     typename G::acc_t acc[G::MT][G::NT];
     const int nk = (int)(((int64_t)p.K * G::E + 127) / 128);
+    phase_begin(p.phases, blockIdx.x, (uint32_t)nk);
     if constexpr (!G::AG) {
 #pragma unroll
         for (int i = 0; i < G::MT; ++i)
@@ -944,7 +1017,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     uint32_t wg2 = blockIdx.x, tid2 = threadIdx.x;
     asm volatile("" : "+s"(wg2));
     asm volatile("" : "+v"(tid2));
+    phase_mark(p.phases, wg2, PH_LOOP);
+    phase_mark(p.phases, wg2, PH_FIX);
     G::epilogue(p, tile_of(p, wg2), acc, smem, tid2 & 63u, __builtin_amdgcn_readfirstlane(tid2 >> 6));
+    phase_end(p.phases, wg2);
 }
 
 
@@ -971,6 +1047,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     if (nk > 0)
         G::prefetch(p, tile_of(p, t), 0, st, threadIdx.x);
     for (; t < total; t += W) {
+        phase_begin(p.phases, t, (uint32_t)nk);
         typename G::acc_t acc[G::MT][G::NT];
 #pragma unroll
         for (int i = 0; i < G::MT; ++i)
@@ -984,9 +1061,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         uint32_t tid_e = threadIdx.x, t2 = t;
         asm volatile("" : "+v"(tid_e));
         asm volatile("" : "+s"(t2));
+        phase_mark(p.phases, t2, PH_LOOP);
         if (nk > 0 && t2 + W < total)
             G::prefetch(p, tile_of(p, t2 + W), 0, st, tid_e);
+        phase_mark(p.phases, t2, PH_FIX);
         G::epilogue(p, tile_of(p, t2), acc, smem, tid_e & 63u, __builtin_amdgcn_readfirstlane(tid_e >> 6));
+        phase_end(p.phases, t2);
         __syncthreads(); // every wavefront is done with its park before the next tile's stages
     }
 }

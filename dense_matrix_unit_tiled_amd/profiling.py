@@ -28,6 +28,7 @@ import csv
 import glob
 import json
 import os
+import statistics
 from collections import defaultdict
 
 COPY_MIB = 256
@@ -200,3 +201,110 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
     if "traffic_bytes_per_launch" in result:
         json.dump(result, open(os.path.join(profiles, f"traffic_{workload_name}.json"), "w"), indent=1)
     return result
+
+
+# ---------------------------------------------------------------------------
+# Phase log: per-workgroup timestamps that the kernels write while a log is set
+# (dmu_phase_log).  One record of 8 64-bit words per workgroup (per tile for the
+# persistent kernel, per worker for stream-K):
+#   0 start, 1 end of the main loop, 2 end of the partial-sum additions (stream-K
+#   finisher; = 1 elsewhere), 3 end of the epilogue or of the partial store
+#   -- the chip's 100 MHz constant clock (s_memrealtime), as wavefront 0 sees them;
+#   4 start, 5 end -- the shader clock counter (s_memtime);
+#   6 HW_ID (low word) and XCC_ID (high word) of wavefront 0;
+#   7 workgroup id (low word) and K-tiles of the record (high word).
+# ---------------------------------------------------------------------------
+REALTIME_HZ = 100e6
+PHASE_KINDS = {1: "one workgroup per tile", 2: "persistent (one record per tile)",
+               3: "stream-K (one record per worker)"}
+
+
+def median_launch(raw: dict) -> dict:
+    """The launch of a --phases file whose span (first start to last end) is the median one: the
+    only launch whose records the file keeps."""
+    return raw["launches"][raw["median_launch"]]
+
+
+def phase_summary(log, kind: int, compute_units: int, launch_us: float | None = None) -> dict:
+    """Figures of one launch's phase log (`log`: n records of 8 unsigned 64-bit words, as
+    written by the kernel): span from the first start to the last end, start skew, per-record
+    main loop / partial-sum / epilogue durations (min, median, max), the compute-unit time the
+    records cover against compute units x span, the shader clock over each record (s_memtime
+    ticks over s_memrealtime time), and the records per XCD.  Pure host arithmetic."""
+    recs = [[int(x) for x in r] for r in log]
+    if not recs:
+        raise ValueError("empty phase log")
+    t0 = min(r[0] for r in recs)
+    us = lambda ticks: ticks / REALTIME_HZ * 1e6
+    start = [us(r[0] - t0) for r in recs]
+    loop = [us(r[1] - r[0]) for r in recs]
+    fix = [us(r[2] - r[1]) for r in recs]
+    epi = [us(r[3] - r[2]) for r in recs]
+    end = [us(r[3] - t0) for r in recs]
+    dur = [e - s for s, e in zip(start, end)]
+    span = max(end)
+    clk = [(r[5] - r[4]) / (us(r[3] - r[0]) * 1e3) for r in recs if r[3] > r[0]]
+    xcd = defaultdict(list)
+    for k, r in enumerate(recs):
+        xcd[(r[6] >> 32) & 0xF].append(k)
+    stat = lambda v: {"min": round(min(v), 3), "median": round(statistics.median(v), 3), "max": round(max(v), 3)}
+    # when the records run in one wave of at most one per compute unit, the compute-unit time
+    # they leave unused is compute units x span minus the time they cover
+    covered = sum(dur)
+    out = {
+        "records": len(recs),
+        "kind": PHASE_KINDS.get(kind, str(kind)),
+        "span_us": round(span, 3),
+        "start_skew_us": round(max(start), 3),
+        "duration_us": stat(dur),
+        "main_loop_us": stat(loop),
+        "partial_sums_us": stat(fix),
+        "epilogue_us": stat(epi),
+        "tail_us": round(span - statistics.median(end), 3),
+        "cu_time_covered": round(covered / (compute_units * span), 4),
+        "shader_clock_ghz": stat(clk) if clk else None,
+        "records_per_xcd": {x: len(v) for x, v in sorted(xcd.items())},
+        "per_xcd": {x: {"main_loop_median_us": round(statistics.median(loop[k] for k in v), 3),
+                        "end_max_us": round(max(end[k] for k in v), 3),
+                        "shader_clock_ghz_median": round(statistics.median(
+                            (recs[k][5] - recs[k][4]) / (us(recs[k][3] - recs[k][0]) * 1e3) for k in v), 3)
+                        if all(recs[k][3] > recs[k][0] for k in v) else None}
+                    for x, v in sorted(xcd.items())},
+    }
+    if launch_us is not None:
+        out["launch_us"] = round(launch_us, 3)
+        out["outside_span_us"] = round(launch_us - span, 3)
+    return out
+
+
+def phase_markdown(workload_name: str, kernel: str, command: str, s: dict) -> str:
+    """The committed summary of a phase breakdown."""
+    f = lambda d: f"{d['min']:.2f} / {d['median']:.2f} / {d['max']:.2f}"
+    lines = [f"# Phase breakdown: {workload_name}", "",
+             f"Kernel `{kernel}`, {s['records']} records ({s['kind']}), one launch at steady clock "
+             "(the median-span launch of those timed).", "",
+             "Command (from the repository root on the GPU host):", "", "```", command, "```", "",
+             "| phase | µs (min / median / max over records) |", "|---|---|",
+             f"| whole record (start to end) | {f(s['duration_us'])} |",
+             f"| main loop (prologue loads and every K-tile) | {f(s['main_loop_us'])} |",
+             f"| partial sums (stream-K finisher) | {f(s['partial_sums_us'])} |",
+             f"| epilogue (or partial store) | {f(s['epilogue_us'])} |", "",
+             "| launch-wide | value |", "|---|---|",
+             f"| span, first start to last end | {s['span_us']:.2f} µs |",
+             f"| start skew (last start after first) | {s['start_skew_us']:.2f} µs |",
+             f"| tail (last end after the median end) | {s['tail_us']:.2f} µs |",
+             f"| compute-unit time covered / (units x span) | {s['cu_time_covered']:.3f} |"]
+    if "launch_us" in s:
+        lines.append(f"| event-timed launch | {s['launch_us']:.2f} µs |")
+        lines.append(f"| launch time outside the span | {s['outside_span_us']:.2f} µs |")
+    if s.get("shader_clock_ghz"):
+        lines.append(f"| shader clock over a record (min / median / max) | {f(s['shader_clock_ghz'])} GHz |")
+    lines.append(f"| records per XCD | {s['records_per_xcd']} |")
+    lines += ["", "| XCD | main loop median (µs) | last end (µs) | shader clock median (GHz) |", "|---|---|---|---|"]
+    for x, v in s["per_xcd"].items():
+        clk = "—" if v["shader_clock_ghz_median"] is None else f"{v['shader_clock_ghz_median']:.3f}"
+        lines.append(f"| {x} | {v['main_loop_median_us']:.2f} | {v['end_max_us']:.2f} | {clk} |")
+    lines += ["", "Timestamps: the 100 MHz constant clock (10 ns steps) read by wavefront 0 of each "
+              "workgroup at its start, after its main loop, after the stream-K partial sums and after "
+              "its epilogue; the shader clock counter at start and end.", ""]
+    return "\n".join(lines)

@@ -120,6 +120,15 @@ def test_empty_problems_launch_nothing():
           out_type="f16", acc_type="f16"), "mfma_256x256_kd_kd_f16_f16"),
     (dict(M=8192, N=8192, K=8192, lda=8192, layout_b="col", ldb=8192, ldd=8192, in_type="i8",
           out_type="i32"), "mfma_256x256_k16_k16_i8_i32"),
+    # 8-bit row-major B: the 8-bit transposed LDS layout when N is a multiple of 16, else the fallback
+    (dict(M=8192, N=8192, K=8192, lda=8192, ldb=8192, ldd=8192, in_type="i8", out_type="i32"),
+     "mfma_256x256_k16_t8_i8_i32"),
+    (dict(M=8192, N=8184, K=8192, lda=8192, ldb=8184, ldd=8184, in_type="i8", out_type="i32"),
+     "mfma_generic64_any_any_i8_i32"),
+    (dict(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096, in_type="e4m3", out_type="bf16",
+          acc_type="f32"), "mfma_256x128_k16_t8_e4m3_bf16"),
+    (dict(M=4096, N=4096, K=4096, lda=4096, layout_a="col", ldb=4096, ldd=4096, in_type="i8",
+          out_type="i32"), "mfma_generic64_any_any_i8_i32"),   # an 8-bit column-major A
     (dict(M=4096, N=128, K=4096, lda=4096, ldb=128, ldd=128, batch=32, stride_a=4096 * 4096,
           stride_b=4096 * 128, stride_d=4096 * 128), "mfma_256x128_k16_t16_f16_f32"),
     # two K-tiles or fewer: 256 x 128 even with enough tiles for 256 x 256; four: 256 x 256
@@ -257,7 +266,8 @@ TN8 = dict(layout_b="col", in_type="e4m3")
     (dict(out_type="f32", **TN8), "mfma_128x128_k16_k16_e4m3_f32"),
     (dict(K=200, lda=200, ldb=200, out_type="f16", **TN8), "mfma_128x128_kd_kd_e4m3_f16"),
     (dict(K=130, lda=130, ldb=130, out_type="f32", **TN8), "mfma_generic64_any_any_e4m3_f32"),
-    (dict(in_type="e4m3", out_type="f32"), "mfma_generic64_any_any_e4m3_f32"),  # B row-major
+    (dict(in_type="e4m3", out_type="f32"), "mfma_128x128_k16_t8_e4m3_f32"),  # B row-major: 8-bit transposed
+    (dict(in_type="e4m3", out_type="f32", N=250, ldb=250, ldd=250), "mfma_generic64_any_any_e4m3_f32"),
     (dict(M=4096, N=128, K=4096, lda=4096, ldb=4096, ldd=128, out_type="f32", **TN8),
      "mfma_256x128_k16_k16_e4m3_f32"),
 ])
@@ -308,3 +318,34 @@ def test_streamk_error_query_argument_errors_before_any_hip_call():
     assert failed.value == 0
     with pytest.raises(dmu.DmuError):
         dmu.dmu_gemm_streamk_error(FAKE + 4, stream=0)
+
+
+def test_phase_log_argument_errors():
+    """The phase log takes a buffer with a count, or NULL with 0; checked before any HIP call."""
+    lib = dmu.library()
+    assert lib.dmu_phase_log(None, 4) == dmu.DMU_ERR_INVALID_ARG
+    assert "record count" in dmu.dmu_last_error()
+    assert lib.dmu_phase_log(ctypes.c_void_p(1 << 40), 0) == dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_phase_log(ctypes.c_void_p((1 << 40) + 4), 4) == dmu.DMU_ERR_INVALID_ARG
+    assert "aligned" in dmu.dmu_last_error()
+    assert lib.dmu_phase_log(None, 0) == dmu.DMU_OK
+    n, k = ctypes.c_size_t(7), ctypes.c_int(7)
+    assert lib.dmu_phase_log_last(None, ctypes.byref(k)) == dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_phase_log_last(ctypes.byref(n), None) == dmu.DMU_ERR_INVALID_ARG
+    assert dmu.dmu_phase_log_last() == (0, 0)
+
+
+def test_phase_log_capacity_checked_before_launch(monkeypatch):
+    """A launch that would write more records than the log holds fails before any HIP call
+    (the log is never dereferenced on the host; the problem's 64 tiles need 64 records)."""
+    monkeypatch.setenv("DMU_PERSIST", "never")  # no device query for the persistent choice
+    fake = 1 << 40
+    a = dmu.gemm_args(1024, 1024, 256, fake, 256, fake + (1 << 36), 256, fake + (2 << 36), 1024,
+                      in_type="bf16", out_type="bf16", layout_a="row", layout_b="col")
+    assert dmu.dmu_gemm_kernel_name(a).startswith("mfma_128x128")
+    dmu.dmu_phase_log(fake + (3 << 36), 63)
+    try:
+        assert dmu.library().dmu_gemm(ctypes.byref(a), None) == dmu.DMU_ERR_INVALID_ARG
+        assert "64 phase records" in dmu.dmu_last_error()
+    finally:
+        dmu.dmu_phase_log(None, 0)

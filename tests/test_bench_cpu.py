@@ -184,3 +184,19 @@ def test_committed_trace_not_slower_than_its_session_bench(cfg):
     b = rec["bench_same_session"]
     assert b["kernel"] == rec["kernel"]
     assert rec["avg_us"] <= b["ms_per_step"] * 1e3 * 1.01
+
+
+@pytest.mark.parametrize("cfg", sorted(bench.WORKLOAD_NAMES))
+def test_committed_phase_breakdowns_match_current_kernels(cfg):
+    """A committed phase breakdown was logged on the current device code and kernel, and its
+    text summary gives the command that made it."""
+    base = os.path.join(bench.ROOT, "profiles", f"phases_{bench.WORKLOAD_NAMES[cfg]}")
+    if not os.path.exists(base + ".json"):
+        pytest.skip(f"no phase breakdown for {cfg}")
+    rec = json.load(open(base + ".json"))
+    assert rec["source_digest"] == bench.source_digest(cfg)
+    assert rec["kernel"] == bench.kernel_for(cfg)
+    assert rec["main_loop_us"]["min"] <= rec["main_loop_us"]["median"] <= rec["main_loop_us"]["max"]
+    assert rec["span_us"] <= rec["launch_us"]
+    text = open(base + ".md").read()
+    assert f"bench.py --workload {cfg} --phases" in text

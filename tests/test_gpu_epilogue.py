@@ -49,6 +49,8 @@ def test_every_form_on_every_tile(tile, cfg, out_t):
     not, no activation / ReLU / GELU) for wavefront blocks inside D and another path for
     blocks on the M/N edge: every form, on each tiled configuration, on a problem with
     both kinds of block, element by element against the oracle."""
+    if tile == "256x256w4" and cfg == "c5":
+        pytest.skip("the four-wavefront tile is built for 16-bit inputs")
     for with_c in (False, True):
         p = problem(cfg, out_t, 21, with_c=with_c, M=600, N=560, K=192)
         for vectors in (False, True):

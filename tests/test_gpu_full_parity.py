@@ -6,7 +6,7 @@ reference), through the C ABI, in the launch configuration the benchmark times:
   out): all outputs against the full oracle product, to the stated tolerance;
 * the batched attention-shaped pair (batch 32): the whole batched call, then one full batch
   slice (the last, whose operands sit furthest from the base pointers) against the oracle;
-* 8192^3 int8: bit-exact by an exact Freivalds check -- D x = A (B x) in int64 for three
+* 8192^3 int8 (B column- and row-major): bit-exact by an exact Freivalds check -- D x = A (B x) in int64 for three
   random integer vectors x, which a single wrong element fails with probability at least
   1 - 1/2048 per vector (the full oracle product, 1.1 T multiply-adds, would take minutes).
 
@@ -60,11 +60,15 @@ def test_last_batch_slice_every_output(cfg):
     gu.assert_close(got, want, s, where=gu.valid_mask(s))
 
 
-def test_int8_full_size_freivalds():
-    p = workloads.make("c5", "random", 0)
+@pytest.mark.parametrize("cfg", ["c5", "c5nn"])
+def test_int8_full_size_freivalds(cfg):
+    p = workloads.make(cfg, "random", 0)
     got = gu.run_dmu(p).astype(np.int64).reshape(p.M, p.ldd)[:, : p.N]
     A = p.A.reshape(p.M, p.lda)[:, : p.K].astype(np.int64)   # row-major M x K
-    Bt = p.B.reshape(p.N, p.ldb)[:, : p.K].astype(np.int64)  # column-major B: row j holds B(:, j)
+    if p.layout_b == "col":
+        Bt = p.B.reshape(p.N, p.ldb)[:, : p.K].astype(np.int64)  # column-major B: row j holds B(:, j)
+    else:
+        Bt = p.B.reshape(p.K, p.ldb)[:, : p.N].astype(np.int64).T  # row-major B
     rng = np.random.default_rng([5, 99])
     for _ in range(3):
         x = rng.integers(-1024, 1024, p.N).astype(np.int64)

@@ -26,6 +26,7 @@ REDUCED = {
     "c4s": dict(M=300, N=260, K=128, batch=3),
     "c4o": dict(M=300, N=128, K=520, batch=2),
     "c5": dict(M=300, N=260, K=384),
+    "c5nn": dict(M=300, N=272, K=384),   # int8 with a row-major B: the 8-bit transposed layout
 }
 KERNELS = [None, "256x256", "256x256w4", "128x128", "256x128", "generic"]
 
@@ -37,8 +38,12 @@ def test_reduced_random_parity(cfg, kernel):
     got, name = gu.run_dmu(p, force=kernel, return_name=True)
     if kernel == "generic":
         assert "generic" in name
+    elif kernel == "256x256w4" and p.in_type == "i8":
+        assert "mfma_256x256_" in name, name  # the four-wavefront tile is built for 16-bit inputs
     elif kernel is not None and cfg != "c3":
         assert kernel in name, name
+    if cfg == "c5nn" and kernel != "generic":
+        assert "_t8_" in name, name
     want = gu.run_oracle(p)
     gu.assert_close(got, want, p, where=gu.valid_mask(p))
 
@@ -76,7 +81,7 @@ def as_values(p, flat):
     return out
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4s", "c4o", "c5"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4s", "c4o", "c5", "c5nn"])
 def test_full_size_structured_exact(cfg):
     p = workloads.make(cfg, "structured")
     got = as_values(p, gu.run_dmu(p))
@@ -85,7 +90,7 @@ def test_full_size_structured_exact(cfg):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4s", "c4o", "c5"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4s", "c4o", "c5", "c5nn"])
 def test_full_size_random_sampled(cfg):
     p = workloads.make(cfg, "random", 0)
     got = gu.run_dmu(p)
@@ -98,14 +103,16 @@ def test_full_size_random_sampled(cfg):
 def test_tiled_equals_fallback_bitwise(kernel):
     """Every output element goes through the same K-step sequence of the same matrix
     instruction in each tiled form and in the fallback: bit-identical results."""
-    for cfg in ("c2", "c3", "c4s", "c5"):
+    for cfg in ("c2", "c3", "c4s", "c5", "c5nn"):
+        if kernel == "256x256w4" and cfg.startswith("c5"):
+            continue  # 16-bit inputs only
         p = workloads.make(cfg, "random", 3, **REDUCED[cfg])
         a = gu.run_dmu(p, force=kernel)
         b = gu.run_dmu(p, force="generic")
         gu.assert_bits_equal(a, b, where=gu.valid_mask(p))
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c3", "c5"])
+@pytest.mark.parametrize("cfg", ["c2", "c3"])
 def test_four_wavefront_tile_full_size(cfg):
     """The four-wavefront 256 x 256 tile (accumulators in AGPRs) on the full problems: structured
     inputs bit for bit against their closed forms, random inputs on sampled outputs."""

@@ -7,8 +7,8 @@ the stage, long before the next K-tile's data lands there.  The stage ring's arg
 ("Tensor Cores, CUTLASS and CuTe" section 4.3: a stage is overwritten only after the
 barrier that follows its last reads) is then checked by the data: any fragment read that
 strays past its barrier feeds poison into D.  Every tiled form (eight and four wavefronts,
-both 16-bit LDS layouts, masked K tails, int8, e4m3, the persistent and the stream-K
-schedules) must give the product build's bits exactly, and meet the oracle's bar."""
+the 16-bit and 8-bit transposed LDS layouts, masked K tails, int8, e4m3, the persistent and
+the stream-K schedules) must give the product build's bits exactly, and meet the oracle's bar."""
 import os
 
 import numpy as np
@@ -28,7 +28,8 @@ CASES = [
     ("c3", dict(M=300, N=270, K=1030), "256x256"),    # fp16 -> fp16, 4-byte rows, masked K tail
     ("c3", dict(M=300, N=270, K=1030), "256x128"),
     ("c5", dict(M=300, N=260, K=1024), "256x256"),    # int8
-    ("c5", dict(M=300, N=260, K=1024), "256x256w4"),
+    ("c5nn", dict(M=300, N=272, K=1024), "256x256"),  # int8, B row-major: the 8-bit transposed layout
+    ("c5nn", dict(M=300, N=272, K=1024), "128x128"),
     ("c6", dict(M=300, N=260, K=1024), "256x128"),    # e4m3
     ("c6", dict(M=300, N=260, K=1024), "128x128"),
     ("c4o", dict(M=300, N=128, K=1024, batch=2), None),

@@ -158,6 +158,43 @@ def test_lds_read_tr16_mapping():
         assert np.array_equal(got[lane], X[kk:kk + 4, lane % 16]), lane
 
 
+def test_lds_read_tr8_mapping():
+    """ds_read_b64_tr_b8: within each group of 16 lanes, the 16 addressed 8-byte rows are read
+    transposed byte-wise: if lane j addresses X[k0 + j / 2][n0 + 8 (j % 2) .. +7] of a K x N
+    row-major byte tile, output lane i holds X[k0 .. k0+7][n0 + i] -- eight consecutive k of one
+    column, half of an int8 / e4m3 operand fragment of the 16 x 16 x 64 instruction."""
+    import torch
+
+    out = torch.zeros(64 * 2, dtype=torch.int32, device="cuda:0")
+    # (a) lane j addresses its own 8 bytes: the raw permutation.  Within group g the addressed
+    # bytes lie in [128 g, 128 g + 128), so a byte's value (its position mod 256) names it.
+    img = (np.arange(4096) % 256).astype(np.uint8)
+    addr = (np.arange(64) * 8).astype(np.int32)
+    dmu.dmu_probe(dmu.DMU_PROBE_LDS_READ_TR8, gu.to_dev(img), gu.to_dev(addr), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint8).reshape(64, 8)
+    src = []
+    for l in range(64):
+        g = l // 16
+        pos = [128 * g + ((int(v) - 128 * g) % 256) for v in got[l]]
+        src.append([(p // 8, p % 8) for p in pos])
+    want = [[(16 * (l // 16) + 2 * e + (l % 16) // 8, l % 8) for e in range(8)] for l in range(64)]
+    table = "\n".join(f"lane {l:2d}: {src[l]}" for l in range(64))
+    assert src == want, "observed (src lane, src byte) per output byte:\n" + table
+    # (b) the operand use: a 32 x 128 row-major byte tile
+    X = (np.arange(32 * 128) * 7 % 251).astype(np.uint8).reshape(32, 128)
+    g = np.arange(64) // 16
+    j = np.arange(64) % 16
+    k0, n0 = 8 * g, 16 * g
+    addr = ((k0 + j // 2) * 128 + n0 + 8 * (j % 2)).astype(np.int32)
+    dmu.dmu_probe(dmu.DMU_PROBE_LDS_READ_TR8, gu.to_dev(X.reshape(-1)), gu.to_dev(addr), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint8).reshape(64, 8)
+    for lane in range(64):
+        kk, nn = 8 * (lane // 16), 16 * (lane // 16) + lane % 16
+        assert np.array_equal(got[lane], X[kk:kk + 8, nn]), lane
+
+
 def test_lds_fragment_format():
     """The tiled kernel's staging writes + fragment reads of a K-contiguous tile return,
     for lane l, row block rb and K-step ks, bytes 64*ks + 16*(l/16) .. +15 of logical
