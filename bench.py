@@ -33,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 # MI355X published dense peaks (matrix cores), TFLOP/s or TOP/s, and HBM3E bandwidth.
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "i8": 5000.0, "e4m3": 5000.0}
+# dense matrix-core FLOP (OP) per clock and compute unit of gfx950, by input type
+DENSE_FLOP_PER_CLOCK_PER_CU = {"bf16": 4096, "f16": 4096, "i8": 8192, "e4m3": 8192}
 PEAK_HBM_GBS = 8000.0
 
 WORKLOAD_NAMES = {
@@ -96,6 +98,25 @@ def stored_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None."""
     rec = stored_record(workload, kernel)
     return None if rec is None else rec.get("traffic_bytes_per_launch")
+
+
+def stored_phases(workload: str, kernel: str):
+    """The committed phase breakdown of a workload (profiles/phases_<workload>.json) in brief --
+    span, median shader clock over the workgroups (s_memtime), the matrix-core busy fraction at
+    that clock -- or None when there is none or it was logged on other device code or another
+    kernel."""
+    path = os.path.join(ROOT, "profiles", f"phases_{WORKLOAD_NAMES[workload]}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_digest") != source_digest(workload) or rec.get("kernel") != kernel:
+        return None
+    clk = rec.get("shader_clock_ghz") or {}
+    return {"span_us": rec["span_us"], "main_loop_median_us": rec["main_loop_us"]["median"],
+            "epilogue_median_us": rec["epilogue_us"]["median"], "shader_clock_ghz": clk.get("median"),
+            "mfma_busy_at_shader_clock": rec.get("mfma_busy_at_shader_clock"),
+            "source": f"profiles/phases_{WORKLOAD_NAMES[workload]}.json (dmu_phase_log, device-code digest "
+                      f"{rec['source_digest']})"}
 
 
 def stored_counters(workload: str, kernel: str):
@@ -435,6 +456,13 @@ def summarize_phases(path: str, workload: str) -> int:
     summ = profiling.phase_summary(best["records"], best["kind"], raw["compute_units"], best["event_us"])
     summ.update(workload=raw["workload"], kernel=raw["kernel"], source_digest=raw["source_digest"],
                 launches_logged=len(raw["launches"]))
+    import workloads
+    base = EPILOGUE_WORKLOADS.get(workload, (STREAMK_WORKLOADS.get(workload, workload),))[0]
+    M, N, K, batch, in_t = workloads.FULL[base][:5]
+    if summ.get("shader_clock_ghz"):
+        summ["mfma_busy_at_shader_clock"] = round(profiling.mfma_busy_at_clock(
+            2.0 * M * N * K * batch, DENSE_FLOP_PER_CLOCK_PER_CU[in_t], raw["compute_units"], summ["span_us"],
+            summ["shader_clock_ghz"]["median"]), 4)
     base = os.path.join(ROOT, "profiles", f"phases_{raw['workload']}")
     with open(base + ".json", "w") as fh:
         json.dump(summ, fh, indent=1)
@@ -583,8 +611,9 @@ def main() -> int:
                    "batch": p.batch, "layout_a": p.layout_a, "layout_b": p.layout_b,
                    "in_type": p.in_type, "acc_type": p.acc_type, "out_type": p.out_type,
                    "kernel": kernel, "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": roofline(flops, algorithmic_bytes(p, ep_bytes), ms * 1e-3, peak, traffic,
-                             stored_counters(args.workload, kernel)),
+        "roofline": dict(roofline(flops, algorithmic_bytes(p, ep_bytes), ms * 1e-3, peak, traffic,
+                                  stored_counters(args.workload, kernel)),
+                         phase_log=stored_phases(args.workload, kernel)),
         "launch_times": lt,
         "peak_derived": peak_derived(dmu, p.in_type),
     }

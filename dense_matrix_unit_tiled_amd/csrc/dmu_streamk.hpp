@@ -57,6 +57,22 @@ __device__ __forceinline__ uint32_t streamk_owner(const StreamKParams &sk, uint3
     return i < big ? i / (sk.q + 1) : sk.r + (i - big) / sk.q;
 }
 
+// Thread 0 of a finisher waits (bounded) for worker v's flag and clears it.  A
+// wait that gives up sets the error word and leaves the flag as the late worker
+// leaves it: the error word tells the caller to clear the workspace again.
+__device__ __forceinline__ void wait_flag(const StreamKParams &sk, uint32_t v)
+{
+    uint32_t n = 0;
+    while (__hip_atomic_load(&sk.flags[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        __builtin_amdgcn_s_sleep(4);
+        if (++n >= sk.spin_limit) {
+            __hip_atomic_store(sk.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+    }
+    __hip_atomic_store(&sk.flags[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
 __global__ void __launch_bounds__(64 * WGM * WGN)
     __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_streamk(GemmParams p, StreamKParams sk)
@@ -109,25 +125,30 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
                 __hip_atomic_store(&sk.flags[w], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             if (kb > 0) { // the lower workers that hold K-tiles [0, kb) of this tile
-                for (uint32_t v = streamk_owner(sk, ts); v < w; ++v) {
+                // Their partials are added in increasing worker order (the same bits on
+                // every run), a whole slot per round trip -- two slots at once when the
+                // registers allow it (up to 32 accumulator registers per slot).
+                constexpr uint32_t STEP = G::MT * G::NT <= 8 ? 2u : 1u;
+                for (uint32_t v = streamk_owner(sk, ts); v < w; v += STEP) {
+                    const bool two = STEP == 2 && v + 1 < w;
                     if (tid == 0) {
-                        uint32_t n = 0;
-                        bool seen = true;
-                        while (__hip_atomic_load(&sk.flags[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                            __builtin_amdgcn_s_sleep(4);
-                            if (++n >= sk.spin_limit) {
-                                __hip_atomic_store(sk.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                                seen = false;
-                                break;
-                            }
-                        }
-                        // a flag that was never seen stays as the late worker leaves it: the
-                        // error word tells the caller to clear the workspace again
-                        if (seen)
-                            __hip_atomic_store(&sk.flags[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        wait_flag(sk, v);
+                        if (two)
+                            wait_flag(sk, v + 1);
                     }
-                    __syncthreads(); // the device-coherent loads below are issued after the flag was seen
-                    G::add_partial(sk.partials + (size_t)v * G::PARTIAL_BYTES, acc, lane, wave);
+                    __syncthreads(); // the device-coherent loads below are issued after the flags were seen
+                    acc_t x[G::MT][G::NT];
+                    G::load_partial(sk.partials + (size_t)v * G::PARTIAL_BYTES, x, lane, wave);
+                    if constexpr (STEP == 2) {
+                        acc_t y[G::MT][G::NT];
+                        if (two)
+                            G::load_partial(sk.partials + (size_t)(v + 1) * G::PARTIAL_BYTES, y, lane, wave);
+                        G::add_into(acc, x);
+                        if (two)
+                            G::add_into(acc, y);
+                    } else {
+                        G::add_into(acc, x);
+                    }
                 }
             }
             __syncthreads(); // every wavefront is done with the stages before the parking

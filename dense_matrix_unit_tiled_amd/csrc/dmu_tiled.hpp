@@ -962,24 +962,26 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r, lane * 16,
                                                        ((wave * MT + i) * NT + j) * 1024, SC1);
     }
-    // (one row of tiles at a time: the loads of all of them would need as many
-    // registers as the accumulators)
-    static __device__ __forceinline__ void add_partial(const char *slot, acc_t (&acc)[MT][NT], uint32_t lane,
-                                                       uint32_t wave)
+    // A whole slot into registers: every load is issued before any is used, since
+    // each round trip to the coherence point costs about a microsecond.
+    static __device__ __forceinline__ void load_partial(const char *slot, acc_t (&v)[MT][NT], uint32_t lane,
+                                                        uint32_t wave)
     {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, PARTIAL_BYTES);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            acc_t v[NT];
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                v[j] = __builtin_bit_cast(acc_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     r, lane * 16, ((wave * MT + i) * NT + j) * 1024, SC1));
+                v[i][j] = __builtin_bit_cast(acc_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        r, lane * 16, ((wave * MT + i) * NT + j) * 1024, SC1));
+    }
+    static __device__ __forceinline__ void add_into(acc_t (&acc)[MT][NT], const acc_t (&v)[MT][NT])
+    {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                acc[i][j] += v[j];
-            __builtin_amdgcn_sched_barrier(0);
-        }
+                acc[i][j] += v[i][j];
     }
 };
 

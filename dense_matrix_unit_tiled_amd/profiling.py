@@ -225,6 +225,14 @@ def median_launch(raw: dict) -> dict:
     return raw["launches"][raw["median_launch"]]
 
 
+def mfma_busy_at_clock(flops: float, flop_per_clock_per_cu: float, compute_units: int, span_us: float,
+                       clock_ghz: float) -> float:
+    """Matrix-core busy fraction over a launch's span at a given shader clock: the clocks the
+    dense matrix cores need for `flops` (flops / (units x dense FLOP per clock and unit)) over the
+    clocks in the span."""
+    return flops / (compute_units * flop_per_clock_per_cu) / (span_us * 1e-6 * clock_ghz * 1e9)
+
+
 def phase_summary(log, kind: int, compute_units: int, launch_us: float | None = None) -> dict:
     """Figures of one launch's phase log (`log`: n records of 8 unsigned 64-bit words, as
     written by the kernel): span from the first start to the last end, start skew, per-record
@@ -299,6 +307,9 @@ def phase_markdown(workload_name: str, kernel: str, command: str, s: dict) -> st
         lines.append(f"| launch time outside the span | {s['outside_span_us']:.2f} µs |")
     if s.get("shader_clock_ghz"):
         lines.append(f"| shader clock over a record (min / median / max) | {f(s['shader_clock_ghz'])} GHz |")
+    if s.get("mfma_busy_at_shader_clock") is not None:
+        lines.append(f"| matrix-core busy over the span at the median shader clock | "
+                     f"{s['mfma_busy_at_shader_clock']:.3f} |")
     lines.append(f"| records per XCD | {s['records_per_xcd']} |")
     lines += ["", "| XCD | main loop median (µs) | last end (µs) | shader clock median (GHz) |", "|---|---|---|---|"]
     for x, v in s["per_xcd"].items():

@@ -200,3 +200,7 @@ def test_committed_phase_breakdowns_match_current_kernels(cfg):
     assert rec["span_us"] <= rec["launch_us"]
     text = open(base + ".md").read()
     assert f"bench.py --workload {cfg} --phases" in text
+    brief = bench.stored_phases(cfg, rec["kernel"])
+    assert brief["span_us"] == rec["span_us"]
+    if rec.get("shader_clock_ghz"):
+        assert 0.0 < brief["mfma_busy_at_shader_clock"] <= 1.0
