@@ -20,13 +20,17 @@
 //               Q's fragments stay in registers for the whole pass.
 //   pipeline    step j computes the scores of block j+1 while block j's
 //               softmax runs (independent work for the matrix core and the
-//               VALU in one region), then O += P V for block j.
+//               VALU in one region) and takes block j+1's row maxima, then
+//               O += P V for block j.
 //   softmax     in base 2 with c = scale log2(e) >= 0 (a negative scale negates
-//               Q instead): per row the running maximum m of c s (across the
-//               four lanes that share the row), p = 2^(c s - m) (one FMA and the
-//               hardware exp2), the running sum l (kept per lane, added up at
-//               the end) and the correction 2^(m_old - m_new) of O and l.  Only
-//               the last block can hold keys past seq_k; they get p = 0.
+//               Q instead): per row a running maximum m of c s (across the four
+//               lanes that share the row), raised only when a block's maximum
+//               passes it by more than 8 -- decided at the start of the block's
+//               step, where the correction 2^(m_old - m_new) of O and l is a
+//               rarely taken branch -- then p = 2^(c s - m) <= 2^8 (one FMA and
+//               the hardware exp2) and the running sum l (kept per lane, added
+//               up at the end).  Only the last block can hold keys past seq_k;
+//               they get p = 0 and no say in its maximum.
 //   O += P V    MFMA(srcA = V^T fragment, srcB = P fragment): P's fragment for 32
 //               keys is the two 16-key accumulator tiles of S, rounded to the
 //               input type and packed -- the V^T fragment is read in the same
@@ -201,12 +205,16 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
                     s[rt][t] = Mfma<T>::step(kf[t], qf[rt][ks], s[rt][t]);
         }
     };
-    // Online softmax of block blk's scores: the running max m and sum l,
-    // O rescaled by 2^(m_old - m_new), P = 2^(c s - m) packed as the operand
-    // of O += P V (tiles 2kk and 2kk+1 of S make P's fragment kk).  Only the
-    // last block can hold keys past seq_k: they get no weight.
-    float corr_[2];           // the last softmax's O correction per row tile
-    auto softmax = [&](f32x4 (&s)[2][4], u32x4 (&pf)[2][2], int blk, auto masked) {
+    // The running maxima m (c times the largest score seen, per row) only rise
+    // when a block's maximum exceeds them by more than TAU (log2 units): the
+    // exponents c s - m of the softmax then stay <= TAU (p <= 2^TAU, well inside
+    // the 16-bit operand formats' range), the softmax itself is unchanged (any m
+    // cancels between O and l), and the rescaling of O and l by 2^(m_old - m_new)
+    // is a branch almost never taken after the first blocks, instead of 64
+    // multiplies per block.
+    constexpr float TAU = 8.0f;
+    float bmx[2]; // c times the maximum score of each row tile of the next block to be exponentiated
+    auto block_max = [&](const f32x4 (&s)[2][4], int blk, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const int key0 = blk * BKEYS + 4 * (int)(lane >> 4);
 #pragma unroll
@@ -217,22 +225,48 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     mx = fmaxf(mx, MASKED && key0 + 16 * t + r >= p.sk ? -INFINITY : s[rt][t][r]);
-            const float m_new = fmaxf(m[rt], row_max4(mx) * c);
-            const float corr = __builtin_amdgcn_exp2f(m[rt] - m_new);
-            m[rt] = m_new;
+            bmx[rt] = row_max4(mx) * c;
+        }
+    };
+    // When any row of the wavefront has bmx > m + TAU, every row takes m = max(m,
+    // bmx) and rescales its O tiles and its sum (one wavefront-uniform branch).
+    auto raise = [&]() {
+        const bool need = bmx[0] > m[0] + TAU || bmx[1] > m[1] + TAU;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const float m_new = fmaxf(m[rt], bmx[rt]);
+                const float corr = __builtin_amdgcn_exp2f(m[rt] - m_new);
+                m[rt] = m_new;
+                l[rt] *= corr;
+#pragma unroll
+                for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o[rt][dt][r] *= corr;
+            }
+        }
+    };
+    // Block blk's P = 2^(c s - m) packed as the operand of O += P V (tiles 2kk
+    // and 2kk+1 of S make P's fragment kk), and its part of the sums l.  Only the
+    // last block can hold keys past seq_k: they get no weight.
+    auto softmax = [&](f32x4 (&s)[2][4], u32x4 (&pf)[2][2], int blk, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const int key0 = blk * BKEYS + 4 * (int)(lane >> 4);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
             float sum = 0.0f;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][t][r], c, -m_new));
+                    float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][t][r], c, -m[rt]));
                     if (MASKED)
                         e = key0 + 16 * t + r < p.sk ? e : 0.0f;
                     s[rt][t][r] = e;
                     sum += e;
                 }
-            l[rt] = l[rt] * corr + sum;
-            corr_[rt] = corr;
+            l[rt] += sum;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 pf[rt][kk] = u32x4{Pack16<T>::two(s[rt][2 * kk][0], s[rt][2 * kk][1]),
@@ -241,7 +275,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
                                    Pack16<T>::two(s[rt][2 * kk + 1][2], s[rt][2 * kk + 1][3])};
         }
     };
-    // O = corr O + P V for the V block at vt (each O tile rescaled right before its first product)
+    // O += P V for the V block at vt
     auto pv = [&](const u32x4 (&pf)[2][2], const char *vt) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -249,13 +283,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int dt = 0; dt < HD / 16; ++dt) {
                 const u32x4 vf = VT::frag_split(vt, 16 * dt, kk, lane);
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    if (kk == 0)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            o[rt][dt][r] *= corr_[rt];
+                for (int rt = 0; rt < 2; ++rt)
                     o[rt][dt] = Mfma<T>::step(vf, pf[rt][kk], o[rt][dt]);
-                }
             }
     };
     // One pipelined step j (j + 1 < nblk; PAR = (j + shift) mod 2).  LDS holds
@@ -268,9 +297,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         constexpr int PAR = decltype(par)::value ? 1 : 0;
         f32x4 (&s_cur)[2][4] = PAR ? sb : sa;
         f32x4 (&s_nxt)[2][4] = PAR ? sa : sb;
+        raise(); // block j's maximum, taken in the previous step (or the prologue)
         scores(s_nxt, kbuf + (1 - PAR) * KBYTES);
         u32x4 pf[2][2];
         softmax(s_cur, pf, j, Bool<false>());
+        block_max(s_nxt, j + 1, Bool<false>()); // (the last block's is taken again, masked, in `last`)
         pv(pf, vbuf + PAR * VBYTES);
         store_k(kbuf + PAR * KBYTES);
         store_v(vbuf + (1 - PAR) * VBYTES);
@@ -282,6 +313,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto last = [&](int j, auto par) {
         constexpr int PAR = decltype(par)::value ? 1 : 0;
         f32x4 (&s_cur)[2][4] = PAR ? sb : sa;
+        block_max(s_cur, j, Bool<true>());
+        raise();
         u32x4 pf[2][2];
         softmax(s_cur, pf, j, Bool<true>());
         pv(pf, vbuf + PAR * VBYTES);
@@ -304,6 +337,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         scores(sb, kbuf + KBYTES);
     else
         scores(sa, kbuf);
+    if (nblk > 1) // block 0's maximum for the first step (a single block is `last`'s, masked)
+        block_max(shift ? sb : sa, 0, Bool<false>());
     store_k(kbuf + (1 - shift) * KBYTES);
     load_k(2);
     stage_barrier();
