@@ -134,9 +134,8 @@ bool aligned(const void *p, int64_t ld, int64_t stride, int esz, int vb)
 }
 
 // Load mode of one operand: -1 if only the generic kernel can read it.
-//  kc: K is the contiguous dimension; mn: the operand's M (or N) size;
-//  is_b: the operand is B (the 8-bit transposed layout serves B only).
-int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, int64_t K, int64_t mn, bool is_b)
+//  kc: K is the contiguous dimension; mn: the operand's M (or N) size.
+int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, int64_t K, int64_t mn)
 {
     if (kc) {
         if (aligned(p, ld, stride, esz, 16) && (K * esz) % 16 == 0)
@@ -147,7 +146,7 @@ int operand_mode(bool kc, const void *p, int64_t ld, int64_t stride, int esz, in
     }
     if (esz == 2 && aligned(p, ld, stride, esz, 16) && mn % 8 == 0)
         return MC16;
-    if (esz == 1 && is_b && aligned(p, ld, stride, esz, 16) && mn % 16 == 0)
+    if (esz == 1 && aligned(p, ld, stride, esz, 16) && mn % 16 == 0)
         return MC8;
     return -1;
 }
@@ -246,8 +245,8 @@ int validate(const dmu_gemm_args *a, Plan *plan)
 
     // kernel selection
     const bool a_kc = a->layout_a == DMU_ROW_MAJOR, b_kc = a->layout_b == DMU_COL_MAJOR;
-    int amode = K > 0 ? operand_mode(a_kc, a->A, a->lda, batch > 1 ? a->stride_a : 0, esz, K, M, false) : -1;
-    int bmode = K > 0 ? operand_mode(b_kc, a->B, a->ldb, batch > 1 ? a->stride_b : 0, esz, K, N, true) : -1;
+    int amode = K > 0 ? operand_mode(a_kc, a->A, a->lda, batch > 1 ? a->stride_a : 0, esz, K, M) : -1;
+    int bmode = K > 0 ? operand_mode(b_kc, a->B, a->ldb, batch > 1 ? a->stride_b : 0, esz, K, N) : -1;
     if (amode >= 0 && extent(a->layout_a, M, K, a->lda) * esz >= ((int64_t)1 << 31))
         amode = -1; // slice too large for one buffer descriptor
     if (bmode >= 0 && extent(a->layout_b, K, N, a->ldb) * esz >= ((int64_t)1 << 31))

@@ -232,7 +232,8 @@ template <int R, int NW> struct McTile {
 };
 
 // ---------------------------------------------------------------------------
-// M/N-contiguous 8-bit operand (row-major int8 or e4m3 B): the 128 K-rows of a
+// M/N-contiguous 8-bit operand (column-major A or row-major B, int8 or e4m3):
+// the 128 K-rows of a
 // K-tile, R bytes each, K-row k at byte k (R + 16) + 128 (k / 16).  A fragment
 // (16 columns, 16 consecutive k of one 64-k half) is two ds_read_b64_tr_b8:
 // within each group of 16 lanes, if lane j addresses X[k0 + j / 2][c0 + 8 (j %
@@ -600,7 +601,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     static_assert(AMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(BMODE != MC16 || E == 2, "transposed operands are 16-bit");
     static_assert(BMODE != MC8 || E == 1, "the 8-bit transposed layout takes 8-bit operands");
-    static_assert(AMODE != MC8, "an 8-bit transposed A goes through the fallback");
+    static_assert(AMODE != MC8 || E == 1, "the 8-bit transposed layout takes 8-bit operands");
     static_assert(!F8 || MN <= 16, "e4m3 fragments (8 registers per tile) fit beside the accumulators");
     static_assert(!AG || !F8, "the four-wavefront tile takes the 16-bit and int8 instructions");
     typedef typename Mfma<T>::acc_t acc_t;
@@ -635,13 +636,13 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
         const char *Ab = p.A + (int64_t)tc.b * p.stride_a * E;
         const char *Bb = p.B + (int64_t)tc.b * p.stride_b * E;
-        const int64_t a_start = AMODE != MC16 ? m0 * p.lda * E : m0 * E;
+        const int64_t a_start = (AMODE == MC16 || AMODE == MC8) ? m0 * E : m0 * p.lda * E;
         const int64_t b_start = (BMODE == MC16 || BMODE == MC8) ? n0 * E : n0 * p.ldb * E;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)((p.a_bytes - a_start + 3) & ~3ll));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)((p.b_bytes - b_start + 3) & ~3ll));
         ATile ta;
         BTile tb;
-        if constexpr (AMODE == MC16)
+        if constexpr (AMODE == MC16 || AMODE == MC8)
             ta.init(p.lda * E, p.M - m0, wave, lane);
         else
             ta.init(p.lda * E, wave, lane);
@@ -677,14 +678,14 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     // or column (M/N-contiguous) and ends with the batch slice.
     const char *Ab = p.A + (int64_t)tc.b * p.stride_a * E;
     const char *Bb = p.B + (int64_t)tc.b * p.stride_b * E;
-    const int64_t a_start = AMODE != MC16 ? m0 * p.lda * E : m0 * E;
+    const int64_t a_start = (AMODE == MC16 || AMODE == MC8) ? m0 * E : m0 * p.lda * E;
     const int64_t b_start = (BMODE == MC16 || BMODE == MC8) ? n0 * E : n0 * p.ldb * E;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_start, (uint32_t)((p.a_bytes - a_start + 3) & ~3ll));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_start, (uint32_t)((p.b_bytes - b_start + 3) & ~3ll));
 
     ATile ta;
     BTile tb;
-    if constexpr (AMODE == MC16)
+    if constexpr (AMODE == MC16 || AMODE == MC8)
         ta.init(p.lda * E, p.M - m0, wave, lane);
     else
         ta.init(p.lda * E, wave, lane);

@@ -326,15 +326,17 @@ int dmu_attention_check(const dmu_attention_args *args);
  * string: "mfma_<tile>_<A mode>_<B mode>_<in>_<out>", e.g.
  * "mfma_256x256_k16_t16_bf16_bf16" -- 256 x 256 tiles, A K-contiguous with
  * 16-byte rows, B M/N-contiguous 16-bit -- or "mfma_generic64_any_any_f16_f32"
- * for the fallback), or NULL if the arguments are invalid or the call would
+ * for the fallback; operand modes: k16 K-contiguous with 16-byte rows, kd
+ * K-contiguous with 4-byte rows, t16 M/N-contiguous 16-bit, t8 M/N-contiguous
+ * 8-bit), or NULL if the arguments are invalid or the call would
  * launch nothing.  The tile is 256 x 128 when N <= 128 < M; otherwise, when
  * 240 or more 256 x 256 tiles cover the problem, 256 x 256 if K spans more
  * than two 128-byte K-tiles and 256 x 128 if it spans at most two; 128 x 128
  * for smaller problems; e4m3 never takes 256 x 256.  The environment
  * variable DMU_FORCE_KERNEL=256x256 | 256x256w4 | 256x128 | 128x128 | generic
  * overrides the choice ("256x256w4": the 256 x 256 tile on four wavefronts of
- * 128 x 128 with AGPR accumulators, 16-bit and int8 inputs; never chosen by
- * default).  Host-only; no GPU access.
+ * 128 x 128 with AGPR accumulators, 16-bit inputs -- int8 takes 256x256
+ * instead; never chosen by default).  Host-only; no GPU access.
  */
 const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
 

@@ -128,7 +128,11 @@ def test_empty_problems_launch_nothing():
     (dict(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096, in_type="e4m3", out_type="bf16",
           acc_type="f32"), "mfma_256x128_k16_t8_e4m3_bf16"),
     (dict(M=4096, N=4096, K=4096, lda=4096, layout_a="col", ldb=4096, ldd=4096, in_type="i8",
-          out_type="i32"), "mfma_generic64_any_any_i8_i32"),   # an 8-bit column-major A
+          out_type="i32"), "mfma_256x256_t8_t8_i8_i32"),   # 8-bit column-major A and row-major B
+    (dict(M=4096, N=4096, K=4096, lda=4096, layout_a="col", ldb=4096, layout_b="col", ldd=4096,
+          in_type="i8", out_type="i32"), "mfma_256x256_t8_k16_i8_i32"),
+    (dict(M=4088, N=4096, K=4096, lda=4088, layout_a="col", ldb=4096, ldd=4096, in_type="i8",
+          out_type="i32"), "mfma_generic64_any_any_i8_i32"),   # M not a multiple of 16
     (dict(M=4096, N=128, K=4096, lda=4096, ldb=128, ldd=128, batch=32, stride_a=4096 * 4096,
           stride_b=4096 * 128, stride_d=4096 * 128), "mfma_256x128_k16_t16_f16_f32"),
     # two K-tiles or fewer: 256 x 128 even with enough tiles for 256 x 256; four: 256 x 256

@@ -54,8 +54,8 @@ def test_reduced_parity(out_t, kernel, K):
 
 @pytest.mark.parametrize("la,lb", [("row", "row"), ("col", "col"), ("col", "row")])
 def test_other_layouts(la, lb):
-    """An M-contiguous A, and an N-contiguous B whose N is not a multiple of 16, go through the
-    fallback kernel."""
+    """An M-contiguous A whose M, or an N-contiguous B whose N, is not a multiple of 16 goes
+    through the fallback kernel."""
     p = problem("bf16", 2, M=150, N=140, K=260, la=la, lb=lb)
     got, name = gu.run_dmu(p, return_name=True)
     assert "generic" in name, name
@@ -65,11 +65,13 @@ def test_other_layouts(la, lb):
 @pytest.mark.parametrize("kernel", ["256x128", "128x128"])
 @pytest.mark.parametrize("out_t", ["f32", "bf16"])
 @pytest.mark.parametrize("K", [384, 200])
-def test_row_major_b_tiled(kernel, out_t, K):
-    """A row-major B (N-contiguous, N a multiple of 16) takes the tiled kernel's 8-bit
-    transposed LDS layout (ds_read_b64_tr_b8 fragments): against the oracle, and bit for bit
-    against the fallback, which issues the same instructions on the same fragments."""
-    p = problem(out_t, 4, M=300, N=272, K=K, la="row", lb="row", with_c=out_t != "f32")
+@pytest.mark.parametrize("la,lb", [("row", "row"), ("col", "col"), ("col", "row")])
+def test_transposed_8bit_tiled(kernel, out_t, K, la, lb):
+    """A row-major B (N-contiguous, N a multiple of 16) or a column-major A (M-contiguous, M a
+    multiple of 16) takes the tiled kernel's 8-bit transposed LDS layout (ds_read_b64_tr_b8
+    fragments): against the oracle, and bit for bit against the fallback, which issues the same
+    instructions on the same fragments."""
+    p = problem(out_t, 4, M=304, N=272, K=K, la=la, lb=lb, with_c=out_t != "f32")
     got, name = gu.run_dmu(p, force=kernel, return_name=True)
     assert "_t8_" in name and kernel in name, name
     gu.assert_close(got, gu.run_oracle(p), p, where=gu.valid_mask(p))

@@ -366,3 +366,26 @@ def test_persistent_form_long_k(cfg, kernel, shape, monkeypatch):
     assert np.array_equal(got, ref)
     bij = gu.sample_bij(p, n=256, seed=3)
     gu.assert_close(got[gu.flat_index(p, bij)], gu.oracle_at(p, bij), p)
+
+
+def int8_layouts(la, lb, seed, M, N, K):
+    """An int8 problem with the same logical A and B values stored in the given layouts."""
+    p = workloads.make("c5nn", "random", seed, M=M, N=N, K=K)
+    a = np.asarray(p.A).reshape(1, M, p.lda)[:, :, :K].astype(np.float64)
+    b = np.asarray(p.B).reshape(1, K, p.ldb)[:, :, :N].astype(np.float64)
+    p.A, p.lda = workloads.store(a, "i8", la)
+    p.B, p.ldb = workloads.store(b, "i8", lb)
+    p.layout_a, p.layout_b = la, lb
+    return p
+
+
+@pytest.mark.parametrize("kernel", ["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("lb", ["row", "col"])
+def test_int8_column_major_a_tiled(kernel, lb):
+    """A column-major int8 A (M a multiple of 16) takes the tiled kernel's 8-bit transposed LDS
+    layout, with either B: exact against the oracle, and bit for bit against the fallback."""
+    p = int8_layouts("col", lb, 41, M=272, N=304, K=448)
+    got, name = gu.run_dmu(p, force=kernel, return_name=True)
+    assert f"mfma_{kernel}_t8_{'t8' if lb == 'row' else 'k16'}_i8" in name, name
+    gu.assert_close(got, gu.run_oracle(p), p, where=gu.valid_mask(p))
+    gu.assert_bits_equal(got, gu.run_dmu(p, force="generic"), where=gu.valid_mask(p))
