@@ -299,6 +299,8 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
     for _ in range(args.warmup):
         dmu.dmu_attention(a, stream)
     torch.cuda.synchronize()
+    if args.phases:
+        return run_phases(args, lambda: dmu.dmu_attention(a, stream), stream, dmu, torch, np, kernel)
     lt = launch_times(lambda: dmu.dmu_attention(a, stream), stream, torch)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -319,9 +321,10 @@ def run_attention(args, dmu, workloads, torch, np, to_dev) -> int:
         "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": batch, "seq_q": sq, "seq_k": sk,
                    "head_dim": hd, "in_type": in_t, "out_type": out_t, "kernel": kernel,
                    "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": roofline(flops, batch * (sq + 2 * sk) * hd * 2 + batch * sq * hd * (4 if out_t == "f32" else 2),
-                             ms * 1e-3, peak, stored_traffic(args.workload, kernel),
-                             stored_counters(args.workload, kernel)),
+        "roofline": dict(roofline(flops, batch * (sq + 2 * sk) * hd * 2 + batch * sq * hd * (4 if out_t == "f32" else 2),
+                                  ms * 1e-3, peak, stored_traffic(args.workload, kernel),
+                                  stored_counters(args.workload, kernel)),
+                         phase_log=stored_phases(args.workload, kernel)),
         "launch_times": lt,
         "peak_derived": peak_derived(dmu, in_t),
         "cpu_baseline": None if args.no_cpu_baseline else
@@ -457,11 +460,16 @@ def summarize_phases(path: str, workload: str) -> int:
     summ.update(workload=raw["workload"], kernel=raw["kernel"], source_digest=raw["source_digest"],
                 launches_logged=len(raw["launches"]))
     import workloads
-    base = EPILOGUE_WORKLOADS.get(workload, (STREAMK_WORKLOADS.get(workload, workload),))[0]
-    M, N, K, batch, in_t = workloads.FULL[base][:5]
+    if workload in ATTENTION_WORKLOADS:
+        batch, sq, sk, hd, in_t, _ = ATTENTION_WORKLOADS[workload]
+        flops = 4.0 * batch * sq * sk * hd
+    else:
+        base = EPILOGUE_WORKLOADS.get(workload, (STREAMK_WORKLOADS.get(workload, workload),))[0]
+        M, N, K, batch, in_t = workloads.FULL[base][:5]
+        flops = 2.0 * M * N * K * batch
     if summ.get("shader_clock_ghz"):
         summ["mfma_busy_at_shader_clock"] = round(profiling.mfma_busy_at_clock(
-            2.0 * M * N * K * batch, DENSE_FLOP_PER_CLOCK_PER_CU[in_t], raw["compute_units"], summ["span_us"],
+            flops, DENSE_FLOP_PER_CLOCK_PER_CU[in_t], raw["compute_units"], summ["span_us"],
             summ["shader_clock_ghz"]["median"]), 4)
     base = os.path.join(ROOT, "profiles", f"phases_{raw['workload']}")
     with open(base + ".json", "w") as fh:
@@ -531,9 +539,6 @@ def main() -> int:
         return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to("cuda:0")
 
     if args.workload in ATTENTION_WORKLOADS:
-        if args.phases:
-            print("bench.py: the phase log covers the GEMM kernels, not attention", file=sys.stderr)
-            return 2
         return run_attention(args, dmu, workloads, torch, np, to_dev)
 
     ep = None

@@ -322,7 +322,7 @@ def dmu_device_info(device: int = 0):
 
 
 def dmu_phase_log(log, records: int) -> None:
-    """Point every following GEMM launch of the process at a phase log: a device buffer of
+    """Point every following GEMM or attention launch of the process at a phase log: a device buffer of
     ``records`` x 8 uint64 (tensor or address), or None and 0 to turn it off.  Raises DmuError."""
     st = _load().dmu_phase_log(_addr(log), records)
     if st != DMU_OK:
@@ -330,8 +330,9 @@ def dmu_phase_log(log, records: int) -> None:
 
 
 def dmu_phase_log_last():
-    """(records, kind) of the last GEMM launch's phase log; kind 0 none, 1 one record per
-    workgroup, 2 one per tile of the persistent kernel, 3 one per stream-K worker."""
+    """(records, kind) of the last launch's phase log; kind 0 none, 1 one record per
+    workgroup, 2 one per tile of the persistent kernel, 3 one per stream-K worker, 4 one per
+    workgroup of the attention kernel."""
     n, kind = ctypes.c_size_t(), ctypes.c_int()
     st = _load().dmu_phase_log_last(ctypes.byref(n), ctypes.byref(kind))
     if st != DMU_OK:

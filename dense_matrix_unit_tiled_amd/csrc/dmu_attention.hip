@@ -55,6 +55,7 @@ struct AttnParams {
     int32_t sq, sk, nqb;                        // query blocks per batch slice
     float scale_log2;                           // scale * log2(e)
     int64_t q_bytes, k_bytes, v_bytes;          // bytes spanned by one batch slice
+    uint64_t *phases;                           // phase log (diagnostics), NULL: off
 };
 
 namespace {
@@ -110,6 +111,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    phase_begin(p.phases, blockIdx.x, (uint32_t)((p.sk + BKEYS - 1) / BKEYS));
     // Workgroup i runs on XCD i mod 8: renumber so that each XCD receives a
     // contiguous range, i.e. the query blocks of one batch slice share that
     // XCD's L2 for K and V.
@@ -353,6 +355,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         step(j + 1, Bool<false>());
     }
     last(nblk - 1, Bool<true>());
+    phase_mark(p.phases, blockIdx.x, PH_LOOP);
+    phase_mark(p.phases, blockIdx.x, PH_FIX);
 
     // O / l, each row's sum added up over the four lanes that hold its parts
     char *Ob = p.O + b * p.stride_o * (int64_t)sizeof(ot);
@@ -376,6 +380,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
             *reinterpret_cast<ov4 *>(row + 16 * dt + 4 * (lane >> 4)) = v;
         }
     }
+    phase_end(p.phases, blockIdx.x);
 }
 
 int elem_size(int t) { return t == DMU_F32 ? 4 : 2; }
@@ -501,7 +506,7 @@ using namespace dmu;
 extern "C" int dmu_attention_check(const dmu_attention_args *args)
 {
     clear_error();
-    AttnParams p;
+    AttnParams p{};
     bool launch;
     return attn_validate(args, &p, &launch);
 }
@@ -509,13 +514,15 @@ extern "C" int dmu_attention_check(const dmu_attention_args *args)
 extern "C" int dmu_attention(const dmu_attention_args *args, void *stream)
 {
     clear_error();
-    AttnParams p;
+    AttnParams p{};
     bool launch;
     int rc = attn_validate(args, &p, &launch);
     if (rc != DMU_OK || !launch)
         return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int64_t grid = (int64_t)p.nqb * args->batch;
+    if ((rc = phase_reserve((size_t)grid, 4, "dmu_attention", &p.phases)) != DMU_OK)
+        return rc;
     hipError_t e;
     const bool bf = args->in_type == DMU_BF16;
     switch (args->out_type) {

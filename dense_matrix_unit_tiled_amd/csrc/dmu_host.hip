@@ -634,10 +634,6 @@ int g_phase_kind = 0;    // how they are indexed (dmu_phase_log_last)
 // worker (`sk_workers` > 0); none for the fallback.
 int phase_attach(Plan *plan, uint32_t sk_workers, const char *who)
 {
-    std::lock_guard<std::mutex> lock(g_phase_mu);
-    plan->p.phases = nullptr;
-    if (!g_phase_log)
-        return DMU_OK;
     size_t n = 0;
     int kind = 0;
     if (sk_workers > 0) {
@@ -647,15 +643,7 @@ int phase_attach(Plan *plan, uint32_t sk_workers, const char *who)
         n = plan->p.total_tiles;
         kind = plan->cfg.workers > 0 ? 2 : 1;
     }
-    if (n > g_phase_cap) {
-        set_error("%s: the launch writes %zu phase records, the log holds %zu", who, n, g_phase_cap);
-        return DMU_ERR_INVALID_ARG;
-    }
-    if (n > 0)
-        plan->p.phases = g_phase_log;
-    g_phase_last = n;
-    g_phase_kind = kind;
-    return DMU_OK;
+    return phase_reserve(n, kind, who, &plan->p.phases);
 }
 
 // Zeroes n 32-bit words (a kernel rather than hipMemsetAsync, so that the call
@@ -667,6 +655,24 @@ __global__ void __launch_bounds__(256) zero_words(uint32_t *w, uint32_t n)
 }
 
 } // namespace
+
+int phase_reserve(size_t records, int kind, const char *who, uint64_t **log)
+{
+    std::lock_guard<std::mutex> lock(g_phase_mu);
+    *log = nullptr;
+    if (!g_phase_log)
+        return DMU_OK;
+    if (records > g_phase_cap) {
+        set_error("%s: the launch writes %zu phase records, the log holds %zu", who, records, g_phase_cap);
+        return DMU_ERR_INVALID_ARG;
+    }
+    if (records > 0)
+        *log = g_phase_log;
+    g_phase_last = records;
+    g_phase_kind = kind;
+    return DMU_OK;
+}
+
 } // namespace dmu
 
 using namespace dmu;

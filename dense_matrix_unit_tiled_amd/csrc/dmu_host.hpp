@@ -11,6 +11,12 @@ namespace dmu {
 
 void set_error(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
 void clear_error();
+
+// Phase log (dmu_phase_log): when a log is set, checks that it holds `records`
+// records and points *log at it (else leaves *log NULL), and remembers the
+// launch's record count and `kind` for dmu_phase_log_last.  DMU_ERR_INVALID_ARG
+// (message set) when the log is too small.
+int phase_reserve(size_t records, int kind, const char *who, uint64_t **log);
 // DMU_OK, or DMU_ERR_HIP with the runtime's message when the last launch failed.
 int check_launch(const char *what);
 

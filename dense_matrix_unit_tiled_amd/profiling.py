@@ -216,7 +216,7 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
 # ---------------------------------------------------------------------------
 REALTIME_HZ = 100e6
 PHASE_KINDS = {1: "one workgroup per tile", 2: "persistent (one record per tile)",
-               3: "stream-K (one record per worker)"}
+               3: "stream-K (one record per worker)", 4: "attention (one record per workgroup)"}
 
 
 def median_launch(raw: dict) -> dict:

@@ -345,21 +345,23 @@ const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
  * backs a kernel claim with profiler evidence that includes its duration, and
  * "Tensor Cores, CUTLASS and CuTe" section 4.5 explains its kernel's distance
  * from peak by where the time goes; this log says where one launch's time goes
- * per workgroup.  While a log is set, every GEMM launch of the process
- * (dmu_gemm, dmu_gemm_ex, dmu_gemm_streamk, dmu_gemm_streamk_noalloc) has
+ * per workgroup.  While a log is set, every launch of the process (dmu_gemm,
+ * dmu_gemm_ex, dmu_gemm_streamk, dmu_gemm_streamk_noalloc, dmu_attention) has
  * thread 0 of each workgroup write one record of 8 uint64_t into it:
- *   [0] start, [1] end of the main loop, [2] end of the stream-K partial sums
+ *   [0] start, [1] end of the main loop (attention: of the last key block),
+ *       [2] end of the stream-K partial sums
  *       (= [1] for the other kernels), [3] end of the epilogue or of the
  *       stream-K partial store -- the chip's 100 MHz constant clock
  *       (s_memrealtime); for a stream-K worker with several tiles, [1] and
  *       [2] are those of its last tile;
  *   [4] start, [5] end -- the shader clock counter (s_memtime);
  *   [6] HW_ID register (low 32 bits) and XCC_ID register (high 32 bits);
- *   [7] workgroup id (low 32 bits) and the K-tiles of the record (high 32).
+ *   [7] workgroup id (low 32 bits) and the K-tiles (attention: key blocks)
+ *       of the record (high 32).
  * Records: one per workgroup of the one-workgroup-per-tile kernel (index =
  * workgroup id), one per tile of the persistent kernel (index = tile number),
- * one per worker of stream-K (index = worker number); the fallback kernel
- * writes none.  `device_log` is a device buffer of `records` x 64 bytes,
+ * one per worker of stream-K (index = worker number), one per workgroup of
+ * the attention kernel; the fallback kernel writes none.  `device_log` is a device buffer of `records` x 64 bytes,
  * 8-byte aligned, owned by the caller, which must keep it alive while launches
  * that write it may run; NULL with 0 turns the log off (the default).  A launch
  * that would write more records than the log holds fails with
@@ -371,10 +373,11 @@ const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
 int dmu_phase_log(void *device_log, size_t records);
 
 /*
- * Records the last GEMM launch wrote into the phase log (*records; 0 when the
+ * Records the last launch wrote into the phase log (*records; 0 when the
  * log was off, the problem empty or the kernel the fallback) and how they are
  * indexed (*kind: 0 none, 1 one per workgroup of the one-per-tile kernel, 2
- * one per tile of the persistent kernel, 3 one per stream-K worker).  Both are
+ * one per tile of the persistent kernel, 3 one per stream-K worker, 4 one per
+ * workgroup of the attention kernel).  Both are
  * host pointers owned by the caller; DMU_ERR_INVALID_ARG if either is NULL.
  * Host-only.
  */

@@ -84,3 +84,28 @@ def test_fallback_writes_no_records():
     got, r, kind = logged(lambda: gu.run_dmu(p, return_name=True))
     assert "generic" in got[1]
     assert kind == 0 and r.shape[0] == 0
+
+
+def test_attention_records_and_same_bits():
+    """The attention kernel writes one record per workgroup (kind 4), and its output does not
+    change with the log."""
+    torch = gu._torch()
+    rng = np.random.default_rng(35)
+    batch, sq, sk, hd = 2, 300, 200, 128
+    Q, K, V = (workloads.to_bits(rng.uniform(-1, 1, batch * n * hd), "f16") for n in (sq, sk, sk))
+    dQ, dK, dV = gu.to_dev(Q), gu.to_dev(K), gu.to_dev(V)
+
+    def run():
+        dO = torch.zeros(batch * sq * hd, dtype=torch.float32, device="cuda:0")
+        a = dmu.attention_args(batch, sq, sk, hd, dQ, hd, dK, hd, dV, hd, dO, hd, in_type="f16",
+                               out_type="f32", scale=0.1, stride_q=sq * hd, stride_k=sk * hd,
+                               stride_v=sk * hd, stride_o=sq * hd)
+        dmu.dmu_attention(a)
+        torch.cuda.synchronize()
+        return dO.cpu().numpy()
+
+    plain = run()
+    got, r, kind = logged(run)
+    assert np.array_equal(got.view(np.uint32), plain.view(np.uint32))
+    assert kind == 4
+    check_records(r, batch * -(-sq // 256), ktiles=-(-sk // 64))
