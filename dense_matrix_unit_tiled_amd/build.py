@@ -24,6 +24,11 @@ VARIANTS = {None: (BUILD, LIB_PATH, []),
             "poison": (os.path.join(ROOT, "_build_poison"), POISON_LIB_PATH, ["-DDMU_LDS_POISON=1"])}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# Multiply-adds are fused freely except where a `#pragma clang fp contract(off)`
+# says otherwise (the fused epilogue, whose every operation rounds on its own so
+# that every kernel computes it to the same bits): plain "fast" would ignore the
+# pragma and fuse differently in different kernels.
+#
 # Packed fp32 VALU instructions are disabled for all device code: this library
 # does not use them, and hipcc -O3 would otherwise form them from plain float
 # code.  The host pass warns that it does not know the feature.
@@ -36,7 +41,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # to VGPR lanes, not to memory; they are listed in _build/resource_usage.txt).
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-munsafe-fp-atomics", "-ffp-contract=fast",
+                "-munsafe-fp-atomics", "-ffp-contract=fast-honor-pragmas",
                 "-mllvm", "-pragma-unroll-threshold=1000000", "-Werror=pass-failed",
                 "-Rpass-analysis=kernel-resource-usage"]
 

@@ -250,6 +250,10 @@ __device__ __forceinline__ typename Out<O>::t epi_one(int epi, int act, ST v, fl
             a = a > 0.0f ? a : 0.0f;
         else if (act == 2)
             a = gelu_tanh(a);
+        // the fp32 result first, then its one rounding to the output type: the
+        // empty statement keeps the last multiply or add from being fused with
+        // the conversion (a mixed-precision multiply-add rounds once, to 16 bits)
+        asm("" : "+v"(a));
         return Out<O>::from_acc(a);
     }
 }
@@ -268,6 +272,7 @@ struct GemmParams {
     uint32_t total_tiles;                       // tiles_m * tiles_n * batch
     int32_t a_kc, b_kc;                         // 1: operand is K-contiguous in memory
     int32_t d_vec4;                             // 1: 4-element vector access to C/D is legal
+    int32_t d_nt;                               // 1: D's rows are whole 128-byte lines (streaming stores)
     int64_t a_bytes, b_bytes;                   // bytes spanned by one batch slice of A / B
     // fused epilogue: D = act(rs(i) * cs(j) * P + bias(j) + C(i,j)); NULL vectors are absent
     const float *rs, *cs, *bias;

@@ -318,6 +318,7 @@ int validate(const dmu_gemm_args *a, Plan *plan)
     p.b_kc = b_kc;
     const bool c_vec = !a->C || (((uintptr_t)a->C % (4 * osz)) == 0 && a->ldc % 4 == 0 && p.stride_c % 4 == 0);
     p.d_vec4 = ((uintptr_t)a->D % (4 * osz)) == 0 && a->ldd % 4 == 0 && p.stride_d % 4 == 0 && c_vec;
+    p.d_nt = ((uintptr_t)a->D % 128) == 0 && (a->ldd * osz) % 128 == 0 && (p.stride_d * osz) % 128 == 0;
     p.a_bytes = extent(a->layout_a, M, K, a->lda) * esz;
     p.b_bytes = extent(a->layout_b, K, N, a->ldb) * esz;
     return DMU_OK;
