@@ -208,7 +208,8 @@ def summarize(d: str, profiles: str, workload_name: str, kernel_label: str, sour
 # (dmu_phase_log).  One record of 8 64-bit words per workgroup (per tile for the
 # persistent kernel, per worker for stream-K):
 #   0 start, 1 end of the main loop, 2 end of the partial-sum additions (stream-K
-#   finisher; = 1 elsewhere), 3 end of the epilogue or of the partial store
+#   finisher; persistent kernel: the next tile's first loads issued; = 1 elsewhere),
+#   3 end of the epilogue or of the partial store
 #   -- the chip's 100 MHz constant clock (s_memrealtime), as wavefront 0 sees them;
 #   4 start, 5 end -- the shader clock counter (s_memtime);
 #   6 HW_ID (low word) and XCC_ID (high word) of wavefront 0;
@@ -295,7 +296,7 @@ def phase_markdown(workload_name: str, kernel: str, command: str, s: dict) -> st
              "| phase | µs (min / median / max over records) |", "|---|---|",
              f"| whole record (start to end) | {f(s['duration_us'])} |",
              f"| main loop (prologue loads and every K-tile) | {f(s['main_loop_us'])} |",
-             f"| partial sums (stream-K finisher) | {f(s['partial_sums_us'])} |",
+             f"| partial sums (stream-K finisher; persistent: next tile's loads issued) | {f(s['partial_sums_us'])} |",
              f"| epilogue (or partial store) | {f(s['epilogue_us'])} |", "",
              "| launch-wide | value |", "|---|---|",
              f"| span, first start to last end | {s['span_us']:.2f} µs |",

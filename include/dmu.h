@@ -349,8 +349,9 @@ const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
  * dmu_gemm_ex, dmu_gemm_streamk, dmu_gemm_streamk_noalloc, dmu_attention) has
  * thread 0 of each workgroup write one record of 8 uint64_t into it:
  *   [0] start, [1] end of the main loop (attention: of the last key block),
- *       [2] end of the stream-K partial sums
- *       (= [1] for the other kernels), [3] end of the epilogue or of the
+ *       [2] end of the stream-K partial sums (persistent kernel: after the
+ *       next tile's first loads are issued; = [1] for the other kernels),
+ *       [3] end of the epilogue or of the
  *       stream-K partial store -- the chip's 100 MHz constant clock
  *       (s_memrealtime); for a stream-K worker with several tiles, [1] and
  *       [2] are those of its last tile;
