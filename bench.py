@@ -53,6 +53,8 @@ WORKLOAD_NAMES = {
 
 # Fused attention (dmu_attention): batch, seq_q, seq_k, head_dim, in type, out type.
 ATTENTION_WORKLOADS = {"c4fa": (32, 4096, 4096, 128, "f16", "f32")}
+# the matrix-core-bound products whose bench line also measures the matrix-core ceiling
+CEILING_WORKLOADS = {"c2", "c3", "c5", "c5nn", "c5dq"}
 WORKLOAD_NAMES["c4fa"] = "batched32_attention_4096x4096x128_f16_f32out_fused"
 
 # Workloads that run the persistent stream-K schedule (dmu_gemm_streamk): base problem.
@@ -381,6 +383,41 @@ def launch_times(launch, stream, torch, n_warm: int = 50, n_cold: int = 20, rewa
 FLOP_PER_CLOCK_PER_CU = {"bf16": 4096, "f16": 4096, "i8": 8192, "e4m3": 8192}
 
 
+CEILING_ROUNDS, CEILING_WORKGROUPS = 128, 256
+
+
+def mfma_ceiling(dmu, torch, in_type: str, stream, n_ramp: int = 400, n_timed: int = 200):
+    """The matrix-core rate this machine sustains with nothing else running (dmu_mfma_ceiling: the
+    tiled kernels' instruction on register operands, a grid shaped like the 4096^3 launch), timed
+    like the product itself, with the median shader clock of its workgroups; None for types that
+    have no ceiling kernel."""
+    if in_type not in ("bf16", "f16", "i8"):
+        return None
+    stamps = torch.zeros(CEILING_WORKGROUPS * 4, dtype=torch.int64, device="cuda:0")
+    launch = lambda st=None: dmu.dmu_mfma_ceiling(in_type, CEILING_ROUNDS, CEILING_WORKGROUPS, st, stream)
+    for _ in range(n_ramp):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n_timed):
+        launch()
+    e1.record(stream)
+    launch(stamps)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n_timed
+    r = stamps.view(-1, 4).cpu().numpy().astype("float64")
+    clk = sorted((r[:, 3] - r[:, 1]) / ((r[:, 2] - r[:, 0]) * 10.0))  # s_memtime ticks per ns
+    flop_per_instr = 16 * 16 * (64 if in_type == "i8" else 32) * 2
+    flops = CEILING_WORKGROUPS * 8 * CEILING_ROUNDS * 32 * flop_per_instr
+    tf = flops / (us * 1e-6) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[in_type], 4), "us": round(us, 3),
+            "shader_clock_ghz": round(clk[len(clk) // 2], 3),
+            "grid": f"{CEILING_WORKGROUPS} workgroups x 8 wavefronts, {CEILING_ROUNDS} rounds of 32 "
+                    f"instructions each ({flops / 1e9:.1f} G{'OP' if in_type == 'i8' else 'FLOP'})",
+            "source": "dmu_mfma_ceiling (register operands, no memory traffic)"}
+
+
 def peak_derived(dmu, dtype: str) -> dict:
     """The dense peak re-derived on this machine: compute units x peak clock x flops per clock."""
     cus, khz = dmu.dmu_device_info(0)
@@ -589,6 +626,9 @@ def main() -> int:
     ms = start.elapsed_time(end) / args.steps
     print(f"# timed {args.steps} launches: {ms * 1e3:.2f} us each", file=sys.stderr, flush=True)
 
+    ceiling = None
+    if not args.copy_calibration and args.workload in CEILING_WORKLOADS:
+        ceiling = mfma_ceiling(dmu, torch, p.in_type, stream)
     copy_calibration(args, torch)
     sk_failed = None
     if args.workload in STREAMK_WORKLOADS and ws_bytes:
@@ -622,6 +662,9 @@ def main() -> int:
         "launch_times": lt,
         "peak_derived": peak_derived(dmu, p.in_type),
     }
+    if ceiling is not None:
+        result["roofline"]["mfma_ceiling"] = ceiling
+        result["roofline"]["frac_of_ceiling"] = round(tflops / ceiling["tflops"], 4)
     if sk_failed is not None:
         result["streamk_wait_failed"] = sk_failed  # a wait that gave up leaves a wrong D (never expected)
     if args.workload == "c2":

@@ -138,6 +138,7 @@ def _open(path):
     lib.dmu_device_info.restype = i32
     lib.dmu_status_string.argtypes, lib.dmu_status_string.restype = [i32], ctypes.c_char_p
     lib.dmu_last_error.argtypes, lib.dmu_last_error.restype = [], ctypes.c_char_p
+    lib.dmu_mfma_ceiling.argtypes, lib.dmu_mfma_ceiling.restype = [i32, i32, i32, vp, vp], i32
     lib.dmu_phase_log.argtypes, lib.dmu_phase_log.restype = [vp, ctypes.c_size_t], i32
     lib.dmu_phase_log_last.argtypes = [ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int)]
     lib.dmu_phase_log_last.restype = i32
@@ -319,6 +320,16 @@ def dmu_device_info(device: int = 0):
     if st != DMU_OK:
         raise DmuError(st, dmu_last_error())
     return cu.value, khz.value
+
+
+def dmu_mfma_ceiling(in_type: str, rounds: int, workgroups: int, stamps=None, stream=None, check: bool = True) -> int:
+    """Launch the matrix-core ceiling microbenchmark (register-only MFMA chains on a grid shaped
+    like the tiled kernels'); the caller times it.  ``stamps``: None or a device buffer of
+    workgroups x 4 uint64."""
+    st = _load().dmu_mfma_ceiling(DTYPES[in_type], rounds, workgroups, _addr(stamps), _stream(stream))
+    if check and st != DMU_OK:
+        raise DmuError(st, dmu_last_error())
+    return st
 
 
 def dmu_phase_log(log, records: int) -> None:

@@ -200,9 +200,92 @@ __global__ void __launch_bounds__(64) probe_cvt(const float *in, uint16_t *out)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core ceiling (diagnostics): the rate this chip sustains for the GEMM
+// kernels' 16 x 16 instructions when nothing else runs.  A grid shaped like the
+// 4096^3 launch (workgroups of 8 wavefronts, two per SIMD) where every
+// wavefront issues `rounds` x 32 independent MFMAs into 32 accumulators, the
+// operands drawn from 4 x 4 register fragments of fixed pseudo-random finite
+// values (data as varied as a real product's, so the power drawn is alike),
+// with no memory traffic.  Thread 0 of each workgroup stamps the 100 MHz clock
+// and the shader clock counter at start and end (4 words per workgroup).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t mix32(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    return x ^ (x >> 16);
+}
+
+template <int T>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    mfma_ceiling(uint64_t *stamps, int rounds)
+{
+    typedef typename Mfma<T>::acc_t acc_t;
+    const uint32_t l = threadIdx.x;
+    // 16-bit inputs: sign and mantissa random, exponent fixed (finite values of
+    // magnitude 1-2 in fp16, small in bf16); int8: any bits
+    const uint32_t keep = T == I8 ? 0xffffffffu : 0x83ff83ffu, set = T == I8 ? 0u : 0x3c003c00u;
+    u32x4 x[4], y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[i][e] = (mix32(l * 64 + i * 4 + e + 1) & keep) | set;
+            y[i][e] = (mix32(l * 64 + i * 4 + e + 0x9e3779b9u) & keep) | set;
+        }
+    if (stamps != nullptr && l == 0) {
+        stamps[blockIdx.x * 4 + 0] = __builtin_amdgcn_s_memrealtime();
+        stamps[blockIdx.x * 4 + 1] = __builtin_amdgcn_s_memtime();
+    }
+    acc_t acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+        acc[j] = acc_t{};
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            acc[j] = Mfma<T>::step(x[j & 3], y[(j >> 2) & 3], acc[j]);
+    }
+    // the results stay live (no store: an empty statement that reads them)
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+        asm volatile("" : : "v"(acc[j]));
+    if (stamps != nullptr && l == 0) {
+        stamps[blockIdx.x * 4 + 2] = __builtin_amdgcn_s_memrealtime();
+        stamps[blockIdx.x * 4 + 3] = __builtin_amdgcn_s_memtime();
+    }
+}
+
 } // namespace dmu
 
 using namespace dmu;
+
+extern "C" int dmu_mfma_ceiling(int in_type, int rounds, int workgroups, void *stamps, void *stream)
+{
+    clear_error();
+    if (rounds < 1 || workgroups < 1) {
+        set_error("dmu_mfma_ceiling: rounds and workgroups must be positive");
+        return DMU_ERR_INVALID_ARG;
+    }
+    if ((uintptr_t)stamps % 8) {
+        set_error("dmu_mfma_ceiling: stamps is not 8-byte aligned");
+        return DMU_ERR_INVALID_ARG;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint64_t *st = static_cast<uint64_t *>(stamps);
+    switch (in_type) {
+    case DMU_BF16: hipLaunchKernelGGL(mfma_ceiling<BF16>, dim3(workgroups), dim3(512), 0, s, st, rounds); break;
+    case DMU_F16: hipLaunchKernelGGL(mfma_ceiling<F16>, dim3(workgroups), dim3(512), 0, s, st, rounds); break;
+    case DMU_I8: hipLaunchKernelGGL(mfma_ceiling<I8>, dim3(workgroups), dim3(512), 0, s, st, rounds); break;
+    default:
+        set_error("dmu_mfma_ceiling: input type %d has no ceiling kernel (bf16, fp16, int8)", in_type);
+        return DMU_ERR_UNSUPPORTED;
+    }
+    return check_launch("dmu_mfma_ceiling");
+}
 
 extern "C" int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type, int *regs)
 {

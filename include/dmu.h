@@ -473,6 +473,26 @@ enum {
 
 int dmu_probe(int variant, const void *in0, const void *in1, void *out, void *stream);
 
+/*
+ * Matrix-core ceiling (diagnostics): the rate this chip sustains for the GEMM
+ * kernels' 16 x 16 matrix instructions when nothing else runs, the practical
+ * counterpart of the dense peak that "Tensor Cores, CUTLASS and CuTe" derives
+ * in its opening section (units x instructions per clock x clock), measured
+ * rather than multiplied out.  Launches `workgroups` workgroups of 8
+ * wavefronts (two per SIMD, as the tiled kernels run); every wavefront issues
+ * rounds x 32 independent instructions of `in_type` (DMU_BF16, DMU_F16:
+ * 16x16x32; DMU_I8: 16x16x64) on register operands of fixed pseudo-random
+ * finite values, with no memory traffic.  With 256 workgroups and 128 rounds
+ * the launch does the 2 x 4096^3 FLOP of the 4096^3 product.  `stamps` (device,
+ * caller-owned, 8-byte aligned, or NULL) receives 4 uint64_t per workgroup:
+ * the 100 MHz constant clock and the shader clock counter at start, then both
+ * at end, from thread 0.  The caller times the launch (HIP events on
+ * `stream`).  DMU_ERR_INVALID_ARG for rounds or workgroups < 1 or a misaligned
+ * `stamps`; DMU_ERR_UNSUPPORTED for another type; DMU_ERR_HIP if the launch
+ * fails.
+ */
+int dmu_mfma_ceiling(int in_type, int rounds, int workgroups, void *stamps, void *stream);
+
 /* Shape of a probe variant: instruction m, n, k, input dmu_dtype and the
  * number of 32-bit output registers per lane.  Host-only. */
 int dmu_probe_info(int variant, int *m, int *n, int *k, int *in_type, int *regs_per_lane);

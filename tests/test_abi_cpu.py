@@ -353,3 +353,15 @@ def test_phase_log_capacity_checked_before_launch(monkeypatch):
         assert "64 phase records" in dmu.dmu_last_error()
     finally:
         dmu.dmu_phase_log(None, 0)
+
+
+def test_mfma_ceiling_argument_errors():
+    """The ceiling microbenchmark rejects bad counts, misaligned stamps and types without a kernel,
+    before any HIP call."""
+    lib = dmu.library()
+    assert lib.dmu_mfma_ceiling(dmu.DMU_BF16, 0, 256, None, None) == dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_mfma_ceiling(dmu.DMU_BF16, 128, 0, None, None) == dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_mfma_ceiling(dmu.DMU_BF16, 128, 256, ctypes.c_void_p((1 << 40) + 4), None) == \
+        dmu.DMU_ERR_INVALID_ARG
+    assert lib.dmu_mfma_ceiling(dmu.DMU_F32, 128, 256, None, None) == dmu.DMU_ERR_UNSUPPORTED
+    assert "no ceiling kernel" in dmu.dmu_last_error()

@@ -267,3 +267,29 @@ def test_lane_swap_pairs():
     for lane in range(64):
         assert sorted(got[lane, :2]) == sorted([vals[lane], vals[lane ^ 16]]), lane
         assert sorted(got[lane, 2:]) == sorted([vals[lane], vals[lane ^ 32]]), lane
+
+
+@pytest.mark.parametrize("in_type,peak", [("bf16", 2500.0), ("i8", 5000.0)])
+def test_mfma_ceiling_rate_and_stamps(in_type, peak):
+    """The ceiling microbenchmark runs at a plausible fraction of the published dense peak (never
+    above it) and stamps every workgroup with a consistent start and end."""
+    import torch
+
+    wgs, rounds = 256, 64
+    stamps = torch.zeros(wgs * 4, dtype=torch.int64, device="cuda:0")
+    for _ in range(50):
+        dmu.dmu_mfma_ceiling(in_type, rounds, wgs)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        dmu.dmu_mfma_ceiling(in_type, rounds, wgs)
+    e1.record()
+    dmu.dmu_mfma_ceiling(in_type, rounds, wgs, stamps)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 20
+    flop = wgs * 8 * rounds * 32 * 16 * 16 * (64 if in_type == "i8" else 32) * 2
+    tflops = flop / (us * 1e-6) / 1e12
+    assert 0.2 * peak < tflops <= 1.02 * peak, tflops
+    r = stamps.view(-1, 4).cpu().numpy()
+    assert np.all(r[:, 0] > 0) and np.all(r[:, 2] >= r[:, 0]) and np.all(r[:, 3] > r[:, 1])
