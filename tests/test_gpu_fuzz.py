@@ -1,0 +1,94 @@
+"""A seeded sweep over the call space: random sizes (ragged and aligned), every type triple, all four
+layout pairs, padded leading dimensions, batches, an optional C and an optional fused epilogue --
+each case against the oracle over every output.  Where the operands qualify for the tiled kernels,
+the default choice, a tile configuration drawn at random, and the persistent form are also held bit
+for bit against the fallback kernel (every one issues the same MFMA instructions on the same
+fragments in the same K order), and the stream-K schedule, whose partial sums are added in another
+order, against the oracle.  The cases are a fixed function of their index, so a failure names a
+reproducible call."""
+import numpy as np
+import pytest
+
+import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [("f16", "f32", "f32"), ("f16", "f32", "f16"), ("f16", "f16", "f16"), ("bf16", "f32", "bf16"),
+         ("bf16", "f32", "f32"), ("i8", "i32", "i32"), ("i8", "i32", "f32"), ("i8", "i32", "bf16"),
+         ("e4m3", "f32", "f32"), ("e4m3", "f32", "bf16")]
+TILES = ["256x256", "256x256w4", "256x128", "128x128"]
+CASES = 96
+
+
+def random_problem(i: int):
+    rng = np.random.default_rng([97, i])
+    in_t, acc_t, out_t = TYPES[i % len(TYPES)]
+    M, N, K = (int(x) for x in rng.integers(1, 600, 3))
+    if rng.random() < 0.5:  # aligned sizes reach the tiled kernels' fast operand modes
+        M, N, K = (-(-v // 16) * 16 for v in (M, N, K))
+    batch = int(rng.choice([1, 1, 1, 2, 3]))
+    la, lb = (str(x) for x in rng.choice(["row", "col"], 2))
+    pad_a, pad_b, pad_d = (int(x) for x in rng.choice([0, 0, 1, 8, 16], 3))
+
+    def draw(shape):
+        if in_t == "i8":
+            return rng.integers(-128, 128, shape).astype(np.float64)
+        if in_t == "e4m3":
+            return rng.standard_normal(shape)
+        return rng.uniform(-1, 1, shape)
+
+    A, lda = workloads.store(draw((batch, M, K)), in_t, la, pad_a)
+    B, ldb = workloads.store(draw((batch, K, N)), in_t, lb, pad_b)
+    ldd = N + pad_d
+    p = workloads.Problem(f"fuzz{i}", M, N, K, batch, in_t, acc_t, out_t, la, lb,
+                          A, lda, ((M if la == "row" else K) * lda) if batch > 1 else 0,
+                          B, ldb, ((K if lb == "row" else N) * ldb) if batch > 1 else 0,
+                          ldd=ldd, stride_d=M * ldd, meta={"cfg": "fuzz", "seed": i})
+    if rng.random() < 0.5:
+        n = batch * M * ldd
+        cv = rng.integers(-1000, 1000, n) if out_t == "i32" else rng.uniform(-1, 1, n)
+        p.C = workloads.to_bits(cv, out_t)
+        p.ldc, p.stride_c = ldd, (M * ldd if batch > 1 else 0)
+    ep = None
+    if out_t != "i32" and rng.random() < 0.35:
+        ep = workloads.make_epilogue(p, i, act=str(rng.choice(["none", "relu", "gelu_tanh"])),
+                                     row=bool(rng.random() < 0.7), col=bool(rng.random() < 0.7),
+                                     bias=bool(rng.random() < 0.7))
+    tile = str(rng.choice(TILES))
+    return p, ep, tile
+
+
+def check(got, want, p, ep):
+    if ep is None:
+        gu.assert_close(got, want, p, where=gu.valid_mask(p))
+    else:
+        bij = gu.all_bij(p)
+        idx = gu.flat_index(p, bij)
+        gu.assert_close_epilogue(got[idx], want[idx], p, ep, bij)
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_random_call(i, monkeypatch):
+    p, ep, tile = random_problem(i)
+    print(f"case {i}: {p.in_type}->{p.out_type} M={p.M} N={p.N} K={p.K} batch={p.batch} "
+          f"{p.layout_a}/{p.layout_b} lda={p.lda} ldb={p.ldb} ldd={p.ldd} C={p.C is not None} "
+          f"ep={ep.act if ep else None} tile={tile}", flush=True)
+    got, name = gu.run_dmu(p, ep=ep, return_name=True)
+    want = gu.run_oracle(p, ep=ep)
+    check(got, want, p, ep)
+    if "generic" in name:
+        return
+    mask = gu.valid_mask(p)
+    ref = gu.run_dmu(p, ep=ep, force="generic")
+    gu.assert_bits_equal(got, ref, where=mask)
+    forced, fname = gu.run_dmu(p, ep=ep, force=tile, return_name=True)
+    gu.assert_bits_equal(forced, ref, where=mask)
+    monkeypatch.setenv("DMU_PERSIST", "always")
+    gu.assert_bits_equal(gu.run_dmu(p, ep=ep), ref, where=mask)
+    monkeypatch.setenv("DMU_PERSIST", "never")
+    monkeypatch.setenv("DMU_STREAMK", "always")
+    sk, skname, _ = gu.run_streamk(p, ep=ep)
+    check(sk, want, p, ep)
+    if p.in_type == "i8" and p.out_type == "i32":
+        gu.assert_bits_equal(sk, ref, where=mask)  # integer sums: exact in any order
