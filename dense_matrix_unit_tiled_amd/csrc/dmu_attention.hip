@@ -26,7 +26,8 @@
 //               Q instead): per row a running maximum m of c s (across the four
 //               lanes that share the row), raised only when a block's maximum
 //               passes it by more than 8 -- decided at the start of the block's
-//               step, where the correction 2^(m_old - m_new) of O and l is a
+//               step from each lane's own maximum, where the maximum across the
+//               lanes and the correction 2^(m_old - m_new) of O and l are a
 //               rarely taken branch -- then p = 2^(c s - m) <= 2^8 (one FMA and
 //               the hardware exp2) and the running sum l (kept per lane, added
 //               up at the end).  Only the last block can hold keys past seq_k;
@@ -215,7 +216,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // is a branch almost never taken after the first blocks, instead of 64
     // multiplies per block.
     constexpr float TAU = 8.0f;
-    float bmx[2]; // c times the maximum score of each row tile of the next block to be exponentiated
+    // Each lane's maximum over its own 16 scores of a row tile decides whether a
+    // raise is due (the row's maximum exceeds m + TAU exactly when one of its four
+    // lanes' maxima does); the maximum across the four lanes is taken only inside
+    // the rare raise.
+    float bmx[2]; // this lane's maximum score in each row tile of the next block to be exponentiated
     auto block_max = [&](const f32x4 (&s)[2][4], int blk, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const int key0 = blk * BKEYS + 4 * (int)(lane >> 4);
@@ -227,17 +232,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     mx = fmaxf(mx, MASKED && key0 + 16 * t + r >= p.sk ? -INFINITY : s[rt][t][r]);
-            bmx[rt] = row_max4(mx) * c;
+            bmx[rt] = mx;
         }
     };
-    // When any row of the wavefront has bmx > m + TAU, every row takes m = max(m,
-    // bmx) and rescales its O tiles and its sum (one wavefront-uniform branch).
+    // When c bmx > m + TAU in any lane of the wavefront, every row takes m =
+    // max(m, c times its block maximum) and rescales its O tiles and its sum (one
+    // wavefront-uniform branch, so that every lane takes part in the cross-lane
+    // maximum).  (c >= 0, so c times the maximum is the maximum of c s.)
     auto raise = [&]() {
-        const bool need = bmx[0] > m[0] + TAU || bmx[1] > m[1] + TAU;
+        const bool need = bmx[0] * c > m[0] + TAU || bmx[1] * c > m[1] + TAU;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                const float m_new = fmaxf(m[rt], bmx[rt]);
+                const float m_new = fmaxf(m[rt], row_max4(bmx[rt]) * c);
                 const float corr = __builtin_amdgcn_exp2f(m[rt] - m_new);
                 m[rt] = m_new;
                 l[rt] *= corr;
@@ -268,13 +275,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
                     s[rt][t][r] = e;
                     sum += e;
                 }
-            l[rt] += sum;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 pf[rt][kk] = u32x4{Pack16<T>::two(s[rt][2 * kk][0], s[rt][2 * kk][1]),
                                    Pack16<T>::two(s[rt][2 * kk][2], s[rt][2 * kk][3]),
                                    Pack16<T>::two(s[rt][2 * kk + 1][0], s[rt][2 * kk + 1][1]),
                                    Pack16<T>::two(s[rt][2 * kk + 1][2], s[rt][2 * kk + 1][3])};
+            l[rt] += sum; // (after the packing: the compiler then schedules the step a little better)
         }
     };
     // O += P V for the V block at vt
