@@ -87,6 +87,24 @@ template <int R, int NW, bool MASK> struct KcTile {
     uint32_t wlane; // LDS offset of this lane's 16 bytes within a transfer
     uint32_t first; // byte offset of the wavefront's first row
     uint32_t xstep; // bytes between the first rows of consecutive transfers
+    uint32_t tm[MASK ? 4 : 1]; // MASK: this lane's byte mask of its chunk in the K-tile holding the row end
+
+    // MASK: rows are only 4-byte aligned and K * element size need not be a
+    // multiple of 16, so in the K-tile that holds the end of the rows, the vector
+    // that straddles a row's end also holds bytes of the next row.  Which bytes
+    // are this lane's own depends only on its chunk, the same in every row.
+    __device__ __forceinline__ void init_mask(uint32_t k_bytes)
+    {
+        if constexpr (MASK) {
+            const uint32_t kl = (k_bytes - 1u) / 128u; // the K-tile holding the row end
+            const int32_t rem = (int32_t)k_bytes - (int32_t)(kl * 128u + cb);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int32_t vb = rem - 4 * d;
+                tm[d] = vb >= 4 ? 0xffffffffu : (vb <= 0 ? 0u : ((1u << (8 * vb)) - 1u));
+            }
+        }
+    }
 
     // Transfer i of wavefront w moves rows 8q .. 8q+7 (q = w NL + i) into LDS
     // bytes 1024 q .. +1023: lane l carries row 8q + l / 8, chunk l % 8 (eight
@@ -106,21 +124,21 @@ template <int R, int NW, bool MASK> struct KcTile {
         const uint32_t kb0 = (uint32_t)kt * 128u;
         return load16s(r, kb0 + cb < k_bytes ? voff : OOB, first + (uint32_t)i * xstep + kb0);
     }
-    // The data of K-tile kt to LDS.  MASK: rows are only 4-byte aligned and
-    // K * element size need not be a multiple of 16, so the vector that
-    // straddles the end of a row also holds bytes of the next row; they are
-    // cleared here, where the load has long completed (clearing them right
-    // after the load would make the wavefront wait for it there).
+    // The data of K-tile kt to LDS.  MASK: in the K-tile holding the row end,
+    // the bytes past it (the next row's) are cleared here, where the load has
+    // long completed (clearing them right after the load would make the
+    // wavefront wait for it there); the other K-tiles keep every byte.  (Before,
+    // the mask was derived in every K-tile from the bytes left: 5000 x 3000 x
+    // 2050 fp16, rows of 4100 bytes, 65.7 -> 64.3 us with the mask taken once,
+    // same bits.)
     __device__ __forceinline__ void store(int i, char *tile, uint32_t wave, uint32_t, u32x4 v, int kt,
                                           uint32_t k_bytes) const
     {
         if constexpr (MASK) {
-            const int32_t rem = (int32_t)k_bytes - (int32_t)((uint32_t)kt * 128u + cb);
+            const uint32_t keep = (uint32_t)kt * 128u + 128u <= k_bytes ? ~0u : 0u;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const int32_t vb = rem - 4 * d;
-                v[d] &= vb >= 4 ? 0xffffffffu : (vb <= 0 ? 0u : ((1u << (8 * vb)) - 1u));
-            }
+            for (int d = 0; d < 4; ++d)
+                v[d] &= tm[d] | keep;
         }
         *reinterpret_cast<u32x4 *>(tile + (wave * NL + i) * 1024 + wlane) = v;
     }
@@ -373,16 +391,27 @@ template <int NT> struct Park {
 
 // One vector of D: a streaming (non-temporal) store -- D is not read again by
 // this kernel, and all tiles write it in one burst at the end (4096^3 bf16:
-// 113 -> 110 us; batched 4096 x 4096 x 128 fp32: 485 -> 386 us) -- or, for the
-// plain form when D's rows start inside a 128-byte line, a plain store, so that
-// the two tiles' parts of a shared line meet in the cache instead of leaving
-// for memory as partial lines (5000 x 3000 x 2050 fp16: 68.8 -> 66.4 us).
+// 113 -> 110 us; batched 4096 x 4096 x 128 fp32: 485 -> 386 us) -- or, when D's
+// rows start inside a 128-byte line, a store written through this XCD's L2
+// (cache policy SC1, i.e. a relaxed store at device scope, 8 bytes at a time):
+// two tiles then write the parts of a shared line, which as streaming stores
+// leave for memory as separate partial lines (5000 x 3000 x 2050 fp16: 68.8 us
+// against 66.4 us with plain stores), while plain stores leave every line of D
+// dirty in the L2s for the write-back at the end of the kernel (66.2 -> 65.2 us
+// written through, interleaved in one process; same bits).
 template <bool NTS, class V> __device__ __forceinline__ void store_d(V *dst, const V &v)
 {
-    if constexpr (NTS)
+    if constexpr (NTS) {
         __builtin_nontemporal_store(v, dst);
-    else
-        *dst = v;
+    } else {
+        static_assert(sizeof(V) % 8 == 0, "D vectors are 8 or 16 bytes");
+        typedef uint64_t w_t __attribute__((ext_vector_type(sizeof(V) / 8)));
+        const w_t w = __builtin_bit_cast(w_t, v);
+        uint64_t *d = reinterpret_cast<uint64_t *>(dst);
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(V) / 8); ++i)
+            __hip_atomic_store(d + i, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // A wavefront block wholly inside D (every row < M, every 4-column vector
@@ -714,6 +743,10 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     else
         tb.init(p.ldb * E, wave, lane);
     const uint32_t k_bytes = (uint32_t)p.K * E;
+    if constexpr (AMODE == KCD)
+        ta.init_mask(k_bytes);
+    if constexpr (BMODE == KCD)
+        tb.init_mask(k_bytes);
 
     // K-tiles between their global loads and their LDS writes, PD sets
     auto &sa = st.sa;
