@@ -7,7 +7,7 @@ type pair), on sampled rows of the full batch-32 4096 x 4096 x 128 problem, and
 bit for bit where the softmax is exactly one-hot.
 
 Tolerance (the products' bar moved through the softmax):
-    |O - ref| <= max|V| (2 u + 2 scale e_S + 1e-5)  [+ 2e-2 |ref| for 16-bit O]
+    |O - ref| <= max|V| (2 u + 2 |scale| e_S + 1e-5)  [+ 2e-2 |ref| for 16-bit O]
 with u the unit roundoff of the input type (P is rounded to it for the P V
 product: 2^-11 fp16, 2^-8 bf16) and e_S = 1e-3 sqrt(d) max|Q| max|K| the bound
 on the scores S = Q K^T.
@@ -74,7 +74,7 @@ class Att:
         k = np.abs(gu.values(self.K, self.in_t)).max()
         v = np.abs(gu.values(self.V, self.in_t)).max()
         e_s = 1e-3 * math.sqrt(HD) * q * k
-        tol = v * (2 * UNIT[self.in_t] + 2 * self.scale * e_s + 1e-5)
+        tol = v * (2 * UNIT[self.in_t] + 2 * abs(self.scale) * e_s + 1e-5)  # the scores' error scales by |scale|
         if self.out_t != "f32":
             tol = tol + 2e-2 * np.abs(ref_vals)
         return tol

@@ -92,3 +92,33 @@ def test_random_call(i, monkeypatch):
     check(sk, want, p, ep)
     if p.in_type == "i8" and p.out_type == "i32":
         gu.assert_bits_equal(sk, ref, where=mask)  # integer sums: exact in any order
+
+
+ATT_TYPES = [("f16", "f32"), ("bf16", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16"), ("bf16", "f16")]
+ATT_CASES = 24
+
+
+def random_attention(i: int):
+    from tests.test_gpu_attention import Att
+
+    rng = np.random.default_rng([98, i])
+    in_t, out_t = ATT_TYPES[i % len(ATT_TYPES)]
+    sq, sk = (int(x) for x in rng.integers(1, 700, 2))
+    batch = int(rng.choice([1, 1, 2, 3]))
+    pad = int(rng.choice([0, 8, 16]))
+    scale = float(rng.choice([128 ** -0.5, 0.5, 2.0, -0.3, 0.0]))
+    lo, hi = [(-1.0, 1.0), (-3.0, 3.0), (0.0, 1.0)][int(rng.integers(0, 3))]
+    return Att(batch, sq, sk, in_t, out_t, 1000 + i, pad=pad, scale=scale, lo=lo, hi=hi)
+
+
+@pytest.mark.parametrize("i", range(ATT_CASES))
+def test_random_attention(i):
+    """Fused attention over random query and key counts (ragged around the 256-query and 64-key
+    blocks), batches, padded strides, every type pair, scales of either sign (zero included) and
+    score ranges that make the running maximum rise often, against the oracle's rows."""
+    from tests.test_gpu_attention import check
+
+    att = random_attention(i)
+    print(f"attention case {i}: {att.in_t}->{att.out_t} batch={att.batch} sq={att.sq} sk={att.sk} "
+          f"ld={att.ldq} scale={att.scale}", flush=True)
+    check(att, att.run(), att.want())
