@@ -219,8 +219,10 @@ def kernel_for(workload: str) -> str:
                       C=(base + (3 << 36)) if workload == "c1" else None, ldc=N if workload == "c1" else 0)
     name = dmu.dmu_gemm_kernel_name(a)
     if workload in STREAMK_WORKLOADS and "generic" not in name:
-        # the stream-K kernel runs 256 x 128 tiles where the data-parallel plan has 256 x 256
-        name = "streamk_" + name.replace("mfma_256x256w4", "mfma_256x128").replace("mfma_256x256", "mfma_256x128")
+        # the stream-K kernel runs 256 x 128 tiles where the data-parallel plan has 256 x 256,
+        # and 128 x 128 where it has 64 x 128
+        name = "streamk_" + name.replace("mfma_256x256w4", "mfma_256x128").replace("mfma_256x256", "mfma_256x128") \
+            .replace("mfma_64x128", "mfma_128x128")
     return name
 
 

@@ -62,6 +62,11 @@ struct Plan {
 };
 
 constexpr int64_t LIM31 = (int64_t)1 << 31;
+// A problem of at most this many 128 x 128 tiles (over all batch slices) takes
+// 64 x 128 tiles instead: half the compute units of the 256-unit chip this
+// library is built for.  (Fixed rather than asked of the device, so that the
+// choice -- and the kernel name -- is known without one.)
+constexpr int64_t FEW_TILES = 128;
 
 int elem_bytes(int t) { return (t == DMU_F32 || t == DMU_I32) ? 4 : (t == DMU_I8 || t == DMU_E4M3 ? 1 : 2); }
 
@@ -96,7 +101,7 @@ struct NameTable {
 const NameTable &kernel_names()
 {
     static const NameTable table = [] {
-        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64", "256x256w4"};
+        static const char *const TILE_NAMES[] = {"256x256", "256x128", "128x128", "generic64", "256x256w4", "64x128"};
         static const char *const MODE_NAMES[] = {"k16", "kd", "t16", "t8"};
         NameTable t;
         for (int a = 0; a < NUM_TILE_CFGS; ++a)
@@ -268,6 +273,13 @@ int validate(const dmu_gemm_args *a, Plan *plan)
             tile = nk <= 2 ? TILE_256x128 : TILE_256x256;
         else
             tile = TILE_128x128;
+        // Few tiles: 64 x 128 tiles put twice as many workgroups on the compute
+        // units (up to all 256 of the chip) at a somewhat lower rate per unit
+        // (1024 x 1024 x 16384 bf16, 64 tiles of 128 x 128: 114.0 -> 81.2 us, same
+        // bits).  The 64-row tile takes K-contiguous A only.
+        const bool a_kc_mode = amode == KC16 || amode == KCD;
+        if (tile == TILE_128x128 && a_kc_mode && ((M + 127) / 128) * ((N + 127) / 128) * batch <= FEW_TILES)
+            tile = TILE_64x128;
         // (The four-wavefront 256 x 256 tile, a third fewer LDS fragment bytes
         // per flop, is not chosen by default: measured in interleaved pairs on
         // one box, 4096^3 bf16 NN 99.0 us on eight wavefronts against 99.6 us,
@@ -277,6 +289,7 @@ int validate(const dmu_gemm_args *a, Plan *plan)
         if (env && strcmp(env, "256x256w4") == 0) tile = TILE_256x256W4;
         if (env && strcmp(env, "256x128") == 0) tile = TILE_256x128;
         if (env && strcmp(env, "128x128") == 0) tile = TILE_128x128;
+        if (env && strcmp(env, "64x128") == 0 && a_kc_mode) tile = TILE_64x128;
         if (a->in_type == DMU_E4M3 && (tile == TILE_256x256 || tile == TILE_256x256W4))
             tile = TILE_256x128; // e4m3 fragments need the registers of a 64 x 64 wavefront tile
         if (a->in_type == DMU_I8 && tile == TILE_256x256W4)
@@ -402,15 +415,23 @@ uint32_t sk_spin_limit()
     return (end && *end == 0 && v <= SK_SPIN_LIMIT) ? (uint32_t)v : SK_SPIN_LIMIT;
 }
 
-// Stream-K runs the 256 x 128 tile where the data-parallel plan has 256 x 256.
+// Stream-K runs the 256 x 128 tile where the data-parallel plan has 256 x 256,
+// and the 128 x 128 tile where it has 64 x 128.
 void sk_retile(Plan *plan, const dmu_gemm_args *a)
 {
-    if (!plan->launch || (plan->cfg.tile != TILE_256x256 && plan->cfg.tile != TILE_256x256W4))
+    if (!plan->launch)
         return;
-    const int64_t tm = (a->M + 255) / 256, tn = (a->N + 127) / 128;
+    int to;
+    if (plan->cfg.tile == TILE_256x256 || plan->cfg.tile == TILE_256x256W4)
+        to = TILE_256x128;
+    else if (plan->cfg.tile == TILE_64x128)
+        to = TILE_128x128;
+    else
+        return;
+    const int64_t tm = (a->M + tile_bm(to) - 1) / tile_bm(to), tn = (a->N + tile_bn(to) - 1) / tile_bn(to);
     if (tm * tn * a->batch >= ((int64_t)1 << 31))
         return; // too many iterations for the 32-bit schedule anyway: stays data-parallel
-    plan->cfg.tile = TILE_256x128;
+    plan->cfg.tile = to;
     plan->p.tiles_m = (int32_t)tm;
     plan->p.tiles_n = (int32_t)tn;
     plan->p.total_tiles = (uint32_t)(tm * tn * a->batch);
@@ -453,8 +474,9 @@ constexpr int64_t PERSIST_MIN_TILES_PER_CU = 4, PERSIST_MAX_KTILES = 4;
 int persist_layout(Plan *plan, const dmu_gemm_args *a)
 {
     plan->cfg.workers = 0;
-    if (!plan->launch || plan->cfg.tile == TILE_GENERIC || plan->cfg.tile == TILE_256x256W4 || a->K == 0)
-        return DMU_OK; // (the four-wavefront tile has no persistent form)
+    if (!plan->launch || plan->cfg.tile == TILE_GENERIC || plan->cfg.tile == TILE_256x256W4 ||
+        plan->cfg.tile == TILE_64x128 || a->K == 0)
+        return DMU_OK; // (the four-wavefront and 64-row tiles have no persistent form)
     const char *mode = getenv("DMU_PERSIST");
     if (mode && strcmp(mode, "never") == 0)
         return DMU_OK;
@@ -506,7 +528,7 @@ int sk_layout(Plan *plan, const dmu_gemm_args *a, SkLayout *sk)
     }
     sk_retile(plan, a);
     const Plan &pl = *plan;
-    if (pl.cfg.tile == TILE_256x256 || pl.cfg.tile == TILE_256x256W4)
+    if (pl.cfg.tile == TILE_256x256 || pl.cfg.tile == TILE_256x256W4 || pl.cfg.tile == TILE_64x128)
         return DMU_OK; // too many tiles to retile: data-parallel
     const uint64_t iters = (uint64_t)pl.p.total_tiles * (uint64_t)nk;
     if (iters >= ((uint64_t)1 << 31))

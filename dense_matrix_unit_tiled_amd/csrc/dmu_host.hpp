@@ -28,7 +28,8 @@ enum TileCfg {
     TILE_128x128 = 2,   // wavefronts 2 x 4, 64 x 32 each
     TILE_GENERIC = 3,   // 64 x 64, element loads
     TILE_256x256W4 = 4, // wavefronts 2 x 2, 128 x 128 each, accumulators in AGPRs (16-bit and int8 inputs)
-    NUM_TILE_CFGS = 5
+    TILE_64x128 = 5,    // wavefronts 2 x 4, 32 x 32 each (A K-contiguous; data-parallel only)
+    NUM_TILE_CFGS = 6
 };
 
 struct LaunchCfg {
@@ -38,7 +39,10 @@ struct LaunchCfg {
     int workers; // > 0: the persistent form of the tiled kernel on this many workgroups
 };
 
-inline int tile_bm(int tile) { return tile == TILE_GENERIC ? 64 : (tile == TILE_128x128 ? 128 : 256); }
+inline int tile_bm(int tile)
+{
+    return (tile == TILE_GENERIC || tile == TILE_64x128) ? 64 : (tile == TILE_128x128 ? 128 : 256);
+}
 inline int tile_bn(int tile)
 {
     return tile == TILE_GENERIC ? 64 : ((tile == TILE_256x256 || tile == TILE_256x256W4) ? 256 : 128);

@@ -332,11 +332,14 @@ int dmu_attention_check(const dmu_attention_args *args);
  * launch nothing.  The tile is 256 x 128 when N <= 128 < M; otherwise, when
  * 240 or more 256 x 256 tiles cover the problem, 256 x 256 if K spans more
  * than two 128-byte K-tiles and 256 x 128 if it spans at most two; 128 x 128
- * for smaller problems; e4m3 never takes 256 x 256.  The environment
- * variable DMU_FORCE_KERNEL=256x256 | 256x256w4 | 256x128 | 128x128 | generic
- * overrides the choice ("256x256w4": the 256 x 256 tile on four wavefronts of
- * 128 x 128 with AGPR accumulators, 16-bit inputs -- int8 takes 256x256
- * instead; never chosen by default).  Host-only; no GPU access.
+ * for smaller problems, and 64 x 128 when at most 128 tiles of 128 x 128
+ * cover the problem (all batch slices) and A is K-contiguous (twice the
+ * workgroups for few tiles); e4m3 never takes 256 x 256.  The environment
+ * variable DMU_FORCE_KERNEL=256x256 | 256x256w4 | 256x128 | 128x128 | 64x128 |
+ * generic overrides the choice ("256x256w4": the 256 x 256 tile on four
+ * wavefronts of 128 x 128 with AGPR accumulators, 16-bit inputs -- int8 takes
+ * 256x256 instead; never chosen by default; "64x128" applies to K-contiguous
+ * A only).  Host-only; no GPU access.
  */
 const char *dmu_gemm_kernel_name(const dmu_gemm_args *args);
 

@@ -115,7 +115,14 @@ def test_empty_problems_launch_nothing():
      "mfma_256x256_k16_t16_bf16_bf16"),
     (dict(M=4096, N=4096, K=4096, lda=4096, layout_b="col", ldb=4096, ldd=4096, in_type="bf16",
           out_type="bf16"), "mfma_256x256_k16_k16_bf16_bf16"),
-    (dict(in_type="f16", out_type="f32"), "mfma_128x128_k16_t16_f16_f32"),
+    (dict(in_type="f16", out_type="f32"), "mfma_64x128_k16_t16_f16_f32"),   # few tiles: 64 x 128
+    (dict(M=1024, N=1024, K=16384, lda=16384, ldb=1024, ldd=1024, in_type="bf16", out_type="bf16"),
+     "mfma_64x128_k16_t16_bf16_bf16"),                                          # 64 tiles of 128 x 128
+    (dict(M=1408, N=1408, K=512, lda=512, ldb=1408, ldd=1408, in_type="bf16", out_type="bf16"),
+     "mfma_64x128_k16_t16_bf16_bf16"),                                          # 121 tiles of 128 x 128
+    (dict(M=1536, N=1536, K=512, lda=512, ldb=1536, ldd=1536, in_type="bf16", out_type="bf16"),
+     "mfma_128x128_k16_t16_bf16_bf16"),                                         # 144: no longer few
+    (dict(layout_a="col", in_type="f16", out_type="f32"), "mfma_128x128_t16_t16_f16_f32"),  # A M-contiguous
     (dict(M=5000, N=3000, K=2050, lda=2050, layout_b="col", ldb=2050, ldd=3000, in_type="f16",
           out_type="f16", acc_type="f16"), "mfma_256x256_kd_kd_f16_f16"),
     (dict(M=8192, N=8192, K=8192, lda=8192, layout_b="col", ldb=8192, ldd=8192, in_type="i8",
@@ -267,10 +274,10 @@ TN8 = dict(layout_b="col", in_type="e4m3")
 @pytest.mark.parametrize("kw,expect", [
     (dict(M=8192, N=8192, K=8192, lda=8192, ldb=8192, ldd=8192, out_type="bf16", **TN8),
      "mfma_256x128_k16_k16_e4m3_bf16"),
-    (dict(out_type="f32", **TN8), "mfma_128x128_k16_k16_e4m3_f32"),
-    (dict(K=200, lda=200, ldb=200, out_type="f16", **TN8), "mfma_128x128_kd_kd_e4m3_f16"),
+    (dict(out_type="f32", **TN8), "mfma_64x128_k16_k16_e4m3_f32"),
+    (dict(K=200, lda=200, ldb=200, out_type="f16", **TN8), "mfma_64x128_kd_kd_e4m3_f16"),
     (dict(K=130, lda=130, ldb=130, out_type="f32", **TN8), "mfma_generic64_any_any_e4m3_f32"),
-    (dict(in_type="e4m3", out_type="f32"), "mfma_128x128_k16_t8_e4m3_f32"),  # B row-major: 8-bit transposed
+    (dict(in_type="e4m3", out_type="f32"), "mfma_64x128_k16_t8_e4m3_f32"),  # B row-major: 8-bit transposed
     (dict(in_type="e4m3", out_type="f32", N=250, ldb=250, ldd=250), "mfma_generic64_any_any_e4m3_f32"),
     (dict(M=4096, N=128, K=4096, lda=4096, ldb=4096, ldd=128, out_type="f32", **TN8),
      "mfma_256x128_k16_k16_e4m3_f32"),
@@ -341,16 +348,16 @@ def test_phase_log_argument_errors():
 
 def test_phase_log_capacity_checked_before_launch(monkeypatch):
     """A launch that would write more records than the log holds fails before any HIP call
-    (the log is never dereferenced on the host; the problem's 64 tiles need 64 records)."""
+    (the log is never dereferenced on the host; the problem's 128 tiles need 128 records)."""
     monkeypatch.setenv("DMU_PERSIST", "never")  # no device query for the persistent choice
     fake = 1 << 40
     a = dmu.gemm_args(1024, 1024, 256, fake, 256, fake + (1 << 36), 256, fake + (2 << 36), 1024,
                       in_type="bf16", out_type="bf16", layout_a="row", layout_b="col")
-    assert dmu.dmu_gemm_kernel_name(a).startswith("mfma_128x128")
-    dmu.dmu_phase_log(fake + (3 << 36), 63)
+    assert dmu.dmu_gemm_kernel_name(a).startswith("mfma_64x128")
+    dmu.dmu_phase_log(fake + (3 << 36), 127)
     try:
         assert dmu.library().dmu_gemm(ctypes.byref(a), None) == dmu.DMU_ERR_INVALID_ARG
-        assert "64 phase records" in dmu.dmu_last_error()
+        assert "128 phase records" in dmu.dmu_last_error()
     finally:
         dmu.dmu_phase_log(None, 0)
 

@@ -42,7 +42,7 @@ def test_reduced_parity(cfg, out_t, act, kernel):
     gu.assert_close_epilogue(got[idx], want[idx], p, ep, bij)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x256w4", "256x128", "128x128"])
+@pytest.mark.parametrize("tile", ["256x256", "256x256w4", "256x128", "128x128", "64x128"])
 @pytest.mark.parametrize("cfg,out_t", [("c2", "bf16"), ("c5", "f32")])
 def test_every_form_on_every_tile(tile, cfg, out_t):
     """The store code has one instantiation per epilogue form (C or not, scales and bias or

@@ -21,7 +21,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = [None, "256x128", "128x128", "generic"]
+KERNELS = [None, "256x128", "128x128", "64x128", "generic"]
 
 
 def problem(out_t, seed, M=300, N=270, K=384, la="row", lb="col", batch=1, pad=0, with_c=False,

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 TYPES = [("f16", "f32", "f32"), ("f16", "f32", "f16"), ("f16", "f16", "f16"), ("bf16", "f32", "bf16"),
          ("bf16", "f32", "f32"), ("i8", "i32", "i32"), ("i8", "i32", "f32"), ("i8", "i32", "bf16"),
          ("e4m3", "f32", "f32"), ("e4m3", "f32", "bf16")]
-TILES = ["256x256", "256x256w4", "256x128", "128x128"]
+TILES = ["256x256", "256x256w4", "256x128", "128x128", "64x128"]
 CASES = 96
 
 

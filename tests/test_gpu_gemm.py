@@ -28,7 +28,7 @@ REDUCED = {
     "c5": dict(M=300, N=260, K=384),
     "c5nn": dict(M=300, N=272, K=384),   # int8 with a row-major B: the 8-bit transposed layout
 }
-KERNELS = [None, "256x256", "256x256w4", "128x128", "256x128", "generic"]
+KERNELS = [None, "256x256", "256x256w4", "128x128", "256x128", "64x128", "generic"]
 
 
 @pytest.mark.parametrize("cfg", list(REDUCED))

@@ -77,8 +77,8 @@ def gemm_case(cfg, seed, with_c=False, **shape):
 
 @pytest.mark.parametrize("cfg,shape,kernel", [
     ("c2", dict(M=4096, N=4096, K=256), "256x256"),
-    ("c3", dict(M=700, N=500, K=1030), "128x128"),
-    ("c5", dict(M=1024, N=512, K=512), "128x128"),
+    ("c3", dict(M=700, N=500, K=1030), "64x128"),
+    ("c5", dict(M=1536, N=1536, K=512), "128x128"),
     ("c1", dict(M=300, N=270, K=130), "generic"),
 ])
 def test_gemm_replays(cfg, shape, kernel):

@@ -25,13 +25,17 @@ CASES = [
     ("c2", dict(M=520, N=264, K=1000), "256x256"),    # bf16, B row-major (transposed tiles), K tail
     ("c2", dict(M=520, N=264, K=1000), "256x256w4"),
     ("c2", dict(M=520, N=264, K=1000), "128x128"),
+    ("c2", dict(M=520, N=264, K=1000), "64x128"),
     ("c3", dict(M=300, N=270, K=1030), "256x256"),    # fp16 -> fp16, 4-byte rows, masked K tail
     ("c3", dict(M=300, N=270, K=1030), "256x128"),
+    ("c3", dict(M=300, N=270, K=1030), "64x128"),
     ("c5", dict(M=300, N=260, K=1024), "256x256"),    # int8
     ("c5nn", dict(M=300, N=272, K=1024), "256x256"),  # int8, B row-major: the 8-bit transposed layout
     ("c5nn", dict(M=300, N=272, K=1024), "128x128"),
     ("c6", dict(M=300, N=260, K=1024), "256x128"),    # e4m3
     ("c6", dict(M=300, N=260, K=1024), "128x128"),
+    ("c6", dict(M=300, N=260, K=1024), "64x128"),
+    ("c5nn", dict(M=300, N=272, K=1024), "64x128"),
     ("c4o", dict(M=300, N=128, K=1024, batch=2), None),
 ]
 

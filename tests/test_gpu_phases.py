@@ -11,6 +11,8 @@ pytestmark = pytest.mark.gpu
 
 CAP = 4096
 
+TILE_DIMS = {"256x256": (256, 256), "256x128": (256, 128), "128x128": (128, 128), "64x128": (64, 128)}
+
 
 def logged(run):
     """Run `run()` with a fresh phase log; returns (its result, records as uint64, kind)."""
@@ -40,13 +42,13 @@ def check_records(r, n, ktiles=None):
     assert end.max() - start.min() < 100_000_000
 
 
-@pytest.mark.parametrize("force", [None, "256x128", "128x128"])
+@pytest.mark.parametrize("force", [None, "256x128", "128x128", "64x128"])
 def test_one_per_tile_records_and_same_bits(force):
     p = workloads.make("c3", "random", 31, M=700, N=500, K=1030)
     plain = gu.run_dmu(p, force=force)
     (got, name), r, kind = logged(lambda: gu.run_dmu(p, force=force, return_name=True))
     gu.assert_bits_equal(got, plain)
-    bm, bn = (256, 256) if "256x256" in name else ((256, 128) if "256x128" in name else (128, 128))
+    bm, bn = TILE_DIMS[name.split("_")[1]]
     tiles = -(-700 // bm) * -(-500 // bn)
     assert kind == 1
     check_records(r, tiles, ktiles=-(-1030 * 2 // 128))
@@ -57,11 +59,12 @@ def test_one_per_tile_records_and_same_bits(force):
 def test_persistent_records(monkeypatch):
     monkeypatch.setenv("DMU_PERSIST", "always")
     p = workloads.make("c4s", "random", 32, batch=3, M=512, N=512, K=128)
-    plain = gu.run_dmu(p)
-    (got, name), r, kind = logged(lambda: gu.run_dmu(p, return_name=True))
+    # (forced: a problem this small would take the 64-row tile, which has no persistent form)
+    plain = gu.run_dmu(p, force="128x128")
+    (got, name), r, kind = logged(lambda: gu.run_dmu(p, force="128x128", return_name=True))
     gu.assert_bits_equal(got, plain)
     assert kind == 2
-    bm, bn = (256, 256) if "256x256" in name else ((256, 128) if "256x128" in name else (128, 128))
+    bm, bn = TILE_DIMS[name.split("_")[1]]
     # one record per tile (index = tile number), written by the worker that ran the tile
     check_records(r, p.batch * -(-512 // bm) * -(-512 // bn), ktiles=2)
 

@@ -24,11 +24,12 @@ def check_workspace_clean(p, ws, name):
     """The error word and the W flag words are zero after a call.  Layout of
     dmu_gemm_streamk: the error word (bytes 0-255), W flag words from byte 256, then
     from the next multiple of 256 bytes W slots of BM x BN 32-bit partial sums (BM x BN
-    of the stream-K tile: 256 x 128 where the data-parallel plan is 256 x 256)."""
+    of the stream-K tile: 256 x 128 where the data-parallel plan is 256 x 256, 128 x 128 where it is
+    64 x 128)."""
     if ws is None:
         return
     tile = name.split("_")[1]
-    bm, bn = {"256x256": (256, 128), "256x128": (256, 128), "128x128": (128, 128)}[tile]
+    bm, bn = {"256x256": (256, 128), "256x128": (256, 128), "128x128": (128, 128), "64x128": (128, 128)}[tile]
     nbytes = 4 * ws.numel()
     round256 = lambda x: (x + 255) // 256 * 256
     size = lambda w: round256(256 + 4 * w) + w * bm * bn * 4

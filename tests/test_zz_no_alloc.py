@@ -68,7 +68,7 @@ def test_noalloc_data_parallel_choice_and_empty():
     an empty problem launches nothing."""
     import torch
 
-    p = workloads.make("c2", "random", 34, M=1024, N=1024, K=256)  # 64 tiles of 128 x 128, 4 K-tiles each
+    p = workloads.make("c2", "random", 34, M=1024, N=1024, K=256)  # 64 tiles of 128 x 128 (128 of 64 x 128), 4 K-tiles
     dA, dB = gu.to_dev(p.A), gu.to_dev(p.B)
     dD = torch.zeros(p.stride_d, dtype=gu.out_dtype(p.out_type), device="cuda:0")
     args = gu.make_args(p, dA, dB, dD)
