@@ -1,5 +1,6 @@
 """A seeded sweep over the call space: random sizes (ragged and aligned), every type triple, all four
-layout pairs, padded leading dimensions, batches, an optional C and an optional fused epilogue --
+layout pairs, padded leading dimensions, batches (an operand shared by every slice at stride 0 now
+and then), an optional C (sometimes the same buffer as D) and an optional fused epilogue --
 each case against the oracle over every output.  Where the operands qualify for the tiled kernels,
 the default choice, a tile configuration drawn at random, and the persistent form are also held bit
 for bit against the fallback kernel (every one issues the same MFMA instructions on the same
@@ -56,7 +57,17 @@ def random_problem(i: int):
                                      row=bool(rng.random() < 0.7), col=bool(rng.random() < 0.7),
                                      bias=bool(rng.random() < 0.7))
     tile = str(rng.choice(TILES))
-    return p, ep, tile
+    # drawn apart, so that the draws above stay those of the earlier cases: one operand shared by
+    # every batch slice (stride 0), and C == D (in place)
+    rng2 = np.random.default_rng([99, i])
+    if batch > 1 and rng2.random() < 0.3:
+        p.A, p.stride_a = p.A[: (M if la == "row" else K) * lda].copy(), 0
+    if batch > 1 and rng2.random() < 0.3:
+        p.B, p.stride_b = p.B[: (K if lb == "row" else N) * ldb].copy(), 0
+    in_place = p.C is not None and rng2.random() < 0.3
+    if in_place:
+        p.stride_c = p.stride_d
+    return p, ep, tile, in_place
 
 
 def check(got, want, p, ep):
@@ -70,22 +81,23 @@ def check(got, want, p, ep):
 
 @pytest.mark.parametrize("i", range(CASES))
 def test_random_call(i, monkeypatch):
-    p, ep, tile = random_problem(i)
+    p, ep, tile, in_place = random_problem(i)
     print(f"case {i}: {p.in_type}->{p.out_type} M={p.M} N={p.N} K={p.K} batch={p.batch} "
           f"{p.layout_a}/{p.layout_b} lda={p.lda} ldb={p.ldb} ldd={p.ldd} C={p.C is not None} "
-          f"ep={ep.act if ep else None} tile={tile}", flush=True)
-    got, name = gu.run_dmu(p, ep=ep, return_name=True)
+          f"strides a/b={p.stride_a}/{p.stride_b} in_place={in_place} ep={ep.act if ep else None} "
+          f"tile={tile}", flush=True)
+    got, name = gu.run_dmu(p, ep=ep, return_name=True, in_place=in_place)
     want = gu.run_oracle(p, ep=ep)
     check(got, want, p, ep)
     if "generic" in name:
         return
     mask = gu.valid_mask(p)
-    ref = gu.run_dmu(p, ep=ep, force="generic")
+    ref = gu.run_dmu(p, ep=ep, force="generic", in_place=in_place)
     gu.assert_bits_equal(got, ref, where=mask)
-    forced, fname = gu.run_dmu(p, ep=ep, force=tile, return_name=True)
+    forced, fname = gu.run_dmu(p, ep=ep, force=tile, return_name=True, in_place=in_place)
     gu.assert_bits_equal(forced, ref, where=mask)
     monkeypatch.setenv("DMU_PERSIST", "always")
-    gu.assert_bits_equal(gu.run_dmu(p, ep=ep), ref, where=mask)
+    gu.assert_bits_equal(gu.run_dmu(p, ep=ep, in_place=in_place), ref, where=mask)
     monkeypatch.setenv("DMU_PERSIST", "never")
     monkeypatch.setenv("DMU_STREAMK", "always")
     sk, skname, _ = gu.run_streamk(p, ep=ep)
