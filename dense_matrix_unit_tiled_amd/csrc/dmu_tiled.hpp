@@ -676,9 +676,10 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
         u32x4 sb[PD][NB];
     };
     // Load K-tile kb of tile tc into staging set 0 (what the main loop's
-    // prologue would load first).
+    // prologue would load first) -- or, with n > 1, K-tiles kb .. kb + n - 1
+    // into sets 0 .. n - 1 (n <= PD: a whole short K range, for short_loop).
     static __device__ __forceinline__ void prefetch(const GemmParams &p, const TileCoord tc, int kb, Staging &st,
-                                                    uint32_t tid)
+                                                    uint32_t tid, int n = 1)
     {
         const uint32_t lane = tid & 63u;
         const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -701,11 +702,90 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
             tb.init(p.ldb * E, wave, lane);
         const uint32_t k_bytes = (uint32_t)p.K * E;
 #pragma unroll
-        for (int c = 0; c < NA; ++c)
-            st.sa[0][c] = ta.load(c, ra, kb, k_bytes);
+        for (int set = 0; set < PD; ++set) {
+            if (set > 0 && set >= n)
+                break;
 #pragma unroll
-        for (int c = 0; c < NB; ++c)
-            st.sb[0][c] = tb.load(c, rb, kb, k_bytes);
+            for (int c = 0; c < NA; ++c)
+                st.sa[set][c] = ta.load(c, ra, kb + set, k_bytes);
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+                st.sb[set][c] = tb.load(c, rb, kb + set, k_bytes);
+        }
+    }
+
+    // acc += the product of tile tc over its nk <= PD K-tiles, all of which are
+    // in the staging sets already (prefetch with n = nk): each goes to its own
+    // stage, one barrier, then the K-steps in order -- the same instructions on
+    // the same fragments as the main loop.  The persistent kernel runs short K
+    // this way, so that none of a tile's loads is issued after the previous
+    // tile's D stores: a wait for such a load would also wait for those stores
+    // to drain (one counter covers vector loads and stores, in order).
+    static __device__ __forceinline__ void short_loop(const GemmParams &p, const TileCoord tc, int nk, char *smem,
+                                                      acc_t (&acc)[MT][NT], uint32_t tid, Staging &st)
+    {
+        const uint32_t lane = tid & 63u;
+        const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const uint32_t wm = wave / WGN, wn = wave % WGN;
+        const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+        ATile ta;
+        BTile tb;
+        if constexpr (AMODE == MC16 || AMODE == MC8)
+            ta.init(p.lda * E, p.M - m0, wave, lane);
+        else
+            ta.init(p.lda * E, wave, lane);
+        if constexpr (BMODE == MC16 || BMODE == MC8)
+            tb.init(p.ldb * E, p.N - n0, wave, lane);
+        else
+            tb.init(p.ldb * E, wave, lane);
+        const uint32_t k_bytes = (uint32_t)p.K * E;
+        if constexpr (AMODE == KCD)
+            ta.init_mask(k_bytes);
+        if constexpr (BMODE == KCD)
+            tb.init_mask(k_bytes);
+#pragma unroll
+        for (int set = 0; set < PD; ++set) {
+            if (set > 0 && set >= nk)
+                break;
+            char *stage = smem + set * STAGE;
+#pragma unroll
+            for (int c = 0; c < NA; ++c)
+                ta.store(c, stage, wave, lane, st.sa[set][c], set, k_bytes);
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+                tb.store(c, stage + ABYTES, wave, lane, st.sb[set][c], set, k_bytes);
+        }
+        stage_barrier();
+        // B's fragments of a K-step, then A's one tile row at a time (registers: the
+        // staging sets are still live beside the accumulators)
+        u32x4 af[FH], bfr[NT][FH];
+#pragma unroll
+        for (int set = 0; set < PD; ++set) {
+            if (set > 0 && set >= nk)
+                break;
+            const char *stage = smem + set * STAGE;
+#pragma unroll
+            for (int ks = 0; ks < (F8 ? 1 : 2); ++ks) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+#pragma unroll
+                    for (int h = 0; h < FH; ++h)
+                        bfr[j][h] = BTile::frag(stage + ABYTES, wn * WTN + j * 16, F8 ? h : ks, lane);
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+#pragma unroll
+                    for (int h = 0; h < FH; ++h)
+                        af[h] = ATile::frag(stage, wm * WTM + i * 16, F8 ? h : ks, lane);
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        if constexpr (F8)
+                            acc[i][j] = Mfma<E4M3>::step2(bfr[j][0], bfr[j][1], af[0], af[1], acc[i][j]);
+                        else
+                            acc[i][j] = Mfma<T>::step(bfr[j][0], af[0], acc[i][j]);
+                    }
+                }
+            }
+        }
     }
 
     // acc += the product of tile tc over K-tiles [kb, ke) (kb < ke), with the
@@ -1100,8 +1180,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     uint32_t t = blockIdx.x;
     if (t >= total)
         return; // more workers than tiles (uniform: before any barrier)
+    // K of at most PD K-tiles: each tile's whole K range is loaded before the
+    // previous tile's epilogue (short_loop; not on the 256 x 256 tile, whose one
+    // staging set leaves no registers for it, nor for e4m3, whose fragments are
+    // twice as large: both spilled)
+    constexpr bool SHORT = G::PD >= 2 && !G::F8;
+    const bool short_k = SHORT && nk <= G::PD;
     if (nk > 0)
-        G::prefetch(p, tile_of(p, t), 0, st, threadIdx.x);
+        G::prefetch(p, tile_of(p, t), 0, st, threadIdx.x, short_k ? nk : 1);
     for (; t < total; t += W) {
         phase_begin(p.phases, t, (uint32_t)nk);
         typename G::acc_t acc[G::MT][G::NT];
@@ -1112,14 +1198,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
                 acc[i][j] = typename G::acc_t{};
         uint32_t tid_m = threadIdx.x;
         asm volatile("" : "+v"(tid_m));
-        if (nk > 0)
+        if constexpr (SHORT) {
+            if (nk > 0 && short_k)
+                G::short_loop(p, tile_of(p, t), nk, smem, acc, tid_m, st);
+            else if (nk > 0)
+                G::template mainloop<true>(p, tile_of(p, t), 0, nk, smem, acc, tid_m, st);
+        } else if (nk > 0) {
             G::template mainloop<true>(p, tile_of(p, t), 0, nk, smem, acc, tid_m, st);
+        }
         uint32_t tid_e = threadIdx.x, t2 = t;
         asm volatile("" : "+v"(tid_e));
         asm volatile("" : "+s"(t2));
         phase_mark(p.phases, t2, PH_LOOP);
         if (nk > 0 && t2 + W < total)
-            G::prefetch(p, tile_of(p, t2 + W), 0, st, tid_e);
+            G::prefetch(p, tile_of(p, t2 + W), 0, st, tid_e, short_k ? nk : 1);
         phase_mark(p.phases, t2, PH_FIX);
         G::epilogue(p, tile_of(p, t2), acc, smem, tid_e & 63u, __builtin_amdgcn_readfirstlane(tid_e >> 6));
         phase_end(p.phases, t2);

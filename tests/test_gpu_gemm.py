@@ -327,13 +327,17 @@ PERSIST_CASES = [
     ("c3", None, dict(M=2000, N=4100, K=130)),                # rows 4-byte aligned, K tail
     ("c4s", None, dict(M=300, N=260, K=128, batch=40)),       # 3 x 3 tiles x 40 batches
     ("c1", "128x128", dict(M=2000, N=4000, K=64)),            # with C
+    ("c6", None, dict(M=2000, N=4100, K=256)),                # e4m3, two K-tiles (main loop: no short-K form)
+    ("c5", "128x128", dict(M=2000, N=4100, K=256)),           # int8, two K-tiles: the short-K loop
+    ("c3", "256x128", dict(M=2000, N=4100, K=100)),           # 4-byte rows, two K-tiles, masked tail: short
 ]
 
 
 @pytest.mark.parametrize("cfg,kernel,shape", PERSIST_CASES, ids=[f"{c}-{k}" for c, k, _ in PERSIST_CASES])
 def test_persistent_form_matches(cfg, kernel, shape, monkeypatch):
     """The persistent form (a fixed set of workgroups looping over the tiles, the next tile's first
-    K-tile loaded before the current tile's epilogue), forced on problems with more tiles than
+    K-tile -- or, when K spans at most the staging sets, its whole K range -- loaded before the
+    current tile's epilogue), forced on problems with more tiles than
     workers, ragged edges and batches: against the oracle, and bit-identical to the
     one-workgroup-per-tile launch."""
     p = workloads.make(cfg, "random", 5, **shape)
