@@ -721,6 +721,7 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
     // this way, so that none of a tile's loads is issued after the previous
     // tile's D stores: a wait for such a load would also wait for those stores
     // to drain (one counter covers vector loads and stores, in order).
+    template <bool PARK_IN_STAGES>
     static __device__ __forceinline__ void short_loop(const GemmParams &p, const TileCoord tc, int nk, char *smem,
                                                       acc_t (&acc)[MT][NT], uint32_t tid, Staging &st)
     {
@@ -786,6 +787,12 @@ template <int T, int O, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE> 
                 }
             }
         }
+        // Every fragment read above came after the one barrier: an epilogue that
+        // parks each wavefront's results in the stages must wait until all
+        // wavefronts are done reading them (the main loop's reads after its last
+        // barrier are of a K-tile past the range, whose values are never used).
+        if constexpr (PARK_IN_STAGES)
+            stage_barrier();
     }
 
     // acc += the product of tile tc over K-tiles [kb, ke) (kb < ke), with the
@@ -1173,18 +1180,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
     __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_persist(GemmParams p)
 {
     typedef Tiled<T, O, BM, BN, WGM, WGN, AMODE, BMODE> G;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+    // K of at most PD K-tiles: each tile's whole K range is loaded before the
+    // previous tile's epilogue (short_loop; not on the 256 x 256 tile, whose one
+    // staging set leaves no registers for it, nor for e4m3, whose fragments are
+    // twice as large: both spilled).  Those configurations park the epilogue's
+    // results beside the stages (LDS: 256 x 128, 96 + 35 KiB), so that a
+    // wavefront done with its K-steps parks while others still read the stages.
+    constexpr bool SHORT = G::PD >= 2 && !G::F8;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE + (SHORT ? G::NW * G::PARK : 0)];
     typename G::Staging st;
     const uint32_t W = gridDim.x, total = p.total_tiles;
     const int nk = (int)(((int64_t)p.K * G::E + 127) / 128);
     uint32_t t = blockIdx.x;
     if (t >= total)
         return; // more workers than tiles (uniform: before any barrier)
-    // K of at most PD K-tiles: each tile's whole K range is loaded before the
-    // previous tile's epilogue (short_loop; not on the 256 x 256 tile, whose one
-    // staging set leaves no registers for it, nor for e4m3, whose fragments are
-    // twice as large: both spilled)
-    constexpr bool SHORT = G::PD >= 2 && !G::F8;
     const bool short_k = SHORT && nk <= G::PD;
     if (nk > 0)
         G::prefetch(p, tile_of(p, t), 0, st, threadIdx.x, short_k ? nk : 1);
@@ -1200,7 +1209,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         asm volatile("" : "+v"(tid_m));
         if constexpr (SHORT) {
             if (nk > 0 && short_k)
-                G::short_loop(p, tile_of(p, t), nk, smem, acc, tid_m, st);
+                G::template short_loop<false>(p, tile_of(p, t), nk, smem, acc, tid_m, st);
             else if (nk > 0)
                 G::template mainloop<true>(p, tile_of(p, t), 0, nk, smem, acc, tid_m, st);
         } else if (nk > 0) {
@@ -1213,7 +1222,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
         if (nk > 0 && t2 + W < total)
             G::prefetch(p, tile_of(p, t2 + W), 0, st, tid_e, short_k ? nk : 1);
         phase_mark(p.phases, t2, PH_FIX);
-        G::epilogue(p, tile_of(p, t2), acc, smem, tid_e & 63u, __builtin_amdgcn_readfirstlane(tid_e >> 6));
+        G::epilogue(p, tile_of(p, t2), acc, (SHORT && short_k) ? smem + 2 * G::STAGE : smem, tid_e & 63u,
+                    __builtin_amdgcn_readfirstlane(tid_e >> 6));
         phase_end(p.phases, t2);
         __syncthreads(); // every wavefront is done with its park before the next tile's stages
     }
