@@ -19,7 +19,7 @@ TYPES = [("f16", "f32", "f32"), ("f16", "f32", "f16"), ("f16", "f16", "f16"), ("
          ("bf16", "f32", "f32"), ("i8", "i32", "i32"), ("i8", "i32", "f32"), ("i8", "i32", "bf16"),
          ("e4m3", "f32", "f32"), ("e4m3", "f32", "bf16")]
 TILES = ["256x256", "256x256w4", "256x128", "128x128", "64x128"]
-CASES = 96
+CASES = 160
 
 
 def random_problem(i: int):
