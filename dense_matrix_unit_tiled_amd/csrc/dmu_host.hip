@@ -468,8 +468,11 @@ int device_cus(const char *who, int *out)
 // x 128 fp16 -> fp32, 64 tiles of two K-tiles per unit, 405.8 -> 379.6 us;
 // long loops lose a little: 8192^3 int8, 4 tiles of 64 K-tiles per unit,
 // 425.7 -> 428.2 us; 8192^3 e4m3, 8 per unit, 435.9 -> 440.4 us).
+// With K of at most two K-tiles (the whole range loaded before the previous
+// tile's epilogue) two tiles per unit already pay: 4096 x 4096 x 128 fp16 ->
+// fp32, 512 tiles, 19.1 -> 18.5 us; 4096 x 4096 x 64, 17.0 -> 16.3 us.
 // DMU_PERSIST=always or never overrides the choice (tests and sweeps).
-constexpr int64_t PERSIST_MIN_TILES_PER_CU = 4, PERSIST_MAX_KTILES = 4;
+constexpr int64_t PERSIST_MIN_TILES_PER_CU = 4, PERSIST_MIN_TILES_PER_CU_SHORT = 2, PERSIST_MAX_KTILES = 4;
 
 int persist_layout(Plan *plan, const dmu_gemm_args *a)
 {
@@ -486,7 +489,11 @@ int persist_layout(Plan *plan, const dmu_gemm_args *a)
         return rc;
     const int64_t tiles = plan->p.total_tiles, nk = (a->K * elem_bytes(a->in_type) + 127) / 128;
     const bool always = mode && strcmp(mode, "always") == 0;
-    if (!always && (tiles < PERSIST_MIN_TILES_PER_CU * cus || nk > PERSIST_MAX_KTILES))
+    // (the short-K form exists for the tiles with two staging sets, not for e4m3)
+    const bool short_form = nk <= 2 && a->in_type != DMU_E4M3 &&
+                            (plan->cfg.tile == TILE_256x128 || plan->cfg.tile == TILE_128x128);
+    const int64_t min_per_cu = short_form ? PERSIST_MIN_TILES_PER_CU_SHORT : PERSIST_MIN_TILES_PER_CU;
+    if (!always && (tiles < min_per_cu * cus || nk > PERSIST_MAX_KTILES))
         return DMU_OK;
     // one workgroup per compute unit, a multiple of the 8 XCDs so that each
     // worker's tiles stay on its XCD; never more workers than tiles
