@@ -508,9 +508,14 @@ int persist_layout(Plan *plan, const dmu_gemm_args *a)
 // chosen when those tiles fill less than 80 % of their waves (measured on the
 // 256-unit chip: 1024 x 1024 x 16384 bf16, 64 tiles, 123 -> 50 us; the
 // 5000 x 3000 x 2050 problem, 240 tiles = 94 %, stays data-parallel: stream-K
-// on its 480 smaller tiles took 97 us against 73 us).  DMU_STREAMK=always or
-// never overrides the choice (tests and sweeps).
-constexpr double SK_MIN_IDLE_FILL = 0.8;
+// on its 480 smaller tiles took 97 us against 73 us).  Where the data-parallel
+// plan has 64 x 128 tiles, those already spread a few-tile problem over more
+// units, and stream-K (on 128 x 128) pays only below 60 % (bf16, interleaved:
+// 1024 x 1024 x 4096, 128 tiles = 50 %, 24.4 -> 21.0 us; 1280 x 1024 x 8192,
+// 160 = 63 %, 43.7 against 48.2 us; 1280^2 x 8192, 200 = 78 %, 47.3 against
+// 51.7 us).  DMU_STREAMK=always or never overrides the choice (tests and
+// sweeps).
+constexpr double SK_MIN_IDLE_FILL = 0.8, SK_MIN_IDLE_FILL_64 = 0.6;
 
 int sk_layout(Plan *plan, const dmu_gemm_args *a, SkLayout *sk)
 {
@@ -530,7 +535,8 @@ int sk_layout(Plan *plan, const dmu_gemm_args *a, SkLayout *sk)
     const uint64_t n = (uint64_t)cu_count;
     if (!(mode && strcmp(mode, "always") == 0)) {
         const uint64_t tiles = plan->p.total_tiles, waves = (tiles + n - 1) / n;
-        if ((double)tiles >= SK_MIN_IDLE_FILL * (double)(waves * n))
+        const double min_fill = plan->cfg.tile == TILE_64x128 ? SK_MIN_IDLE_FILL_64 : SK_MIN_IDLE_FILL;
+        if ((double)tiles >= min_fill * (double)(waves * n))
             return DMU_OK; // the data-parallel waves are full enough
     }
     sk_retile(plan, a);

@@ -208,8 +208,9 @@ int dmu_gemm_ex_check(const dmu_gemm_args *args, const dmu_epilogue *ep);
  *                  the workspace again before its next use.
  *  workspace_bytes its size.
  * The schedule is used where it pays: when the data-parallel kernel's tiles
- * fill less than 80 % of its waves of one workgroup per compute unit (few
- * tiles, long K).  Otherwise -- and for products that only the fallback kernel
+ * fill less than 80 % of its waves of one workgroup per compute unit (60 %
+ * where its tiles are 64 x 128, which already spread few tiles over more
+ * units; few tiles, long K).  Otherwise -- and for products that only the fallback kernel
  * can read, and K == 0 -- the call runs the data-parallel kernel and uses no
  * workspace (its size is then 0).  The environment variable DMU_STREAMK=always
  * or =never overrides the choice.
